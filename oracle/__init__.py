@@ -1,0 +1,10 @@
+"""fp64 CPU oracle of the retention operator -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may
+import this package.  It shares no code with the HIP library and imports nothing from
+it.  Pins: every public function is checked in ``tests/test_oracle.py`` against exact
+rational arithmetic, closed forms, textbook special cases and hand-worked fixtures
+(``tests/golden/``); no function here is "parity unpinned".
+"""
+from .retention_oracle import *  # noqa: F401,F403
+from .retention_oracle import __all__  # noqa: F401
