@@ -1,0 +1,156 @@
+/*
+ * retention.h -- C ABI of the MI355X (gfx950) retention operator library
+ *                (libretention_fwd.so).
+ *
+ * The operator is RetNet's retention.  Per (batch b, head h) it carries a state
+ * S in R^{dk x dv} through the sequence:
+ *
+ *     S_n = lambda_n * S_{n-1} + k_n^T v_n,        o_n = q_n S_n
+ *
+ * with lambda_n = gamma_h (one decay per head) or lambda_n = exp(g[b,h,n]) (gated,
+ * per-token log-decay).  Sources, cited by page title and section:
+ *   - "RetNet retention mechanism" tutorial (aiqz.cc), section 递归推理: the
+ *     recurrence above; section 衰减矩阵: D_nm = gamma^(n-m) for n >= m, else 0;
+ *     section 并行训练: (Q K^T (.) D) V; section 块级循环: the chunkwise form --
+ *     parallel inside a chunk, the state relayed across chunks.
+ *   - "Retentive Network (RetNet) 详解" (171host.com), section 3.1: the three
+ *     equivalent forms (recurrent, parallel, chunkwise recurrent).
+ *   - "unilm RetNet 技术指南 ... YOCO 中 Gated RetNet 的源码解析" (pwwt.cn), sections
+ *     GateRetention 模块的内部结构 (log-decay gate), 三种计算路径与增量状态 (the
+ *     one-token path with a constant-size state; prefill seeding the decode state)
+ *     and Triton 内核与自校验测试 (chunk-end decays for the cross-chunk state).
+ *
+ * Conventions shared by every entry point
+ *   Layout     All tensors are dense, row-major, contiguous, in DEVICE memory:
+ *                q, k   [B, H, N, dk]     v, o  [B, H, N, dv]
+ *                gamma  [H]  fp32         g     [B, H, N]  fp32
+ *                state  [B, H, dk, dv] fp32
+ *              q, k, v and o share one element type, RETN_F32 or RETN_BF16;
+ *              gamma, g and states are always fp32.  Accumulation is fp32; a bf16
+ *              output is rounded to nearest-even.
+ *   Ownership  The caller allocates and owns every buffer.  The library keeps no
+ *              pointer after a call returns and allocates no device memory.
+ *   Streams    Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *              and the call returns without synchronising.
+ *   Errors     Arguments are validated before anything is enqueued; on any error
+ *              nothing is launched and nothing is written.  A failed launch returns
+ *              RETN_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *              synchronisation.  Nothing is printed.
+ *   Domain     gamma in (0, 1] (gamma = 1 is undecayed linear attention); g finite
+ *              and <= 0.  Values are not scanned on the device.
+ *   Sizes      B, H, N >= 0 (B*H*N = 0 is a valid empty call: state_out, if given,
+ *              receives state_in or zeros); dk, dv in [1, 256] for the generic
+ *              kernels; chunk >= 1.  The bf16 matrix-core path is used when dk is
+ *              64, 128 or 256, dv is a multiple of 64 and chunk is 64, 128, 256 or
+ *              512; every other shape in range runs on the generic kernels.
+ *              A ragged last chunk (N not a multiple of chunk) is computed exactly;
+ *              there is no padding.
+ */
+#ifndef RETENTION_FWD_H
+#define RETENTION_FWD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RETN_OK = 0,
+    RETN_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    RETN_ERR_SHAPE = 2,        /* a size is negative or out of range                */
+    RETN_ERR_DTYPE = 3,        /* unknown element type                              */
+    RETN_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. dk > 256)         */
+    RETN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
+    RETN_ERR_ALIAS = 6,        /* an output overlaps an input                       */
+    RETN_ERR_HIP = 7           /* the HIP runtime reported an error at launch       */
+} retn_status;
+
+typedef enum {
+    RETN_F32 = 0,
+    RETN_BF16 = 1
+} retn_dtype;
+
+/*
+ * Chunkwise-recurrent retention forward with one decay per head.
+ *
+ * Computes, for every (b, h), the outputs o_n = q_n S_n of the recurrence above with
+ * lambda_n = gamma[h], evaluated in chunks of `chunk` tokens: inside a chunk the
+ * parallel form (Q K^T (.) D) V with D_jl = gamma^(j-l) (j >= l), across chunks the
+ * state, decayed by gamma^L for a chunk of L tokens, with the cross-chunk query
+ * term weighted per row by gamma^(j+1) (tutorial, sections 衰减矩阵 and 块级循环).
+ *
+ *   q, k, v     inputs, element type `dtype`, layout above
+ *   gamma       [H] fp32 per-head decays
+ *   o           output [B,H,N,dv], element type `dtype`; must not overlap any input
+ *   state_in    optional [B,H,dk,dv] fp32 initial state (NULL = zeros); it is decayed
+ *               by the first token's lambda like any state
+ *   state_out   optional [B,H,dk,dv] fp32 final state S_N (NULL = not written); may
+ *               equal state_in (in-place update) but must not overlap q/k/v/o
+ *   chunk       chunk size in tokens (>= 1); changes rounding only, not the result
+ *   workspace   device scratch of at least retention_workspace_bytes(...) bytes
+ *               (may be NULL when that is 0); contents need not be initialised
+ *   stream      hipStream_t to enqueue on
+ */
+retn_status retention_chunkwise_fwd(const void* q, const void* k, const void* v,
+                                    const float* gamma, void* o,
+                                    const float* state_in, float* state_out,
+                                    int B, int H, int N, int dk, int dv, int chunk,
+                                    retn_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * Gated chunkwise retention forward: per-token, per-head log-decay g[B,H,N] (fp32,
+ * g <= 0).  The weight of token m in output n >= m is exp(G_n - G_m) with G the
+ * inclusive cumulative sum of g along the sequence, and the incoming state reaches
+ * output n with weight exp(G_n) (pwwt.cn guide, sections GateRetention 模块的内部结构
+ * and Triton 内核与自校验测试).  Other arguments as retention_chunkwise_fwd.
+ */
+retn_status gated_retention_chunkwise_fwd(const void* q, const void* k, const void* v,
+                                          const float* g, void* o,
+                                          const float* state_in, float* state_out,
+                                          int B, int H, int N, int dk, int dv, int chunk,
+                                          retn_dtype dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step (tutorial, section 递归推理):
+ *     S <- gamma[h] S + k^T v   (fp32, in place),   o = q S   (with the updated S)
+ *   q, k   [B,H,dk]  v, o [B,H,dv]  element type `dtype`
+ *   state  [B,H,dk,dv] fp32, read and overwritten; must not overlap q/k/v/o
+ * Needs no workspace.
+ */
+retn_status retention_decode_step(const void* q, const void* k, const void* v,
+                                  const float* gamma, float* state, void* o,
+                                  int B, int H, int dk, int dv,
+                                  retn_dtype dtype, void* stream);
+
+/*
+ * One gated decode step: S <- exp(g[b,h]) S + k^T v, o = q S (pwwt.cn guide, section
+ * 三种计算路径与增量状态: the previous state scaled by the decay, then the new
+ * k^T v added).  g is [B,H] fp32.  Other arguments as retention_decode_step.
+ */
+retn_status gated_retention_decode_step(const void* q, const void* k, const void* v,
+                                        const float* g, float* state, void* o,
+                                        int B, int H, int dk, int dv,
+                                        retn_dtype dtype, void* stream);
+
+/*
+ * Bytes of workspace the chunkwise entry points need for these sizes (0 when the
+ * sequence is not split across workgroups).  gated: 0 = per-head gamma, 1 = gated.
+ * Returns 0 for invalid sizes as well; the entry point then reports the error.
+ */
+size_t retention_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk,
+                                 retn_dtype dtype, int gated);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* retention_status_string(retn_status status);
+
+/* Version of this ABI (incremented on any signature change). */
+int retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_FWD_H */

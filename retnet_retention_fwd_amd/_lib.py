@@ -1,0 +1,224 @@
+"""ctypes binding of libretention_fwd.so (the C ABI declared in include/retention.h).
+
+Argument marshalling only: every step of the operator runs in the library's HIP
+kernels.  torch provides device memory (outputs, workspace) and the current stream.
+If the library is missing or cannot be loaded, every call raises; there is no other
+code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libretention_fwd.so")
+
+RETN_F32 = 0
+RETN_BF16 = 1
+
+STATUS_NAMES = {
+    0: "RETN_OK", 1: "RETN_ERR_NULL", 2: "RETN_ERR_SHAPE", 3: "RETN_ERR_DTYPE",
+    4: "RETN_ERR_UNSUPPORTED", 5: "RETN_ERR_WORKSPACE", 6: "RETN_ERR_ALIAS", 7: "RETN_ERR_HIP",
+}
+
+# Every symbol include/retention.h declares.
+EXPORTED = (
+    "retention_chunkwise_fwd",
+    "gated_retention_chunkwise_fwd",
+    "retention_decode_step",
+    "gated_retention_decode_step",
+    "retention_workspace_bytes",
+    "retention_status_string",
+    "retention_abi_version",
+)
+
+
+class RetentionError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m retnet_retention_fwd_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    chunk_sig = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+    for name in ("retention_chunkwise_fwd", "gated_retention_chunkwise_fwd"):
+        f = getattr(L, name)
+        f.argtypes = chunk_sig
+        f.restype = ctypes.c_int
+    for name in ("retention_decode_step", "gated_retention_decode_step"):
+        f = getattr(L, name)
+        f.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+        f.restype = ctypes.c_int
+    L.retention_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    L.retention_workspace_bytes.restype = _sz
+    L.retention_status_string.argtypes = [_i]
+    L.retention_status_string.restype = ctypes.c_char_p
+    L.retention_abi_version.argtypes = []
+    L.retention_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().retention_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RetentionError(status, where, status_string(status))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RETN_BF16
+    if t.dtype == torch.float32:
+        return RETN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:
+    return int(lib().retention_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, 1 if gated else 0))
+
+
+def _chunk_call(fn_name, q, k, v, decay, chunk, state_in, return_state, out, state_out, stream,
+                workspace, gated):
+    torch = _torch()
+    L = lib()
+    _require(q, "q")
+    dev = q.device
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(decay, "g" if gated else "gamma", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"expected q,k [B,H,N,dk] and v [B,H,N,dv]; got {tuple(q.shape)} "
+                         f"{tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    exp_decay = (B, H, N) if gated else (H,)
+    if tuple(decay.shape) != exp_decay:
+        raise ValueError(f"decay must have shape {exp_decay}, got {tuple(decay.shape)}")
+    if state_in is not None:
+        _require(state_in, "state_in", torch.float32, dev)
+        if tuple(state_in.shape) != (B, H, dk, dv):
+            raise ValueError("state_in must be [B,H,dk,dv]")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", q.dtype, dev)
+        if tuple(out.shape) != (B, H, N, dv):
+            raise ValueError("out must be [B,H,N,dv]")
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _require(state_out, "state_out", torch.float32, dev)
+        if tuple(state_out.shape) != (B, H, dk, dv):
+            raise ValueError("state_out must be [B,H,dk,dv]")
+    code = _dtype_code(q)
+    ws_need = workspace_bytes(B, H, N, dk, dv, chunk, code, gated)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(L, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), _ptr(state_in),
+                             _ptr(state_out), B, H, N, dk, dv, int(chunk), code, _ptr(workspace),
+                             ws_bytes, _stream(stream))
+    _check(st, fn_name)
+    return (out, state_out) if (return_state or state_out is not None) else out
+
+
+def retention_chunkwise_fwd(q, k, v, gamma, chunk, state_in=None, return_state=False, out=None,
+                            state_out=None, stream=None, workspace=None):
+    """Chunkwise retention forward with per-head decays gamma[H] (fp32).
+
+    q, k: [B,H,N,dk], v: [B,H,N,dv] (bf16 or fp32, contiguous, on the GPU).  Returns o
+    [B,H,N,dv] in the input dtype, or (o, state_out) if return_state or state_out is given.
+    """
+    return _chunk_call("retention_chunkwise_fwd", q, k, v, gamma, chunk, state_in, return_state, out,
+                       state_out, stream, workspace, False)
+
+
+def gated_retention_chunkwise_fwd(q, k, v, g, chunk, state_in=None, return_state=False, out=None,
+                                  state_out=None, stream=None, workspace=None):
+    """Gated chunkwise retention forward with per-token log-decays g[B,H,N] (fp32, <= 0)."""
+    return _chunk_call("gated_retention_chunkwise_fwd", q, k, v, g, chunk, state_in, return_state, out,
+                       state_out, stream, workspace, True)
+
+
+def _decode_call(fn_name, q, k, v, decay, state, out, stream, gated):
+    torch = _torch()
+    L = lib()
+    _require(q, "q")
+    dev = q.device
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(decay, "g" if gated else "gamma", torch.float32, dev)
+    _require(state, "state", torch.float32, dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q,k [B,H,dk] and v [B,H,dv]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(decay.shape) != ((B, H) if gated else (H,)):
+        raise ValueError("decay has the wrong shape")
+    if tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError("state must be [B,H,dk,dv]")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", q.dtype, dev)
+    st = getattr(L, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state), _ptr(out), B, H, dk,
+                             dv, _dtype_code(q), _stream(stream))
+    _check(st, fn_name)
+    return out
+
+
+def retention_decode_step(q, k, v, gamma, state, out=None, stream=None):
+    """One decode step: state <- gamma state + k^T v (in place, fp32), returns o = q state."""
+    return _decode_call("retention_decode_step", q, k, v, gamma, state, out, stream, False)
+
+
+def gated_retention_decode_step(q, k, v, g, state, out=None, stream=None):
+    """One gated decode step with log-decay g[B,H]: state <- exp(g) state + k^T v, o = q state."""
+    return _decode_call("gated_retention_decode_step", q, k, v, g, state, out, stream, True)

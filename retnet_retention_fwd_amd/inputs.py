@@ -132,16 +132,22 @@ def make_chunkwise(w: Workload, *, B=None, H=None, N=None, seed=None, state_in=F
 def make_decode(w: Workload, *, B=None, steps=None, seed=None):
     """Decode workload: S0 ~ N(0, 0.1^2) fp32 [B,H,dk,dv], then per-step q,k,v.
 
-    Returns dict: state0 (tensor, f64), q, k, v as [steps,B,H,d] (tensor, f64), gamma.
-    Drawing order: S0, then Q, K, V for all steps (each [steps,B,H,d]).
+    Drawing order: S0, then for each step t: q_t [B,H,dk], k_t [B,H,dk], v_t [B,H,dv].
+    Returns dict: state0 (tensor, f64); q, k, v as torch CPU tensors [steps,B,H,d] in the
+    workload dtype (no float64 copies: at full size they would take ~13 GB; take rows
+    with ``.to(torch.float64)`` where the oracle needs them); gamma (tensor, f64).
     """
     B = w.B if B is None else B
     steps = w.N if steps is None else steps
     rng = np.random.default_rng(w.seed if seed is None else seed)
     out = {"state0": to_dtype(rng.standard_normal((B, w.H, w.dk, w.dv)) * 0.1, "f32")}
     s = 1.0 / math.sqrt(w.dk)
-    for nm, d in (("q", w.dk), ("k", w.dk), ("v", w.dv)):
-        out[nm] = to_dtype(rng.standard_normal((steps, B, w.H, d)) * s, w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    bufs = {nm: torch.empty((steps, B, w.H, d), dtype=tdt) for nm, d in (("q", w.dk), ("k", w.dk), ("v", w.dv))}
+    for t in range(steps):
+        for nm, d in (("q", w.dk), ("k", w.dk), ("v", w.dv)):
+            bufs[nm][t] = to_dtype(rng.standard_normal((B, w.H, d)) * s, w.dtype)[0]
+    out.update(bufs)
     out["gamma"] = to_dtype(gammas("decode_bf16", w.H).astype(np.float64), "f32")
     return out
 

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed: every call here fails validation and so
+returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from retnet_retention_fwd_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "retention.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.retention_abi_version() == 1
+    for s in range(8):
+        assert _lib.status_string(s)
+    assert _lib.status_string(99) == "unknown status"
+
+
+FAKE = 1 << 40          # never dereferenced: validation fails before any launch
+MB = 1 << 20
+
+
+def chunk(L, q=FAKE, k=FAKE + 64 * MB, v=FAKE + 128 * MB, d=FAKE + 192 * MB, o=FAKE + 256 * MB,
+          si=None, so=None, B=1, H=2, N=64, dk=16, dv=16, C=16, dt=0, ws=None, wsb=0, gated=False):
+    f = L.gated_retention_chunkwise_fwd if gated else L.retention_chunkwise_fwd
+    return f(q, k, v, d, o, si, so, B, H, N, dk, dv, C, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_chunk_validation(L, gated):
+    c = lambda **kw: chunk(L, gated=gated, **kw)  # noqa: E731
+    assert c(dt=7) == ERR_DTYPE
+    assert c(B=-1) == ERR_SHAPE
+    assert c(N=-3) == ERR_SHAPE
+    assert c(dk=0) == ERR_SHAPE
+    assert c(C=0) == ERR_SHAPE
+    assert c(dk=257) == ERR_UNSUPPORTED
+    assert c(dv=2000) == ERR_UNSUPPORTED
+    assert c(q=None) == ERR_NULL
+    assert c(o=None) == ERR_NULL
+    assert c(d=None) == ERR_NULL
+    # output overlapping an input
+    assert c(o=FAKE + 100) == ERR_ALIAS
+    assert c(so=FAKE + 64 * MB) == ERR_ALIAS                 # state_out over k
+    assert c(si=FAKE + 300 * MB, so=FAKE + 300 * MB + 16) == ERR_ALIAS   # partial overlap
+    # gated long chunks on the generic (fp32) path need their cumsum in LDS
+    if gated:
+        assert c(N=4096, C=2048) == ERR_UNSUPPORTED
+    # bf16 matrix-core path with a split sequence needs workspace
+    need = L.retention_workspace_bytes(1, 2, 65536, 128, 128, 64, 1, int(gated))
+    assert need > 0
+    assert c(N=65536, dk=128, dv=128, C=64, dt=1) == ERR_WORKSPACE
+    assert c(N=65536, dk=128, dv=128, C=64, dt=1, ws=FAKE + 400 * MB, wsb=need - 1) == ERR_WORKSPACE
+
+
+def test_decode_validation(L):
+    f = L.retention_decode_step
+    args = dict(q=FAKE, k=FAKE + MB, v=FAKE + 2 * MB, d=FAKE + 3 * MB, s=FAKE + 4 * MB, o=FAKE + 8 * MB)
+
+    def call(B=2, H=2, dk=16, dv=16, dt=1, **kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["d"], a["s"], a["o"], B, H, dk, dv, dt, None)
+
+    assert call(dt=5) == ERR_DTYPE
+    assert call(B=-1) == ERR_SHAPE
+    assert call(dk=0) == ERR_SHAPE
+    assert call(dk=300) == ERR_UNSUPPORTED
+    assert call(s=None) == ERR_NULL
+    assert call(o=FAKE + 4 * MB + 8) == ERR_ALIAS       # o inside the state
+    assert call(s=FAKE + 2 * MB) == ERR_ALIAS            # state over v
+    assert call(B=0) == OK                               # empty: nothing to do, nothing launched
+    g = L.gated_retention_decode_step
+    assert g(FAKE, FAKE + MB, FAKE + 2 * MB, None, FAKE + 4 * MB, FAKE + 8 * MB, 2, 2, 16, 16, 1, None) == ERR_NULL
+
+
+def test_workspace_query(L):
+    # fp32 and generic shapes never need workspace
+    assert L.retention_workspace_bytes(1, 2, 64, 16, 16, 16, 0, 0) == 0
+    # a short sequence with enough (b,h) x column tiles runs unsplit
+    assert L.retention_workspace_bytes(4, 8, 2048, 256, 512, 64, 1, 0) == 0
+    # long sequences with few heads are split; workspace holds one fp32 state per segment
+    ws = L.retention_workspace_bytes(1, 16, 16384, 128, 128, 512, 1, 0)
+    assert ws >= 2 * 16 * 128 * 128 * 4
+    assert L.retention_workspace_bytes(2, 16, 8192, 128, 128, 64, 1, 1) >= 2 * 2 * 16 * 128 * 128 * 4
+    assert L.retention_workspace_bytes(-1, 2, 64, 16, 16, 16, 0, 0) == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    from retnet_retention_fwd_amd import retention_chunkwise_fwd
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        retention_chunkwise_fwd(q, q, q, torch.ones(1), 4)
