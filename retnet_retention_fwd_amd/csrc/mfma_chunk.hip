@@ -60,9 +60,6 @@ __device__ __forceinline__ f32x4_t mfma16(u16x8_t a, u16x8_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 16-byte unit swizzle of an LDS row (rows of >= 8 units).
-__device__ __forceinline__ int swz(int row) { return (row + (row >> 3)) & 7; }
-
 __device__ __forceinline__ u16x8_t lds16(const char* base, int byte_off) {
     return *reinterpret_cast<const u16x8_t*>(base + byte_off);
 }
@@ -74,117 +71,107 @@ __device__ __forceinline__ u16x8_t cat(u16x4_t a, u16x4_t b) {
 }
 __device__ __forceinline__ uint16_t bf(float x) { return f32_to_bf16(x); }
 
-// Byte offset of (row, 16-byte unit) in a token-major tile with DK columns.
-template <int DK>
-__device__ __forceinline__ int tm_off(int row, int unit) {
-    return row * (DK * 2) + ((unit ^ swz(row)) << 4);
-}
-// Byte offset of (dim row, 16-byte unit of 8 tokens) in a dimension-major tile (64 tokens).
-__device__ __forceinline__ int dm_off(int row, int unit) {
-    return row * (kBlk * 2) + ((unit ^ swz(row)) << 4);
+// Raw hardware 2^x (v_exp_f32).  Every argument here is <= 0 or a masked lane, and
+// results below the fp32 normal range may flush to zero, which is harmless for decays.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, result lane
+// i, element j is the (i%4)-th 16-bit value at the address given by lane 4j + i/4.
+// So if lane 4j+q of a group points at row t_j, columns c0+4q..c0+4q+3 of a row-major
+// tile, lane i receives that tile's column c0+i at rows t_0..t_3.
+__device__ __forceinline__ u16x4_t lds_tr(const char* base, int byte_off) {
+    const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((lds_char_t*)(base) + byte_off));
+    return __builtin_bit_cast(u16x4_t, r);
 }
 
-__device__ __forceinline__ u16x8_t gload16(const bf16_t* p) {
-    return *reinterpret_cast<const u16x8_t*>(p);
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
+// s_barrier.  (__syncthreads() also waits for outstanding global loads, which would
+// stall on the asynchronous prefetch of the next block.)  The memory clobber keeps the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 8x8 transpose of 16-bit values: out[i][j] = in[j][i].
-__device__ __forceinline__ void transpose8(const u16x8_t (&in)[8], u16x8_t (&out)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        out[i] = u16x8_t{in[0][i], in[1][i], in[2][i], in[3][i], in[4][i], in[5][i], in[6][i], in[7][i]};
+// Asynchronous 16-byte-per-lane copy global -> LDS: lane l's 16 bytes land at
+// lds_base + 16 l (lds_base is wave-uniform).
+__device__ __forceinline__ void g2lds16(const bf16_t* gsrc, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)((lds_char_t*)lds_base), 16, 0, 0);
+}
+
+// Row swizzles (XOR of the 16-byte unit index).  Q rows: 4-bit (16 consecutive rows
+// hit distinct units, so the 8-byte cross-term reads are conflict free).  K and V rows:
+// 2(r&3) | ((r>>2)&1), which keeps 8 consecutive rows distinct (16-byte reads) and
+// makes the 4 rows read by one 16-lane group of a transpose read hit distinct
+// 32-byte pairs.
+template <int UPR>
+__device__ __forceinline__ int swz_q(int r) { return r & ((UPR >= 16 ? 16 : 8) - 1); }
+__device__ __forceinline__ int swz_kv(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int RB>   // row bytes
+__device__ __forceinline__ int q_off(int row, int unit) {
+    return row * RB + ((unit ^ swz_q<RB / 16>(row)) << 4);
+}
+template <int RB>
+__device__ __forceinline__ int kv_off(int row, int unit) {
+    return row * RB + ((unit ^ swz_kv(row)) << 4);
 }
 
 template <int DK, int DVT>
 struct Lds {
-    static constexpr int kQs = 0;
-    static constexpr int kKs = kQs + kBlk * DK * 2;
-    static constexpr int kKt = kKs + kBlk * DK * 2;
-    static constexpr int kVt = kKt + DK * kBlk * 2;
-    static constexpr int kP = kVt + DVT * kBlk * 2;
-    static constexpr int kOsStride = DVT * 2 + 16;
-    static constexpr int kOs = kP + 4 * 2 * 64 * 16;
-    static constexpr int kG = kOs + kBlk * kOsStride;
-    static constexpr int kWsum = kG + kMaxChunk * 4;
-    static constexpr int kBytes = kWsum + 16;
+    static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
+    static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
+    static constexpr int kQ = 0;                          // 2 buffers
+    static constexpr int kK = kQ + 2 * kQTile;            // 2 buffers
+    static constexpr int kV = kK + 2 * kKTile;            // 2 buffers
+    static constexpr int kP = kV + 2 * kVTile;            // P fragments [4 qt][2 key pairs][64][16 B]
+    static constexpr int kG = kP + 4 * 2 * 64 * 16;       // chunk log2 decays
+    static constexpr int kBytes = kG + kMaxChunk * 4;
 };
 
-// Stage a 64-token block of K into the token-major tile (and, if `both`, the
-// dimension-major tile).  Rows at or beyond `nvalid` are zero.  Each thread moves
-// 8x8 micro-tiles: 8 rows x one 16-byte unit.
-template <int DK>
-__device__ __forceinline__ void stage_k(char* Ks, char* Kt, const bf16_t* src, int nvalid, bool both) {
-    constexpr int UPR = DK / 8;  // 16-byte units per row
-    for (int e = threadIdx.x; e < 8 * UPR; e += kThreads) {
-        const int rg = e & 7, u = e >> 3;
-        u16x8_t r[8];
+// Issue the asynchronous copy of one 64-row tile (row bytes RB) whose row r comes from
+// global row min(r, nvalid-1) of `src` (row stride `ld` elements).  Rows past the
+// valid length hold copies of the last valid row; every use masks them (zero scores,
+// zero decay weights, outputs not stored).
+template <int RB, bool QSWZ>
+__device__ __forceinline__ void issue_tile(char* tile, const bf16_t* src, int ld, int nvalid, int wave, int lane) {
+    constexpr int kChunks = kBlk * RB / 1024;           // 1 KB per wave instruction
+    static_assert(kChunks % kWaves == 0, "tile must split evenly over the waves");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = rg * 8 + j;
-            r[j] = row < nvalid ? gload16(src + static_cast<size_t>(row) * DK + u * 8) : u16x8_t{};
-            *reinterpret_cast<u16x8_t*>(Ks + tm_off<DK>(row, u)) = r[j];
-        }
-        if (both) {
-            u16x8_t t[8];
-            transpose8(r, t);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) *reinterpret_cast<u16x8_t*>(Kt + dm_off(u * 8 + i, rg)) = t[i];
-        }
+    for (int i = 0; i < kChunks / kWaves; ++i) {
+        const int c = wave + i * kWaves;
+        const int off = c * 1024 + lane * 16;
+        const int row = off / RB, p = (off % RB) >> 4;
+        const int u = p ^ (QSWZ ? swz_q<RB / 16>(row) : swz_kv(row));
+        const uint32_t grow = min(row, nvalid - 1);
+        g2lds16(src + grow * static_cast<uint32_t>(ld) + static_cast<uint32_t>(u) * 8u, tile + c * 1024);
     }
-}
-
-// Stage a 64-token block of Q (token-major only).
-template <int DK>
-__device__ __forceinline__ void stage_q(char* Qs, const bf16_t* src, int nvalid) {
-    constexpr int UPR = DK / 8;
-    for (int e = threadIdx.x; e < kBlk * UPR; e += kThreads) {
-        const int row = e / UPR, u = e % UPR;
-        const u16x8_t x = row < nvalid ? gload16(src + static_cast<size_t>(row) * DK + u * 8) : u16x8_t{};
-        *reinterpret_cast<u16x8_t*>(Qs + tm_off<DK>(row, u)) = x;
-    }
-}
-
-// Stage DVT columns of a 64-token block of V, dimension-major.
-template <int DVT>
-__device__ __forceinline__ void stage_v(char* Vt, const bf16_t* src, int ld, int nvalid) {
-    constexpr int UPR = DVT / 8;
-    for (int e = threadIdx.x; e < 8 * UPR; e += kThreads) {
-        const int rg = e & 7, u = e >> 3;
-        u16x8_t r[8], t[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = rg * 8 + j;
-            r[j] = row < nvalid ? gload16(src + static_cast<size_t>(row) * ld + u * 8) : u16x8_t{};
-        }
-        transpose8(r, t);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u16x8_t*>(Vt + dm_off(u * 8 + i, rg)) = t[i];
-    }
-}
-
-// Chunk-local log2 decays for the gated form: gl[j] = sum_{t<=j} g[t] * log2(e), j < L.
-// Positions L..kMaxChunk-1 repeat gl[L-1] (they are masked wherever they are used).
-__device__ __forceinline__ void gated_prefix(float* gl, float* wsum, const float* g, int L) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const float a0 = 2 * t < L ? g[2 * t] * kLog2e : 0.f;
-    const float a1 = 2 * t + 1 < L ? g[2 * t + 1] * kLog2e : 0.f;
-    float s = a0 + a1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(s, off, 64);
-        if (lane >= off) s += y;
-    }
-    if (lane == 63) wsum[wave] = s;
-    __syncthreads();
-    float pre = 0.f;
-    for (int w = 0; w < wave; ++w) pre += wsum[w];
-    const float excl = pre + s - (a0 + a1);
-    gl[2 * t] = excl + a0;
-    gl[2 * t + 1] = excl + a0 + a1;
-    __syncthreads();
 }
 
 enum Mode { kFull = 0, kStateOnly = 1 };
+
+// Position in the walk over a segment: chunk start cs, query block qb, key block kb.
+struct Step {
+    int cs, qb, kb;
+};
+
+// Advance to the next (chunk, query block, key block); false past the segment end.
+// The full pass visits key blocks 0..qb for each query block; the state pre-pass only
+// the diagonal one.
+template <int MODE>
+__device__ __forceinline__ bool next_step(Step& s, int t_end, int N, int C) {
+    const int L = min(C, N - s.cs);
+    const int nb = (L + kBlk - 1) / kBlk;
+    if (MODE == kFull && s.kb < s.qb) { ++s.kb; return true; }
+    if (s.qb + 1 < nb) { ++s.qb; s.kb = MODE == kFull ? 0 : s.qb; return true; }
+    s.cs += C;
+    s.qb = 0;
+    s.kb = 0;
+    return s.cs < t_end;
+}
 
 // Main kernel (MODE = kFull) and segment-state pre-pass (MODE = kStateOnly).
 //   s_init: incoming state; for nseg == 1 it is state_in (may be null = zeros) with
@@ -202,15 +189,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     constexpr int NT = DVT / 64;          // 16-column tiles per wave
     constexpr int DT = DK / 16;           // 16-row tiles of the state
     constexpr int KS = DK / 32;           // reduction steps over DK
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* Qs = smem + L_::kQs;
-    char* Ks = smem + L_::kKs;
-    char* Kt = smem + L_::kKt;
-    char* Vt = smem + L_::kVt;
-    char* Pf = smem + L_::kP;
-    char* Os = smem + L_::kOs;
-    float* gl = reinterpret_cast<float*>(smem + L_::kG);
-    float* wsum = reinterpret_cast<float*>(smem + L_::kWsum);
+    constexpr int QRB = L_::kQRow, VRB = L_::kVRow;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    char* const Pf = smem + L_::kP;
+    float* const gl = reinterpret_cast<float*>(smem + L_::kG);
 
     // ---- work item: XCD-aware order (consecutive launch ids rotate over the 8 XCDs;
     // give each XCD a contiguous range of work so a (b,h)'s column tiles share an L2).
@@ -225,6 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     const int l16 = lane & 15, g4 = lane >> 4;
     const int col0 = dvt * DVT;                         // first column of this tile
     const int wcol = wave * (DVT / kWaves);             // wave's first column in the tile
+    // transpose-read source coordinates of this lane within its 16-lane group
+    const int trj = l16 >> 2, trq = l16 & 3;
 
     const int t_begin = seg * seg_tokens;
     const int t_end = min(N, t_begin + seg_tokens);
@@ -234,6 +218,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     const size_t v_bh = static_cast<size_t>(bh) * N * dv;
     const size_t s_bh = static_cast<size_t>(bh) * DK * dv;
     const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
+    const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
+    const bf16_t* q_bh = q + qk_bh;
+    const bf16_t* k_bh = k + qk_bh;
+    const bf16_t* v_bh_p = v + v_bh + col0;
 
     // ---- incoming state
     f32x4_t S[DT][NT];
@@ -243,185 +231,238 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
             if (nseg > 1) src = s_init + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg;
             else if (s_init != nullptr) src = s_init + s_bh;
         }
+        const int cidx = col0 + wcol + l16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[dt][nt][i] = src ? src[static_cast<size_t>(dt * 16 + 4 * g4 + i) * dv + col0 + wcol + nt * 16 + l16] : 0.f;
+                    S[dt][nt][i] = src ? src[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] : 0.f;
     }
 
-    float seg_l2 = 0.f;   // log2 of the decay accumulated over the segment (pre-pass)
+    float seg_l2 = 0.f;      // log2 of the decay accumulated over the segment (pre-pass)
+    u16x8_t Sp[KS][NT];      // bf16 copy of the chunk's incoming state (B operand of Q S)
+    f32x4_t X[4][NT];        // output accumulators of the current query block
+    float gpre[8];           // prefetched log-decays of the next chunk (wave 0, gated)
 
-    for (int cs = t_begin; cs < t_end; cs += C) {
-        const int L = min(C, N - cs);
-        const int nb = (L + kBlk - 1) / kBlk;
-        if (GATED) gated_prefix(gl, wsum, decay + static_cast<size_t>(bh) * N + cs, L);
-        // log2 of the decay over chunk positions (l, j] and over [0, j]
-        auto l2d = [&](int j, int l) -> float { return GATED ? gl[j] - gl[l] : static_cast<float>(j - l) * lg; };
-        auto l2x = [&](int j) -> float { return GATED ? gl[j] : static_cast<float>(j + 1) * lg; };
-        const float l2chunk = l2x(L - 1);
+    // log2 of the decay over chunk positions (l, j] and over [0, j]
+    auto l2d = [&](int j, int l) -> float { return GATED ? gl[j] - gl[l] : static_cast<float>(j - l) * lg; };
+    auto l2x = [&](int j) -> float { return GATED ? gl[j] : static_cast<float>(j + 1) * lg; };
 
-        // old state as the bf16 B operand of Q S (slots -> rows {4g..4g+3, 16+4g..})
-        u16x8_t Sp[KS][NT];
-        if (MODE == kFull) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const f32x4_t a = S[2 * ks][nt], b = S[2 * ks + 1][nt];
-                    Sp[ks][nt] = u16x8_t{bf(a[0]), bf(a[1]), bf(a[2]), bf(a[3]), bf(b[0]), bf(b[1]), bf(b[2]), bf(b[3])};
-                }
+    int qbuf = 0, kvbuf = 0;
+    // issue the asynchronous loads of step s into buffers (qb_, kvb_)
+    auto issue = [&](const Step& s, int qb_, int kvb_) {
+        const int L = min(C, N - s.cs);
+        const int k0 = s.cs + s.kb * kBlk;
+        const int nk = min(kBlk, L - s.kb * kBlk);
+        if (MODE == kFull && s.kb == 0) {
+            const int q0 = s.cs + s.qb * kBlk;
+            issue_tile<QRB, true>(smem + L_::kQ + qb_ * L_::kQTile, q_bh + static_cast<size_t>(q0) * DK, DK,
+                                  min(kBlk, L - s.qb * kBlk), wave, lane);
         }
-        // S <- 2^(G_{L-1}) S; block contributions are added below
-        {
-            const float c = exp2f(l2chunk);
+        issue_tile<QRB, false>(smem + L_::kK + kvb_ * L_::kKTile, k_bh + static_cast<size_t>(k0) * DK, DK, nk, wave, lane);
+        issue_tile<VRB, false>(smem + L_::kV + kvb_ * L_::kVTile, v_bh_p + static_cast<size_t>(k0) * dv, dv, nk, wave, lane);
+        if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
+            const float* gs = g_bh + s.cs;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, L - 1)];
+        }
+    };
+
+    int pend_q0 = -1, pend_nq = 0;   // rows of a finished query block not yet stored
+    auto store_pending = [&]() {
+        if (MODE != kFull || pend_q0 < 0) return;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = mt * 16 + 4 * g4 + i;
+                if (row < pend_nq) {
+                    bf16_t* dst = o + v_bh + static_cast<size_t>(pend_q0 + row) * dv + col0 + wcol + l16;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) dst[nt * 16] = bf(X[mt][nt][i]);
+                }
+            }
+        pend_q0 = -1;
+    };
+
+    Step cur{t_begin, 0, 0};
+    issue(cur, 0, 0);
+
+    while (true) {
+        __builtin_amdgcn_s_waitcnt(0);   // this step's tiles (issued one step ago) have landed
+        __syncthreads();
+        const int L = min(C, N - cur.cs);
+        const int qb = cur.qb, kb = cur.kb;
+        const bool diag = kb == qb;
+        if (qb == 0 && kb == 0) {
+            // start of a chunk: decays, bf16 snapshot of the old state, S <- 2^(G_{L-1}) S
+            if (GATED) {
+                if (wave == 0) {
+                    float run = 0.f, loc[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        run += lane * 8 + i < L ? gpre[i] * kLog2e : 0.f;
+                        loc[i] = run;
+                    }
+                    float incl = run;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(incl, off, 64);
+                        if (lane >= off) incl += y;
+                    }
+                    const float base = incl - run;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) gl[lane * 8 + i] = base + loc[i];
+                }
+                lds_barrier();
+            }
+            const float l2chunk = l2x(L - 1);
+            if (MODE == kFull) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const f32x4_t a = S[2 * ks][nt], b = S[2 * ks + 1][nt];
+                        Sp[ks][nt] = u16x8_t{bf(a[0]), bf(a[1]), bf(a[2]), bf(a[3]), bf(b[0]), bf(b[1]), bf(b[2]), bf(b[3])};
+                    }
+            }
+            const float c = exp2_fast(l2chunk);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= c;
+            seg_l2 += l2chunk;
         }
-        seg_l2 += l2chunk;
 
-        for (int qb = 0; qb < nb; ++qb) {
-            const int q0 = cs + qb * kBlk;                 // first token of the query block
-            const int nq = min(kBlk, L - qb * kBlk);
-            f32x4_t X[4][NT];                              // output accumulators, rows of block qb
-            if (MODE == kFull) {
-                stage_q<DK>(Qs, q + qk_bh + static_cast<size_t>(q0) * DK, nq);
-            }
-            for (int kb = (MODE == kFull ? 0 : qb); kb <= qb; ++kb) {
-                const bool diag = kb == qb;
-                const int k0 = cs + kb * kBlk;
-                const int nk = min(kBlk, L - kb * kBlk);
-                if (MODE == kFull || diag)
-                    stage_k<DK>(Ks, Kt, k + qk_bh + static_cast<size_t>(k0) * DK, nk, diag);
-                stage_v<DVT>(Vt, v + v_bh + static_cast<size_t>(k0) * dv + col0, dv, nk);
-                __syncthreads();
+        Step nxt = cur;
+        const bool has_next = next_step<MODE>(nxt, t_end, N, C);
+        const int nqbuf = (MODE == kFull && nxt.kb == 0) ? qbuf ^ 1 : qbuf;
+        if (has_next) issue(nxt, nqbuf, kvbuf ^ 1);
+        store_pending();
 
-                if (MODE == kFull) {
-                    if (kb == 0) {
-                        // cross-chunk term X = diag(2^G) (Q S_prev), rows of block qb
-#pragma unroll
-                        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt) X[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                            const int row = mt * 16 + l16;
-#pragma unroll
-                            for (int ks = 0; ks < KS; ++ks) {
-                                const int u0 = ks * 4 + (g4 >> 1), half = (g4 & 1) * 8;
-                                const u16x8_t a = cat(lds8(Qs, tm_off<DK>(row, u0) + half),
-                                                      lds8(Qs, tm_off<DK>(row, u0 + 2) + half));
-#pragma unroll
-                                for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, Sp[ks][nt], X[mt][nt]);
-                            }
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int j = qb * kBlk + mt * 16 + 4 * g4 + i;
-                                const float xi = j < L ? exp2f(l2x(j)) : 0.f;
-#pragma unroll
-                                for (int nt = 0; nt < NT; ++nt) X[mt][nt][i] *= xi;
-                            }
-                        }
-                    }
-                    // scores of (query block qb, key block kb), 16x16 tiles split over waves
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        const int qt = t >> 2, kt = t & 3;
-                        if (((qt + kt) & 3) != wave) continue;
-                        char* dst = Pf + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8;
-                        if (diag && kt > qt) {
-                            *reinterpret_cast<u16x4_t*>(dst) = u16x4_t{};
-                            continue;
-                        }
-                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            const u16x8_t a = lds16(Ks, tm_off<DK>(kt * 16 + l16, ks * 4 + g4));
-                            const u16x8_t b = lds16(Qs, tm_off<DK>(qt * 16 + l16, ks * 4 + g4));
-                            acc = mfma16(a, b, acc);
-                        }
-                        const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
-                        u16x4_t p;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int l = kb * kBlk + kt * 16 + 4 * g4 + i;   // key (chunk-local)
-                            const bool keep = l <= j && l < L && j < L;
-                            p[i] = bf(keep ? acc[i] * exp2f(l2d(j, l)) : 0.f);
-                        }
-                        *reinterpret_cast<u16x4_t*>(dst) = p;
-                    }
-                    __syncthreads();
-                    // X += P V over the 64 keys of block kb
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            if (diag && 2 * ks > mt) continue;
-                            const u16x8_t a = lds16(Pf, ((mt * 2 + ks) * 64 + lane) * 16);
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt) {
-                                const int n = wcol + nt * 16 + l16;
-                                const int u0 = ks * 4 + (g4 >> 1), half = (g4 & 1) * 8;
-                                const u16x8_t b = cat(lds8(Vt, dm_off(n, u0) + half), lds8(Vt, dm_off(n, u0 + 2) + half));
-                                X[mt][nt] = mfma16(a, b, X[mt][nt]);
-                            }
-                        }
-                    }
-                }
-                if (diag) {
-                    // S += K^T (V (.) zeta) over the keys of block qb
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        u16x8_t b[NT];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            const int n = wcol + nt * 16 + l16;
-                            const u16x8_t raw = lds16(Vt, dm_off(n, ks * 4 + g4));
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
-                                const float z = l < L ? exp2f(l2d(L - 1, l)) : 0.f;
-                                b[nt][i] = bf(bf16_to_f32(raw[i]) * z);
-                            }
-                        }
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            const u16x8_t a = lds16(Kt, dm_off(dt * 16 + l16, ks * 4 + g4));
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt) S[dt][nt] = mfma16(a, b[nt], S[dt][nt]);
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-
-            if (MODE == kFull) {
-                // outputs of block qb: registers -> LDS -> coalesced 16-byte stores
+        const char* Qs = smem + L_::kQ + qbuf * L_::kQTile;
+        const char* Ks = smem + L_::kK + kvbuf * L_::kKTile;
+        const char* Vs = smem + L_::kV + kvbuf * L_::kVTile;
+        if (MODE == kFull) {
+            if (kb == 0) {
+                // cross-chunk term X = diag(2^G) (Q S_prev), rows of block qb
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
+                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = mt * 16 + 4 * g4 + i;
-                            const int c = wcol + nt * 16 + l16;
-                            *reinterpret_cast<uint16_t*>(Os + row * L_::kOsStride + c * 2) = bf(X[mt][nt][i]);
-                        }
-                __syncthreads();
-                constexpr int UPR = DVT / 8;
-                for (int e = tid; e < kBlk * UPR; e += kThreads) {
-                    const int row = e / UPR, u = e % UPR;
-                    if (row < nq) {
-                        const u16x8_t x = *reinterpret_cast<const u16x8_t*>(Os + row * L_::kOsStride + u * 16);
-                        *reinterpret_cast<u16x8_t*>(o + v_bh + static_cast<size_t>(q0 + row) * dv + col0 + u * 8) = x;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int u0 = ks * 4 + (g4 >> 1), half = (g4 & 1) * 8;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const int row = mt * 16 + l16;
+                        const u16x8_t a = cat(lds8(Qs, q_off<QRB>(row, u0) + half),
+                                              lds8(Qs, q_off<QRB>(row, u0 + 2) + half));
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, Sp[ks][nt], X[mt][nt]);
                     }
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = qb * kBlk + mt * 16 + 4 * g4 + i;
+                        const float xi = j < L ? exp2_fast(l2x(j)) : 0.f;
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) X[mt][nt][i] *= xi;
+                    }
+            }
+            // scores of (query block qb, key block kb): wave w owns the 16x16 tiles
+            // (qt, kt) with qt + kt = w (mod 4), which balances the causal diagonal block
+            for (int qt = 0; qt < 4; ++qt) {
+                const int kt = (wave - qt) & 3;
+                char* dst = Pf + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8;
+                if (diag && kt > qt) {
+                    *reinterpret_cast<u16x4_t*>(dst) = u16x4_t{};
+                    continue;
+                }
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u16x8_t a = lds16(Ks, kv_off<QRB>(kt * 16 + l16, ks * 4 + g4));
+                    const u16x8_t b = lds16(Qs, q_off<QRB>(qt * 16 + l16, ks * 4 + g4));
+                    acc = mfma16(a, b, acc);
+                }
+                const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
+                u16x4_t p;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int l = kb * kBlk + kt * 16 + 4 * g4 + i;   // key (chunk-local)
+                    const bool keep = l <= j && l < L && j < L;
+                    p[i] = bf(keep ? acc[i] * exp2_fast(l2d(j, l)) : 0.f);
+                }
+                *reinterpret_cast<u16x4_t*>(dst) = p;
+            }
+            lds_barrier();
+            // X += P V over the 64 keys of block kb; V fragments by transpose reads:
+            // slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u16x8_t b[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c0 = wcol + nt * 16 + 4 * trq;      // this lane's 4 source columns
+                    const int r0 = ks * 32 + 4 * g4 + trj;
+                    b[nt] = cat(lds_tr(Vs, kv_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
+                                lds_tr(Vs, kv_off<VRB>(r0 + 16, c0 >> 3) + (c0 & 7) * 2));
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (diag && 2 * ks > mt) continue;
+                    const u16x8_t a = lds16(Pf, ((mt * 2 + ks) * 64 + lane) * 16);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, b[nt], X[mt][nt]);
                 }
             }
         }
-        if (GATED) __syncthreads();   // gl is rewritten by the next chunk
+        if (diag) {
+            // S += K^T (V (.) zeta) over the keys of block qb; slots are keys
+            // 32ks + 8g .. 32ks + 8g + 7, gathered by transpose reads of K and V
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int r0 = ks * 32 + 8 * g4 + trj;
+                float z[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
+                    z[i] = l < L ? exp2_fast(l2d(L - 1, l)) : 0.f;
+                }
+                u16x8_t b[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c0 = wcol + nt * 16 + 4 * trq;
+                    const u16x8_t raw = cat(lds_tr(Vs, kv_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
+                                            lds_tr(Vs, kv_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) b[nt][i] = bf(bf16_to_f32(raw[i]) * z[i]);
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int d0 = dt * 16 + 4 * trq;
+                    const u16x8_t a = cat(lds_tr(Ks, kv_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
+                                          lds_tr(Ks, kv_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) S[dt][nt] = mfma16(a, b[nt], S[dt][nt]);
+                }
+            }
+        }
+        if (MODE == kFull && diag) {
+            pend_q0 = cur.cs + qb * kBlk;
+            pend_nq = min(kBlk, L - qb * kBlk);
+        }
+        if (!has_next) break;
+        cur = nxt;
+        qbuf = nqbuf;
+        kvbuf ^= 1;
     }
+    store_pending();
 
     // ---- results
     float* dst = nullptr;
@@ -432,13 +473,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
         if (dvt == 0 && tid == 0) seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
     }
     if (dst != nullptr) {
+        const int cidx = col0 + wcol + l16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[static_cast<size_t>(dt * 16 + 4 * g4 + i) * dv + col0 + wcol + nt * 16 + l16] = S[dt][nt][i];
+                    dst[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] = S[dt][nt][i];
     }
 }
 
