@@ -67,9 +67,14 @@ __device__ __forceinline__ u16x4_t lds8(const char* base, int byte_off) {
     return *reinterpret_cast<const u16x4_t*>(base + byte_off);
 }
 __device__ __forceinline__ u16x8_t cat(u16x4_t a, u16x4_t b) {
-    return u16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ uint16_t bf(float x) { return f32_to_bf16(x); }
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// four floats -> four bf16 (round to nearest even), two per v_cvt_pk_bf16_f32
+__device__ __forceinline__ u16x4_t bf4(f32x4_t x) {
+    return __builtin_bit_cast(u16x4_t, __builtin_convertvector(x, bf16x4_t));
+}
 
 // Raw hardware 2^x (v_exp_f32).  Every argument here is <= 0 or a masked lane, and
 // results below the fp32 normal range may flush to zero, which is harmless for decays.
@@ -96,10 +101,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Asynchronous 16-byte-per-lane copy global -> LDS: lane l's 16 bytes land at
-// lds_base + 16 l (lds_base is wave-uniform).
-__device__ __forceinline__ void g2lds16(const bf16_t* gsrc, char* lds_base) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)((lds_char_t*)lds_base), 16, 0, 0);
+// Raw buffer resource (V#) over [base, base + bytes): 48-bit base, stride 0,
+// num_records = bytes, word 3 as for gfx9 raw buffers.  Offsets at or past `bytes`
+// read as zero instead of faulting.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    // every word is wave-uniform; readfirstlane keeps the descriptor in SGPRs
+    return u32x4_t{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a))),
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu))),
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bytes))), 0x00020000u};
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane
+// l reads rsrc + soffset + voffset and its 16 bytes land at LDS byte lds_addr + 16 l
+// (lds_addr and soffset are wave-uniform).  The instruction writes no registers; it is
+// issued from inline assembly so that the compiler does not treat it as aliasing every
+// later LDS read.  Completion is awaited explicitly (s_waitcnt vmcnt(0) followed by a
+// workgroup barrier) before the tile is read.
+__device__ __forceinline__ void buf2lds16(const u32x4_t& rsrc, uint32_t voffset, uint32_t soffset,
+                                          uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)(p)));
 }
 
 // Row swizzles (XOR of the 16-byte unit index).  Q rows: 4-bit (16 consecutive rows
@@ -132,25 +160,44 @@ struct Lds {
     static constexpr int kBytes = kG + kMaxChunk * 4;
 };
 
-// Issue the asynchronous copy of one 64-row tile (row bytes RB) whose row r comes from
-// global row min(r, nvalid-1) of `src` (row stride `ld` elements).  Rows past the
-// valid length hold copies of the last valid row; every use masks them (zero scores,
-// zero decay weights, outputs not stored).
+// Asynchronous copy of one 64-row tile (row bytes RB) of a row-major matrix with row
+// stride `sb` bytes.  Each wave issues kChunks/4 instructions of 1 KB; lane l of
+// instruction i fills LDS bytes [c*1024 + 16 l, +16) with c = wave + 4 i, i.e. row
+// (c*1024 + 16 l) / RB and the 16-byte unit whose swizzled position that is.
 template <int RB, bool QSWZ>
-__device__ __forceinline__ void issue_tile(char* tile, const bf16_t* src, int ld, int nvalid, int wave, int lane) {
-    constexpr int kChunks = kBlk * RB / 1024;           // 1 KB per wave instruction
+struct TileCopy {
+    static constexpr int kChunks = kBlk * RB / 1024;
+    static constexpr int kPerWave = kChunks / kWaves;
     static_assert(kChunks % kWaves == 0, "tile must split evenly over the waves");
-#pragma unroll
-    for (int i = 0; i < kChunks / kWaves; ++i) {
-        const int c = wave + i * kWaves;
-        const int off = c * 1024 + lane * 16;
-        const int row = off / RB, p = (off % RB) >> 4;
-        const int u = p ^ (QSWZ ? swz_q<RB / 16>(row) : swz_kv(row));
-        const uint32_t grow = min(row, nvalid - 1);
-        g2lds16(src + grow * static_cast<uint32_t>(ld) + static_cast<uint32_t>(u) * 8u, tile + c * 1024);
-    }
-}
+    uint32_t voff[kPerWave];     // byte offset of this lane's unit, relative to the block's first row
+    int row[kPerWave];
 
+    __device__ __forceinline__ void init(int sb, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const int c = wave + i * kWaves;
+            const int off = c * 1024 + lane * 16;
+            const int r = off / RB, p = (off % RB) >> 4;
+            const int u = p ^ (QSWZ ? swz_q<RB / 16>(r) : swz_kv(r));
+            row[i] = r;
+            voff[i] = static_cast<uint32_t>(r * sb + u * 16);
+        }
+    }
+    // Rows at or past `nrows` (the end of the tensor) re-read the last row, so every
+    // LDS row holds finite data; uses mask those rows.
+    __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes, int sb,
+                                          int nrows, int wave) const {
+        const bool full = nrows >= kBlk;
+        const uint32_t base = tile_lds + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            uint32_t vo = voff[i];
+            if (!full && row[i] >= nrows)
+                vo = vo - static_cast<uint32_t>((row[i] - (nrows - 1)) * sb);
+            buf2lds16(rsrc, vo, row0_bytes, base + i * kWaves * 1024u);
+        }
+    }
+};
 enum Mode { kFull = 0, kStateOnly = 1 };
 
 // Position in the walk over a segment: chunk start cs, query block qb, key block kb.
@@ -219,9 +266,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     const size_t s_bh = static_cast<size_t>(bh) * DK * dv;
     const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
-    const bf16_t* q_bh = q + qk_bh;
-    const bf16_t* k_bh = k + qk_bh;
-    const bf16_t* v_bh_p = v + v_bh + col0;
+    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * DK * 2);
+    const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
+    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
+    const uint32_t lds0 = lds_addr_of(smem);
+    TileCopy<QRB, true> qcp;
+    TileCopy<QRB, false> kcp;
+    TileCopy<VRB, false> vcp;
+    if (MODE == kFull) qcp.init(DK * 2, wave, lane);
+    kcp.init(DK * 2, wave, lane);
+    vcp.init(dv * 2, wave, lane);
 
     // ---- incoming state
     f32x4_t S[DT][NT];
@@ -241,14 +295,33 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     S[dt][nt][i] = src ? src[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] : 0.f;
     }
 
+    // The state registers hold S / 2^lk2: the chunk decay is applied by moving lk2 (a
+    // uniform scalar) instead of rescaling every element; new contributions are
+    // multiplied by 2^-lk2 and the query-side factor by 2^lkx.  When lk2 drops below
+    // -64 the registers are rescaled once and lk2 reset, which keeps them in range.
+    float lk2 = 0.f;         // log2 of the current state scale
+    float lkx = 0.f;         // log2 of the scale of the chunk's incoming state
     float seg_l2 = 0.f;      // log2 of the decay accumulated over the segment (pre-pass)
     u16x8_t Sp[KS][NT];      // bf16 copy of the chunk's incoming state (B operand of Q S)
     f32x4_t X[4][NT];        // output accumulators of the current query block
     float gpre[8];           // prefetched log-decays of the next chunk (wave 0, gated)
 
-    // log2 of the decay over chunk positions (l, j] and over [0, j]
-    auto l2d = [&](int j, int l) -> float { return GATED ? gl[j] - gl[l] : static_cast<float>(j - l) * lg; };
+    // log2 of the decay over chunk positions (l, j] and over [0, j] (gated form)
+    auto l2d = [&](int j, int l) -> float { return gl[j] - gl[l]; };
     auto l2x = [&](int j) -> float { return GATED ? gl[j] : static_cast<float>(j + 1) * lg; };
+
+    // Per-head form: gamma^(j-l) splits into a per-lane factor (the lane's offsets
+    // inside a 16x16 tile) and a uniform factor (the tile/block offset).
+    float fe[4], fx[4], fz[8];
+    bool dmask[4];           // inside a diagonal 16x16 tile: key <= query
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fe[i] = GATED ? 1.f : exp2_fast(static_cast<float>(l16 - 4 * g4 - i) * lg);
+        fx[i] = GATED ? 1.f : exp2_fast(static_cast<float>(4 * g4 + i) * lg);
+        dmask[i] = 4 * g4 + i <= l16;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fz[i] = GATED ? 1.f : exp2_fast(-static_cast<float>(8 * g4 + i) * lg);
 
     int qbuf = 0, kvbuf = 0;
     // issue the asynchronous loads of step s into buffers (qb_, kvb_)
@@ -256,13 +329,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
         const int L = min(C, N - s.cs);
         const int k0 = s.cs + s.kb * kBlk;
         const int nk = min(kBlk, L - s.kb * kBlk);
+        (void)nk;
         if (MODE == kFull && s.kb == 0) {
             const int q0 = s.cs + s.qb * kBlk;
-            issue_tile<QRB, true>(smem + L_::kQ + qb_ * L_::kQTile, q_bh + static_cast<size_t>(q0) * DK, DK,
-                                  min(kBlk, L - s.qb * kBlk), wave, lane);
+            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, DK * 2, N - q0, wave);
         }
-        issue_tile<QRB, false>(smem + L_::kK + kvb_ * L_::kKTile, k_bh + static_cast<size_t>(k0) * DK, DK, nk, wave, lane);
-        issue_tile<VRB, false>(smem + L_::kV + kvb_ * L_::kVTile, v_bh_p + static_cast<size_t>(k0) * dv, dv, nk, wave, lane);
+        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, DK * 2, N - k0, wave);
+        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, dv * 2, N - k0, wave);
         if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
             const float* gs = g_bh + s.cs;
 #pragma unroll
@@ -325,14 +398,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         const f32x4_t a = S[2 * ks][nt], b = S[2 * ks + 1][nt];
-                        Sp[ks][nt] = u16x8_t{bf(a[0]), bf(a[1]), bf(a[2]), bf(a[3]), bf(b[0]), bf(b[1]), bf(b[2]), bf(b[3])};
+                        Sp[ks][nt] = cat(bf4(a), bf4(b));
                     }
             }
-            const float c = exp2_fast(l2chunk);
+            lkx = lk2;
+            lk2 += l2chunk;
+            if (lk2 < -64.f) {
+                const float r = exp2_fast(lk2);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= c;
+                    for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= r;
+                lk2 = 0.f;
+            }
             seg_l2 += l2chunk;
         }
 
@@ -342,6 +420,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
         if (has_next) issue(nxt, nqbuf, kvbuf ^ 1);
         store_pending();
 
+        const bool fullq = (qb + 1) * kBlk <= L;     // no row of the blocks is past the chunk end
+        const bool fullk = (kb + 1) * kBlk <= L;
         const char* Qs = smem + L_::kQ + qbuf * L_::kQTile;
         const char* Ks = smem + L_::kK + kvbuf * L_::kKTile;
         const char* Vs = smem + L_::kV + kvbuf * L_::kVTile;
@@ -365,14 +445,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     }
                 }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt) {
+                    const float sx = GATED ? 0.f : exp2_fast(static_cast<float>(qb * kBlk + mt * 16 + 1) * lg + lkx);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int j = qb * kBlk + mt * 16 + 4 * g4 + i;
-                        const float xi = j < L ? exp2_fast(l2x(j)) : 0.f;
+                        float xi = GATED ? exp2_fast(gl[j] + lkx) : sx * fx[i];
+                        if (!fullq && j >= L) xi = 0.f;
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) X[mt][nt][i] *= xi;
                     }
+                }
             }
             // scores of (query block qb, key block kb): wave w owns the 16x16 tiles
             // (qt, kt) with qt + kt = w (mod 4), which balances the causal diagonal block
@@ -391,13 +474,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     acc = mfma16(a, b, acc);
                 }
                 const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
-                u16x4_t p;
+                const bool dtile = diag && kt == qt;
+                const float sd = GATED ? 0.f : exp2_fast(static_cast<float>((qb - kb) * kBlk + (qt - kt) * 16) * lg);
+                float pv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int l = kb * kBlk + kt * 16 + 4 * g4 + i;   // key (chunk-local)
-                    const bool keep = l <= j && l < L && j < L;
-                    p[i] = bf(keep ? acc[i] * exp2_fast(l2d(j, l)) : 0.f);
+                    bool keep = !dtile || dmask[i];
+                    if (!(fullq && fullk)) keep = keep && l < L && j < L;
+                    const float w = GATED ? exp2_fast(l2d(j, l)) : sd * fe[i];
+                    pv[i] = keep ? acc[i] * w : 0.f;
                 }
+                const u16x4_t p = bf4(f32x4_t{pv[0], pv[1], pv[2], pv[3]});
                 *reinterpret_cast<u16x4_t*>(dst) = p;
             }
             lds_barrier();
@@ -428,11 +516,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int r0 = ks * 32 + 8 * g4 + trj;
+                // zeta_l / 2^lk2: decay from key l to the chunk end, in the state's scale
+                const float sz = GATED ? 0.f : exp2_fast(static_cast<float>(L - 1 - kb * kBlk - ks * 32) * lg - lk2);
                 float z[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
-                    z[i] = l < L ? exp2_fast(l2d(L - 1, l)) : 0.f;
+                    z[i] = GATED ? exp2_fast(l2d(L - 1, l) - lk2) : sz * fz[i];
+                    if (!fullk && l >= L) z[i] = 0.f;
                 }
                 u16x8_t b[NT];
 #pragma unroll
@@ -440,8 +531,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     const int c0 = wcol + nt * 16 + 4 * trq;
                     const u16x8_t raw = cat(lds_tr(Vs, kv_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
                                             lds_tr(Vs, kv_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
+                    f32x4_t lo, hi;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) b[nt][i] = bf(bf16_to_f32(raw[i]) * z[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        lo[i] = bf16_to_f32(raw[i]) * z[i];
+                        hi[i] = bf16_to_f32(raw[i + 4]) * z[i + 4];
+                    }
+                    b[nt] = cat(bf4(lo), bf4(hi));
                 }
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
@@ -474,13 +570,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     }
     if (dst != nullptr) {
         const int cidx = col0 + wcol + l16;
+        const float r = exp2_fast(lk2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] = S[dt][nt][i];
+                    dst[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] = S[dt][nt][i] * r;
     }
 }
 
