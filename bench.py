@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the retention operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+
+Headline workload (one "step" = one chunkwise forward over one batch, i.e. every stage
+of the chunkwise hot path: tile staging, decay generation, intra-chunk scores and
+P V, the cross-chunk term, the state carry, and the output store):
+    train_bf16: B=4 H=8 N=2048 d_k=256 d_v=512 chunk=64, bf16 in / fp32 accumulate,
+    gamma_h = 1 - 2^(-5-h).
+Throughput is tokens/s = B*N / step time, with inputs resident in HBM.  Several
+input sets are rotated so a step never finds its inputs in the 256 MB MALL left
+over from the previous step.
+
+Secondary lines (same JSON object, "secondary"): the recurrent decode step (batch
+128, H=32, d=128, 1024 consecutive steps, GB/s of the fp32 state stream), the
+long-sequence workload at chunk 128/256/512 and the gated workload.
+
+"roofline" describes the dominant kernel of the headline step: algorithmic bytes
+(Q, K, V read once, O written once) per launch / average launch time from HIP events
+on the launch stream, against 8 TB/s.  "traffic" is HBM bytes per launch from the
+committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the copy-kernel
+calibration factor, or null when the kernel source changed since it was taken.
+"cpu_baseline" times the fp64 oracle (recurrent form, numpy) on a bounded sample of
+the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunkwise retention fwd tokens/s & % MFMA peak; decode-step HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_bf16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "retnet_retention_fwd_amd", "csrc", "mfma_chunk.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def alg_bytes(B, H, N, dk, dv, gated=False, elem=2):
+    """Q, K, V read once and O written once (plus g for the gated form)."""
+    return B * H * N * ((2 * dk + 2 * dv) * elem + (4 if gated else 0))
+
+
+def alg_flops(B, H, N, dk, dv, C):
+    """Causal chunkwise flops: (C+1)(dk+dv) + 4 dk dv per token-head."""
+    return B * H * N * ((C + 1) * (dk + dv) + 4 * dk * dv)
+
+
+def time_steps(fn, steps, warmup, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / 1e3, wall     # seconds (events), seconds (host clock)
+
+
+def chunk_inputs(torch, B, H, N, dk, dv, gated, sets, seed):
+    """Seeded synthetic inputs on the GPU: Q,K,V ~ N(0,1)/sqrt(dk) in bf16; per-head
+    gammas or g = logsigmoid(x)/16.  `sets` independent copies to rotate through."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = []
+    s = 1.0 / math.sqrt(dk)
+    for _ in range(sets):
+        q = (torch.randn(B, H, N, dk, device="cuda", generator=g) * s).to(torch.bfloat16)
+        k = (torch.randn(B, H, N, dk, device="cuda", generator=g) * s).to(torch.bfloat16)
+        v = (torch.randn(B, H, N, dv, device="cuda", generator=g) * s).to(torch.bfloat16)
+        if gated:
+            d = torch.nn.functional.logsigmoid(torch.randn(B, H, N, device="cuda", generator=g)) / 16
+        else:
+            d = None
+        o = torch.empty(B, H, N, dv, device="cuda", dtype=torch.bfloat16)
+        out.append((q, k, v, d, o))
+    return out
+
+
+def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps, warmup, seed):
+    per_set = alg_bytes(B, H, N, dk, dv, gated)
+    sets = max(2, min(8, int(math.ceil(768e6 / per_set))))
+    data = chunk_inputs(torch, B, H, N, dk, dv, gated, sets, seed)
+    gm = torch.tensor(gammas, device="cuda", dtype=torch.float32) if not gated else None
+    code = 1
+    ws_bytes = R.workspace_bytes(B, H, N, dk, dv, C, code, gated)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q, k, v, d, o = data[i % sets]
+        if gated:
+            R.gated_retention_chunkwise_fwd(q, k, v, d, C, out=o, workspace=ws)
+        else:
+            R.retention_chunkwise_fwd(q, k, v, gm, C, out=o, workspace=ws)
+
+    t, wall = time_steps(step, steps, warmup, torch)
+    per = t / steps
+    nb = alg_bytes(B, H, N, dk, dv, gated)
+    fl = alg_flops(B, H, N, dk, dv, C)
+    return {
+        "workload": name, "B": B, "H": H, "N": N, "dk": dk, "dv": dv, "chunk": C,
+        "us_per_step": per * 1e6, "tokens_per_s": B * N / per,
+        "alg_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS,
+        "alg_TFLOPs": fl / per / 1e12, "mfma_frac": fl / per / 1e12 / BF16_PEAK_TFLOPS,
+        "input_sets": sets, "workspace_bytes": ws_bytes, "wall_s": wall,
+    }
+
+
+def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4):
+    """Recurrent decode: batch 128, H=32, d=128; S0 ~ N(0, 0.1^2) fp32; fresh bf16
+    q,k,v per step (pre-generated on the GPU); gamma_h = 1 - 2^(-5 - 7h/31)."""
+    B, H, d = 128, 32, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    S = torch.randn(B, H, d, d, device="cuda", generator=g) * 0.1
+    s = 1.0 / math.sqrt(d)
+    q = (torch.randn(steps_per_call, B, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
+    k = (torch.randn(steps_per_call, B, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
+    v = (torch.randn(steps_per_call, B, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
+    gm = torch.tensor([1.0 - 2.0 ** (-5.0 - h * 7.0 / 31.0) for h in range(H)], device="cuda")
+    o = torch.empty(B, H, d, device="cuda", dtype=torch.bfloat16)
+
+    def step(i):
+        R.retention_decode_step(q[i % steps_per_call], k[i % steps_per_call], v[i % steps_per_call], gm, S, out=o)
+
+    t, _ = time_steps(step, steps_per_call, warm_calls * 16, torch)
+    per = t / steps_per_call
+    nb = B * H * (2 * d * d * 4 + 4 * d * 2)
+    return {"workload": "decode_bf16", "batch": B, "H": H, "dk": d, "dv": d, "steps": steps_per_call,
+            "us_per_step": per * 1e6, "tokens_per_s": B / per,
+            "hbm_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(max_seconds=15.0):
+    """fp64 oracle (recurrent form) on the headline workload's first T tokens of every
+    (b,h), T chosen so the run takes about `max_seconds`."""
+    import numpy as np
+    from oracle import retention_recurrent
+    from retnet_retention_fwd_amd import inputs as I
+    w = I.WORKLOADS["train_bf16"]
+    rng = np.random.default_rng(w.seed)
+    probe_T = 32
+    shp = (w.B, w.H)
+
+    def mk(T):
+        s = 1.0 / math.sqrt(w.dk)
+        q = rng.standard_normal(shp + (T, w.dk)) * s
+        k = rng.standard_normal(shp + (T, w.dk)) * s
+        v = rng.standard_normal(shp + (T, w.dv)) * s
+        return q, k, v
+
+    gm = I.gammas("train_bf16", w.H).astype(np.float64)
+    t0 = os.times()
+    w0 = time.perf_counter()
+    retention_recurrent(*mk(probe_T), gm)
+    probe = time.perf_counter() - w0
+    T = int(max(probe_T, min(w.N, probe_T * max_seconds / max(probe, 1e-6))))
+    t1 = os.times()
+    w1 = time.perf_counter()
+    retention_recurrent(*mk(T), gm)
+    wall = time.perf_counter() - w1
+    t2 = os.times()
+    cpu = (t2.user - t1.user) + (t2.system - t1.system)
+    threads = max(1, int(round(cpu / max(wall, 1e-9))))
+    del t0
+    return {"value": w.B * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"train_bf16 workload, all {w.B}x{w.H} (b,h), first {T} of {w.N} tokens, "
+                      f"fp64 numpy recurrence; {wall:.1f} s wall, {cpu:.1f} s CPU; "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed counter summary, or None if stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip decode/long/gated lines")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the operator on a single MI355X and has no "
+              "multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import retnet_retention_fwd_amd as R
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    R.lib()   # fail loudly if the HIP library is missing
+
+    if args.calib_copy:
+        n = 1 << 28   # 1 GiB of fp32
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n * 4}))
+        return
+
+    h = [1.0 - 2.0 ** (-5.0 - i) for i in range(8)]
+    head = run_chunk_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h, False,
+                              args.steps, args.warmup, seed=2)
+
+    secondary = {}
+    if not args.no_secondary:
+        secondary["decode_bf16"] = run_decode(torch, R)
+        g3 = [1.0 - 2.0 ** (-5.0 - i * 7.0 / 15.0) for i in range(16)]
+        for C in (512, 256, 128):
+            secondary[f"long_bf16_C{C}"] = run_chunk_workload(torch, R, "long_bf16", 1, 16, 16384, 128, 128, C, g3,
+                                                              False, 50, 5, seed=3)
+        secondary["gated_bf16"] = run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
+                                                     True, 50, 5, seed=5)
+
+    per = head["us_per_step"] / 1e6
+    nb = alg_bytes(4, 8, 2048, 256, 512)
+    achieved = nb / per / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(),
+            "kernel": "chunk_kernel<256,64,false,0> (one launch per step)",
+            "alg_bytes_per_launch": nb, "avg_launch_us": round(head["us_per_step"], 2),
+            "mfma_tflops": round(head["alg_TFLOPs"], 1), "mfma_frac": round(head["mfma_frac"], 4)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs at the workload's shapes, resident in HBM)",
+        "config": {"workload": "train_bf16 chunkwise retention forward", "B": 4, "H": 8, "N": 2048,
+                   "dk": 256, "dv": 512, "chunk": 64, "global_batch": 4, "seq_len": 2048,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    if secondary:
+        line["secondary"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                             for k, v in secondary.items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
