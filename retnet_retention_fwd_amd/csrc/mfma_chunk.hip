@@ -49,8 +49,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+// Waves per workgroup: each wave owns 16 state columns of a 64-column tile (4 waves)
+// or of a 128-column tile (8 waves, two per SIMD).
+template <int DVT>
+struct Waves {
+    static constexpr int kCount = DVT / 16;
+    static constexpr int kThreads = kCount * 64;
+};
 constexpr int kBlk = 64;       // tokens per LDS block
 constexpr int kMaxChunk = 512;
 constexpr int kTargetGroups = 256;
@@ -121,9 +126,12 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // workgroup barrier) before the tile is read.
 __device__ __forceinline__ void buf2lds16(const u32x4_t& rsrc, uint32_t voffset, uint32_t soffset,
                                           uint32_t lds_addr) {
+    // the scalar operands are wave-uniform; readfirstlane pins them to SGPRs
+    const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr)));
+    const uint32_t soff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(soffset)));
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
@@ -164,41 +172,47 @@ struct Lds {
 // stride `sb` bytes.  Each wave issues kChunks/4 instructions of 1 KB; lane l of
 // instruction i fills LDS bytes [c*1024 + 16 l, +16) with c = wave + 4 i, i.e. row
 // (c*1024 + 16 l) / RB and the 16-byte unit whose swizzled position that is.
-template <int RB, bool QSWZ>
+template <int RB, bool QSWZ, int NW>
 struct TileCopy {
     static constexpr int kChunks = kBlk * RB / 1024;
-    static constexpr int kPerWave = kChunks / kWaves;
-    static_assert(kChunks % kWaves == 0, "tile must split evenly over the waves");
+    static constexpr int kPerWave = kChunks / NW;
+    static_assert(kChunks % NW == 0, "tile must split evenly over the waves");
     uint32_t voff[kPerWave];     // byte offset of this lane's unit, relative to the block's first row
-    int row[kPerWave];
 
     __device__ __forceinline__ void init(int sb, int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            const int c = wave + i * kWaves;
+            const int c = wave + i * NW;
             const int off = c * 1024 + lane * 16;
             const int r = off / RB, p = (off % RB) >> 4;
             const int u = p ^ (QSWZ ? swz_q<RB / 16>(r) : swz_kv(r));
-            row[i] = r;
             voff[i] = static_cast<uint32_t>(r * sb + u * 16);
         }
     }
     // Rows at or past `nrows` (the end of the tensor) re-read the last row, so every
     // LDS row holds finite data; uses mask those rows.
     __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes, int sb,
-                                          int nrows, int wave) const {
+                                          int nrows, int wave, int lane) const {
         const bool full = nrows >= kBlk;
         const uint32_t base = tile_lds + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             uint32_t vo = voff[i];
-            if (!full && row[i] >= nrows)
-                vo = vo - static_cast<uint32_t>((row[i] - (nrows - 1)) * sb);
-            buf2lds16(rsrc, vo, row0_bytes, base + i * kWaves * 1024u);
+            if (!full) {
+                const int r = ((wave + i * NW) * 1024 + lane * 16) / RB;
+                if (r >= nrows) vo = vo - static_cast<uint32_t>((r - (nrows - 1)) * sb);
+            }
+            buf2lds16(rsrc, vo, row0_bytes, base + i * NW * 1024u);
         }
     }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
+
+// The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
+// 0,4,5,8,9,10,12,13,14,15, then 1,2,3,6,7,11 (one 4-bit entry per slot).
+__device__ __forceinline__ int tile_order(int slot) {
+    return static_cast<int>((0xB76321FEDCA98540ULL >> (4 * slot)) & 15);
+}
 
 // Position in the walk over a segment: chunk start cs, query block qb, key block kb.
 struct Step {
@@ -227,13 +241,14 @@ __device__ __forceinline__ bool next_step(Step& s, int t_end, int N, int C) {
 //   seg_out (pre-pass): local final state of each segment, same layout as s_init;
 //           seg_log2 (pre-pass): log2 of each segment's total decay.
 template <int DK, int DVT, bool GATED, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
+__global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ decay, bf16_t* __restrict__ o, const float* __restrict__ s_init,
     float* __restrict__ state_out, float* __restrict__ seg_out, float* __restrict__ seg_log2, int H,
     int N, int dv, int C, int seg_tokens, int nseg, int ndvt, int total_groups) {
     using L_ = Lds<DK, DVT>;
-    constexpr int NT = DVT / 64;          // 16-column tiles per wave
+    constexpr int NW = Waves<DVT>::kCount;
+    constexpr int NT = 1;                 // 16-column tiles per wave
     constexpr int DT = DK / 16;           // 16-row tiles of the state
     constexpr int KS = DK / 32;           // reduction steps over DK
     constexpr int QRB = L_::kQRow, VRB = L_::kVRow;
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int col0 = dvt * DVT;                         // first column of this tile
-    const int wcol = wave * (DVT / kWaves);             // wave's first column in the tile
+    const int wcol = wave * 16;                         // wave's first column in the tile
     // transpose-read source coordinates of this lane within its 16-lane group
     const int trj = l16 >> 2, trq = l16 & 3;
 
@@ -270,12 +285,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
     const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
     const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
     const uint32_t lds0 = lds_addr_of(smem);
-    TileCopy<QRB, true> qcp;
-    TileCopy<QRB, false> kcp;
-    TileCopy<VRB, false> vcp;
+    TileCopy<QRB, true, NW> qcp;
+    TileCopy<QRB, false, NW> kcp;
+    TileCopy<VRB, false, NW> vcp;
     if (MODE == kFull) qcp.init(DK * 2, wave, lane);
     kcp.init(DK * 2, wave, lane);
     vcp.init(dv * 2, wave, lane);
+
+    // State accumulator element (dt, i) of lane l holds state row srow(dt, i): tiles 2s and
+    // 2s+1 together cover rows 32s..32s+31, with lane group g holding rows 32s+8g..32s+8g+7
+    // (tile 2s: +0..3, tile 2s+1: +4..7).  So the B operand of Q S built from tiles
+    // (2s, 2s+1) has 8 contiguous reduction rows, matching one 16-byte Q read.
+    auto srow = [&](int dt, int i) -> int { return 32 * (dt >> 1) + 8 * g4 + 4 * (dt & 1) + i; };
 
     // ---- incoming state
     f32x4_t S[DT][NT];
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[dt][nt][i] = src ? src[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] : 0.f;
+                    S[dt][nt][i] = src ? src[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)] : 0.f;
     }
 
     // The state registers hold S / 2^lk2: the chunk decay is applied by moving lk2 (a
@@ -332,10 +353,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
         (void)nk;
         if (MODE == kFull && s.kb == 0) {
             const int q0 = s.cs + s.qb * kBlk;
-            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, DK * 2, N - q0, wave);
+            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, DK * 2, N - q0, wave, lane);
         }
-        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, DK * 2, N - k0, wave);
-        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, dv * 2, N - k0, wave);
+        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, DK * 2, N - k0, wave, lane);
+        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, dv * 2, N - k0, wave, lane);
         if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
             const float* gs = g_bh + s.cs;
 #pragma unroll
@@ -434,12 +455,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     for (int nt = 0; nt < NT; ++nt) X[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int u0 = ks * 4 + (g4 >> 1), half = (g4 & 1) * 8;
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        const int row = mt * 16 + l16;
-                        const u16x8_t a = cat(lds8(Qs, q_off<QRB>(row, u0) + half),
-                                              lds8(Qs, q_off<QRB>(row, u0 + 2) + half));
+                        const u16x8_t a = lds16(Qs, q_off<QRB>(mt * 16 + l16, ks * 4 + g4));
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, Sp[ks][nt], X[mt][nt]);
                     }
@@ -457,10 +475,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                     }
                 }
             }
-            // scores of (query block qb, key block kb): wave w owns the 16x16 tiles
-            // (qt, kt) with qt + kt = w (mod 4), which balances the causal diagonal block
-            for (int qt = 0; qt < 4; ++qt) {
-                const int kt = (wave - qt) & 3;
+            // scores of (query block qb, key block kb): the 16 tiles (qt, kt) are listed
+            // causal ones first and dealt round-robin to the waves, which balances the
+            // diagonal block; tiles above the diagonal are written as zeros
+#pragma unroll
+            for (int s16 = 0; s16 < 16 / NW; ++s16) {
+                const int slot = wave + s16 * NW;
+                const int code = tile_order(slot);
+                const int qt = code >> 2, kt = code & 3;
                 char* dst = Pf + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8;
                 if (diag && kt > qt) {
                     *reinterpret_cast<u16x4_t*>(dst) = u16x4_t{};
@@ -541,7 +563,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
                 }
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int d0 = dt * 16 + 4 * trq;
+                    // result lane m must receive state row srow(dt, m%4 of group m/4):
+                    // source lane (j, q) reads dims 32(dt/2) + 8q + 4(dt&1) .. +3
+                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * (dt & 1);
                     const u16x8_t a = cat(lds_tr(Ks, kv_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
                                           lds_tr(Ks, kv_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
 #pragma unroll
@@ -577,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[static_cast<uint32_t>((dt * 16 + 4 * g4 + i) * dv + cidx + nt * 16)] = S[dt][nt][i] * r;
+                    dst[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)] = S[dt][nt][i] * r;
     }
 }
 
@@ -631,7 +655,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         // pre-pass: local final state of every segment but the last is needed; the
         // grid covers all segments so the launch shape matches the main pass.
         const int groups = bh * p.nseg * ndvt;
-        hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kStateOnly>), dim3(groups), dim3(kThreads), lds,
+        hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kStateOnly>), dim3(groups), dim3(Waves<DVT>::kThreads), lds,
                            stream, q, k, v, a.decay, o, nullptr, nullptr, segbuf, segl2, a.H, a.N,
                            a.dv, a.chunk, seg_tokens, p.nseg, ndvt, groups);
         hipError_t e = hipGetLastError();
@@ -644,7 +668,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         s_init = segbuf;
     }
     const int groups = bh * p.nseg * ndvt;
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kFull>), dim3(groups), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kFull>), dim3(groups), dim3(Waves<DVT>::kThreads), lds, stream,
                        q, k, v, a.decay, o, s_init, a.state_out, nullptr, nullptr, a.H, a.N, a.dv,
                        a.chunk, seg_tokens, p.nseg, ndvt, groups);
     return hipGetLastError();
