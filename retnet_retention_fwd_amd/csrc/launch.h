@@ -48,6 +48,7 @@ struct MfmaPlan {
     int seg_chunks;   // chunks per segment (each workgroup walks one segment)
     int nseg;         // segments per (b,h)
     int dvt;          // state columns per workgroup
+    int nw;           // waves per workgroup
     size_t workspace_bytes;
 };
 MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated);

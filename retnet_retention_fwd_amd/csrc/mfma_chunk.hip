@@ -8,9 +8,9 @@
 //     S_new = 2^(G_{L-1}) S_prev + K^T (V (.) zeta),        zeta_l = 2^(G_{L-1} - G_l)
 // Per head, G_j = (j+1) log2(gamma); gated, G is the inclusive prefix sum of g*log2(e).
 //
-// Work decomposition.  A workgroup (4 waves) owns one (b,h), one segment of the
-// sequence and DVT state columns; it walks the segment's chunks in order, holding its
-// DK x DVT slice of S in fp32 MFMA accumulators.  Each wave owns DVT/4 columns.  A
+// Work decomposition.  A workgroup owns one (b,h), one segment of the sequence and
+// DVT state columns; it walks the segment's chunks in order, holding its DK x DVT slice
+// of S in fp32 MFMA accumulators spread over its waves (NT 16-column tiles each).  A
 // chunk is processed in 64-token blocks: for query block qb the scores against key
 // blocks kb <= qb are formed, decayed, rounded to bf16 and multiplied with V; the
 // state contribution of block qb is accumulated once the chunk's old state has been
@@ -25,10 +25,11 @@
 //     which is the A operand of P V when slots map to keys {4g..4g+3, 16+4g..16+4g+3};
 //   * the state accumulators hold S[4 rows][column l%16], which is the B operand of
 //     Q S when slots map to state rows the same way.
-// Q and K are kept token-major in LDS; K and V are also kept dimension-major (the
-// reduction over tokens needs token-contiguous slots), transposed in registers
-// while staging.  Rows are XOR-swizzled in 16-byte units so that staging writes and
-// fragment reads are free of bank conflicts.
+// Q, K and V blocks are copied token-major into LDS by asynchronous global->LDS loads,
+// one block ahead of use.  Operands that need tokens as the reduction slots (V for
+// P V, K^T and V for the state update) are gathered with LDS transpose reads.  Rows
+// are XOR-swizzled in 16-byte units so that every fragment read is free of bank
+// conflicts.
 //
 // Long sequences with few (b,h) are split into segments so that the grid fills the
 // chip: a pre-pass computes each segment's local final state (the same state
@@ -49,13 +50,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
-// Waves per workgroup: each wave owns 16 state columns of a 64-column tile (4 waves)
-// or of a 128-column tile (8 waves, two per SIMD).
-template <int DVT>
-struct Waves {
-    static constexpr int kCount = DVT / 16;
-    static constexpr int kThreads = kCount * 64;
-};
 constexpr int kBlk = 64;       // tokens per LDS block
 constexpr int kMaxChunk = 512;
 constexpr int kTargetGroups = 256;
@@ -107,8 +101,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Raw buffer resource (V#) over [base, base + bytes): 48-bit base, stride 0,
-// num_records = bytes, word 3 as for gfx9 raw buffers.  Offsets at or past `bytes`
-// read as zero instead of faulting.
+// num_records = bytes, word 3 as for gfx9 raw buffers.  A lane whose offset
+// (voffset + soffset) is at or past `bytes` reads zeros instead of memory; a load into
+// LDS then writes those zeros.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -138,41 +133,68 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)(p)));
 }
 
-// Row swizzles (XOR of the 16-byte unit index).  Q rows: 4-bit (16 consecutive rows
-// hit distinct units, so the 8-byte cross-term reads are conflict free).  K and V rows:
-// 2(r&3) | ((r>>2)&1), which keeps 8 consecutive rows distinct (16-byte reads) and
-// makes the 4 rows read by one 16-lane group of a transpose read hit distinct
-// 32-byte pairs.
+// Row swizzles: the 16-byte unit u of row r is stored at unit u ^ swz(r).  LDS serves
+// 256 bytes per clock from 64 four-byte banks: a 16-byte-per-lane read in groups of 16
+// lanes, an 8-byte (or 8-byte transpose) read in groups of 32 lanes; a group is
+// conflict free when its lanes cover distinct banks.
+//   Q and K (row = token, units over the head dimension): score and cross-term reads
+//   take one unit from 16 consecutive rows, so swz must be distinct on them; the
+//   transposed K reads of the state update take 8 bytes from rows {0..3, 8..11} (or
+//   {4..7, 12..15}) with the two 8-byte halves alternating over the lanes of a row, so
+//   rows of such a set must land in distinct 32-byte pairs (or opposite halves).
+//   With 16+ units per row, swz(r) = r with bits 1 and 2 exchanged does both; with 8
+//   units per row (two rows per bank cycle), (r >> 1) & 7.
+//   V (row = token, units over state columns): transposed reads take one 32-byte pair
+//   from rows {0..7} (P V) or {0..3, 8..11} (state update), so swz = 2 g(r) with
+//   g(r) = (r & 3) | (bit 2 ^ bit 3 of r) << 2 is distinct on both; with 8 units per
+//   row, 2 (g(r) >> 1).
 template <int UPR>
-__device__ __forceinline__ int swz_q(int r) { return r & ((UPR >= 16 ? 16 : 8) - 1); }
-__device__ __forceinline__ int swz_kv(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int swz_qk(int r) {
+    if (UPR >= 16) return (r & 9) | ((r & 4) >> 1) | ((r & 2) << 1);
+    return (r >> 1) & 7;
+}
+template <int UPR>
+__device__ __forceinline__ int swz_v(int r) {
+    const int g = (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+    return UPR >= 16 ? 2 * g : 2 * (g >> 1);
+}
 
 template <int RB>   // row bytes
-__device__ __forceinline__ int q_off(int row, int unit) {
-    return row * RB + ((unit ^ swz_q<RB / 16>(row)) << 4);
+__device__ __forceinline__ int qk_off(int row, int unit) {
+    return row * RB + ((unit ^ swz_qk<RB / 16>(row)) << 4);
 }
 template <int RB>
-__device__ __forceinline__ int kv_off(int row, int unit) {
-    return row * RB + ((unit ^ swz_kv(row)) << 4);
+__device__ __forceinline__ int v_off(int row, int unit) {
+    return row * RB + ((unit ^ swz_v<RB / 16>(row)) << 4);
 }
 
-template <int DK, int DVT>
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64 lanes][16 B]
+
+// LDS layout: double-buffered Q, K and V blocks, the P fragments of the current block
+// pair and (gated) the chunk's log2 decays.  When the buffers leave no room for P
+// (kPInK), P is written into the current K buffer once every wave is done with K.
+template <int DK, int DVT, bool GATED>
 struct Lds {
     static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
     static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
     static constexpr int kQ = 0;                          // 2 buffers
     static constexpr int kK = kQ + 2 * kQTile;            // 2 buffers
     static constexpr int kV = kK + 2 * kKTile;            // 2 buffers
-    static constexpr int kP = kV + 2 * kVTile;            // P fragments [4 qt][2 key pairs][64][16 B]
-    static constexpr int kG = kP + 4 * 2 * 64 * 16;       // chunk log2 decays
-    static constexpr int kBytes = kG + kMaxChunk * 4;
+    static constexpr int kEnd = kV + 2 * kVTile;
+    static constexpr int kGBytes = GATED ? kMaxChunk * 4 : 0;
+    static constexpr bool kPInK = kEnd + kPBytes + kGBytes > kLdsBytes;
+    static constexpr int kP = kPInK ? 0 : kEnd;           // unused when kPInK
+    static constexpr int kG = kPInK ? kEnd : kEnd + kPBytes;
+    static constexpr int kBytes = kG + kGBytes;
+    static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
 
 // Asynchronous copy of one 64-row tile (row bytes RB) of a row-major matrix with row
 // stride `sb` bytes.  Each wave issues kChunks/4 instructions of 1 KB; lane l of
 // instruction i fills LDS bytes [c*1024 + 16 l, +16) with c = wave + 4 i, i.e. row
 // (c*1024 + 16 l) / RB and the 16-byte unit whose swizzled position that is.
-template <int RB, bool QSWZ, int NW>
+template <int RB, bool VSWZ, int NW>
 struct TileCopy {
     static constexpr int kChunks = kBlk * RB / 1024;
     static constexpr int kPerWave = kChunks / NW;
@@ -185,25 +207,17 @@ struct TileCopy {
             const int c = wave + i * NW;
             const int off = c * 1024 + lane * 16;
             const int r = off / RB, p = (off % RB) >> 4;
-            const int u = p ^ (QSWZ ? swz_q<RB / 16>(r) : swz_kv(r));
+            const int u = p ^ (VSWZ ? swz_v<RB / 16>(r) : swz_qk<RB / 16>(r));
             voff[i] = static_cast<uint32_t>(r * sb + u * 16);
         }
     }
-    // Rows at or past `nrows` (the end of the tensor) re-read the last row, so every
-    // LDS row holds finite data; uses mask those rows.
-    __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes, int sb,
-                                          int nrows, int wave, int lane) const {
-        const bool full = nrows >= kBlk;
+    // Rows past the end of the tensor lie outside the buffer's range and land in LDS
+    // as zeros, so every LDS row holds finite data; uses mask those rows.
+    __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes,
+                                          int wave) const {
         const uint32_t base = tile_lds + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
 #pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            uint32_t vo = voff[i];
-            if (!full) {
-                const int r = ((wave + i * NW) * 1024 + lane * 16) / RB;
-                if (r >= nrows) vo = vo - static_cast<uint32_t>((r - (nrows - 1)) * sb);
-            }
-            buf2lds16(rsrc, vo, row0_bytes, base + i * NW * 1024u);
-        }
+        for (int i = 0; i < kPerWave; ++i) buf2lds16(rsrc, voff[i], row0_bytes, base + i * NW * 1024u);
     }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
@@ -235,25 +249,28 @@ __device__ __forceinline__ bool next_step(Step& s, int t_end, int N, int C) {
 }
 
 // Main kernel (MODE = kFull) and segment-state pre-pass (MODE = kStateOnly).
+// ONEBLK: every chunk is a single block (chunk <= 64), so each step starts a chunk and
+// the cross term can read the old state straight from the accumulators; no bf16
+// snapshot of the state is kept, which frees registers for wider column tiles.
 //   s_init: incoming state; for nseg == 1 it is state_in (may be null = zeros) with
 //           (b,h) stride dk*dv; for nseg > 1 it is the scanned workspace with
 //           (b,h, seg) stride dk*dv.  The pre-pass starts from zero.
 //   seg_out (pre-pass): local final state of each segment, same layout as s_init;
 //           seg_log2 (pre-pass): log2 of each segment's total decay.
-template <int DK, int DVT, bool GATED, int MODE>
-__global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
+__global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ decay, bf16_t* __restrict__ o, const float* __restrict__ s_init,
     float* __restrict__ state_out, float* __restrict__ seg_out, float* __restrict__ seg_log2, int H,
     int N, int dv, int C, int seg_tokens, int nseg, int ndvt, int total_groups) {
-    using L_ = Lds<DK, DVT>;
-    constexpr int NW = Waves<DVT>::kCount;
-    constexpr int NT = 1;                 // 16-column tiles per wave
+    using L_ = Lds<DK, DVT, GATED>;
+    constexpr int NT = DVT / (16 * NW);   // 16-column tiles per wave
+    static_assert(NT >= 1 && NT * 16 * NW == DVT && 16 % NW == 0, "bad wave split");
     constexpr int DT = DK / 16;           // 16-row tiles of the state
     constexpr int KS = DK / 32;           // reduction steps over DK
     constexpr int QRB = L_::kQRow, VRB = L_::kVRow;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    char* const Pf = smem + L_::kP;
+    char* const Pfix = smem + L_::kP;
     float* const gl = reinterpret_cast<float*>(smem + L_::kG);
 
     // ---- work item: XCD-aware order (consecutive launch ids rotate over the 8 XCDs;
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int col0 = dvt * DVT;                         // first column of this tile
-    const int wcol = wave * 16;                         // wave's first column in the tile
+    const int wcol = wave * 16 * NT;                    // wave's first column in the tile
     // transpose-read source coordinates of this lane within its 16-lane group
     const int trj = l16 >> 2, trq = l16 & 3;
 
@@ -285,18 +302,20 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
     const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
     const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
     const uint32_t lds0 = lds_addr_of(smem);
-    TileCopy<QRB, true, NW> qcp;
+    TileCopy<QRB, false, NW> qcp;
     TileCopy<QRB, false, NW> kcp;
-    TileCopy<VRB, false, NW> vcp;
+    TileCopy<VRB, true, NW> vcp;
     if (MODE == kFull) qcp.init(DK * 2, wave, lane);
     kcp.init(DK * 2, wave, lane);
     vcp.init(dv * 2, wave, lane);
 
     // State accumulator element (dt, i) of lane l holds state row srow(dt, i): tiles 2s and
     // 2s+1 together cover rows 32s..32s+31, with lane group g holding rows 32s+8g..32s+8g+7
-    // (tile 2s: +0..3, tile 2s+1: +4..7).  So the B operand of Q S built from tiles
-    // (2s, 2s+1) has 8 contiguous reduction rows, matching one 16-byte Q read.
-    auto srow = [&](int dt, int i) -> int { return 32 * (dt >> 1) + 8 * g4 + 4 * (dt & 1) + i; };
+    // (even g: tile 2s +0..3, tile 2s+1 +4..7; odd g the other way round, so that the
+    // transposed K reads of one tile alternate 8-byte halves).  So the B operand of Q S
+    // built from tiles 2s and 2s+1 has 8 contiguous reduction rows, matching one 16-byte
+    // Q read.
+    auto srow = [&](int dt, int i) -> int { return 32 * (dt >> 1) + 8 * g4 + 4 * ((dt ^ g4) & 1) + i; };
 
     // ---- incoming state
     f32x4_t S[DT][NT];
@@ -316,6 +335,12 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
                     S[dt][nt][i] = src ? src[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)] : 0.f;
     }
 
+    // bf16 B operand of Q S from tiles 2ks, 2ks+1 (reduction rows 32ks+8g .. +7 in order)
+    auto state_b = [&](int ks, int nt) -> u16x8_t {
+        const u16x4_t a = bf4(S[2 * ks][nt]), b = bf4(S[2 * ks + 1][nt]);
+        return (g4 & 1) ? cat(b, a) : cat(a, b);
+    };
+
     // The state registers hold S / 2^lk2: the chunk decay is applied by moving lk2 (a
     // uniform scalar) instead of rescaling every element; new contributions are
     // multiplied by 2^-lk2 and the query-side factor by 2^lkx.  When lk2 drops below
@@ -323,7 +348,7 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
     float lk2 = 0.f;         // log2 of the current state scale
     float lkx = 0.f;         // log2 of the scale of the chunk's incoming state
     float seg_l2 = 0.f;      // log2 of the decay accumulated over the segment (pre-pass)
-    u16x8_t Sp[KS][NT];      // bf16 copy of the chunk's incoming state (B operand of Q S)
+    u16x8_t Sp[ONEBLK ? 1 : KS][NT];   // bf16 copy of the chunk's incoming state (B operand of Q S)
     f32x4_t X[4][NT];        // output accumulators of the current query block
     float gpre[8];           // prefetched log-decays of the next chunk (wave 0, gated)
 
@@ -349,14 +374,12 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
     auto issue = [&](const Step& s, int qb_, int kvb_) {
         const int L = min(C, N - s.cs);
         const int k0 = s.cs + s.kb * kBlk;
-        const int nk = min(kBlk, L - s.kb * kBlk);
-        (void)nk;
         if (MODE == kFull && s.kb == 0) {
             const int q0 = s.cs + s.qb * kBlk;
-            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, DK * 2, N - q0, wave, lane);
+            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, wave);
         }
-        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, DK * 2, N - k0, wave, lane);
-        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, dv * 2, N - k0, wave, lane);
+        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, wave);
+        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, wave);
         if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
             const float* gs = g_bh + s.cs;
 #pragma unroll
@@ -381,6 +404,18 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
         pend_q0 = -1;
     };
 
+    // bf16 score tiles of this wave (slot s16 holds tile tile_order(wave + s16 NW)),
+    // written to LDS as P fragments [qt][key pair][lane][16 B]
+    u16x4_t Pr[16 / NW];
+    auto write_p = [&](char* base) {
+#pragma unroll
+        for (int s16 = 0; s16 < 16 / NW; ++s16) {
+            const int code = tile_order(wave + s16 * NW);
+            const int qt = code >> 2, kt = code & 3;
+            *reinterpret_cast<u16x4_t*>(base + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8) = Pr[s16];
+        }
+    };
+
     Step cur{t_begin, 0, 0};
     issue(cur, 0, 0);
 
@@ -388,7 +423,7 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
         __builtin_amdgcn_s_waitcnt(0);   // this step's tiles (issued one step ago) have landed
         __syncthreads();
         const int L = min(C, N - cur.cs);
-        const int qb = cur.qb, kb = cur.kb;
+        const int qb = ONEBLK ? 0 : cur.qb, kb = ONEBLK ? 0 : cur.kb;
         const bool diag = kb == qb;
         if (qb == 0 && kb == 0) {
             // start of a chunk: decays, bf16 snapshot of the old state, S <- 2^(G_{L-1}) S
@@ -413,25 +448,14 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
                 lds_barrier();
             }
             const float l2chunk = l2x(L - 1);
-            if (MODE == kFull) {
+            if (MODE == kFull && !ONEBLK) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const f32x4_t a = S[2 * ks][nt], b = S[2 * ks + 1][nt];
-                        Sp[ks][nt] = cat(bf4(a), bf4(b));
-                    }
+                    for (int nt = 0; nt < NT; ++nt) Sp[ks][nt] = state_b(ks, nt);
             }
             lkx = lk2;
             lk2 += l2chunk;
-            if (lk2 < -64.f) {
-                const float r = exp2_fast(lk2);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= r;
-                lk2 = 0.f;
-            }
             seg_l2 += l2chunk;
         }
 
@@ -457,9 +481,12 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        const u16x8_t a = lds16(Qs, q_off<QRB>(mt * 16 + l16, ks * 4 + g4));
+                        const u16x8_t a = lds16(Qs, qk_off<QRB>(mt * 16 + l16, ks * 4 + g4));
 #pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, Sp[ks][nt], X[mt][nt]);
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const u16x8_t b = ONEBLK ? state_b(ks, nt) : Sp[ONEBLK ? 0 : ks][nt];
+                            X[mt][nt] = mfma16(a, b, X[mt][nt]);
+                        }
                     }
                 }
 #pragma unroll
@@ -483,16 +510,13 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
                 const int slot = wave + s16 * NW;
                 const int code = tile_order(slot);
                 const int qt = code >> 2, kt = code & 3;
-                char* dst = Pf + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8;
-                if (diag && kt > qt) {
-                    *reinterpret_cast<u16x4_t*>(dst) = u16x4_t{};
-                    continue;
-                }
+                Pr[s16] = u16x4_t{};
+                if (diag && kt > qt) continue;
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const u16x8_t a = lds16(Ks, kv_off<QRB>(kt * 16 + l16, ks * 4 + g4));
-                    const u16x8_t b = lds16(Qs, q_off<QRB>(qt * 16 + l16, ks * 4 + g4));
+                    const u16x8_t a = lds16(Ks, qk_off<QRB>(kt * 16 + l16, ks * 4 + g4));
+                    const u16x8_t b = lds16(Qs, qk_off<QRB>(qt * 16 + l16, ks * 4 + g4));
                     acc = mfma16(a, b, acc);
                 }
                 const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
@@ -507,30 +531,19 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
                     const float w = GATED ? exp2_fast(l2d(j, l)) : sd * fe[i];
                     pv[i] = keep ? acc[i] * w : 0.f;
                 }
-                const u16x4_t p = bf4(f32x4_t{pv[0], pv[1], pv[2], pv[3]});
-                *reinterpret_cast<u16x4_t*>(dst) = p;
+                Pr[s16] = bf4(f32x4_t{pv[0], pv[1], pv[2], pv[3]});
             }
-            lds_barrier();
-            // X += P V over the 64 keys of block kb; V fragments by transpose reads:
-            // slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
+            if (!L_::kPInK) write_p(Pfix);
+        }
+        if (qb == 0 && kb == 0 && lk2 < -64.f) {
+            // rescale the registers once the state scale gets small (after the cross
+            // term, which reads them at the old scale)
+            const float r = exp2_fast(lk2);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                u16x8_t b[NT];
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int c0 = wcol + nt * 16 + 4 * trq;      // this lane's 4 source columns
-                    const int r0 = ks * 32 + 4 * g4 + trj;
-                    b[nt] = cat(lds_tr(Vs, kv_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
-                                lds_tr(Vs, kv_off<VRB>(r0 + 16, c0 >> 3) + (c0 & 7) * 2));
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    if (diag && 2 * ks > mt) continue;
-                    const u16x8_t a = lds16(Pf, ((mt * 2 + ks) * 64 + lane) * 16);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, b[nt], X[mt][nt]);
-                }
-            }
+                for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= r;
+            lk2 = 0.f;
         }
         if (diag) {
             // S += K^T (V (.) zeta) over the keys of block qb; slots are keys
@@ -551,8 +564,8 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const int c0 = wcol + nt * 16 + 4 * trq;
-                    const u16x8_t raw = cat(lds_tr(Vs, kv_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
-                                            lds_tr(Vs, kv_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
+                    const u16x8_t raw = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
+                                            lds_tr(Vs, v_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
                     f32x4_t lo, hi;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -564,12 +577,42 @@ __global__ __launch_bounds__(Waves<DVT>::kThreads, 1) void chunk_kernel(
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     // result lane m must receive state row srow(dt, m%4 of group m/4):
-                    // source lane (j, q) reads dims 32(dt/2) + 8q + 4(dt&1) .. +3
-                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * (dt & 1);
-                    const u16x8_t a = cat(lds_tr(Ks, kv_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
-                                          lds_tr(Ks, kv_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
+                    // source lane (j, q) reads dims 32(dt/2) + 8q + 4((dt^q)&1) .. +3
+                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * ((dt ^ trq) & 1);
+                    const u16x8_t a = cat(lds_tr(Ks, qk_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
+                                          lds_tr(Ks, qk_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[dt][nt] = mfma16(a, b[nt], S[dt][nt]);
+                }
+            }
+        }
+        if (MODE == kFull) {
+            // P goes to its own LDS area, or into the K buffer once no wave reads K
+            const char* Pf = Pfix;
+            if (L_::kPInK) {
+                lds_barrier();
+                write_p(const_cast<char*>(Ks));
+                Pf = Ks;
+            }
+            lds_barrier();
+            // X += P V over the 64 keys of block kb; V fragments by transpose reads:
+            // slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u16x8_t b[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c0 = wcol + nt * 16 + 4 * trq;      // this lane's 4 source columns
+                    const int r0 = ks * 32 + 4 * g4 + trj;
+                    b[nt] = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
+                                lds_tr(Vs, v_off<VRB>(r0 + 16, c0 >> 3) + (c0 & 7) * 2));
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    if (diag && 2 * ks > mt) continue;
+                    const u16x8_t a = lds16(Pf, ((mt * 2 + ks) * 64 + lane) * 16);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, b[nt], X[mt][nt]);
                 }
             }
         }
@@ -626,9 +669,9 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
     }
 }
 
-template <int DK, int DVT, bool GATED>
+template <int DK, int DVT, int NW, bool GATED, bool ONEBLK>
 hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
-    using L_ = Lds<DK, DVT>;
+    using L_ = Lds<DK, DVT, GATED>;
     const int ndvt = a.dv / DVT;
     const int bh = a.B * a.H;
     const int seg_tokens = p.seg_chunks * a.chunk;
@@ -639,9 +682,9 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
     const size_t lds = L_::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, GATED, kFull>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, GATED, kStateOnly>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, kStateOnly, ONEBLK>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
@@ -655,7 +698,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         // pre-pass: local final state of every segment but the last is needed; the
         // grid covers all segments so the launch shape matches the main pass.
         const int groups = bh * p.nseg * ndvt;
-        hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kStateOnly>), dim3(groups), dim3(Waves<DVT>::kThreads), lds,
+        hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, kStateOnly, ONEBLK>), dim3(groups), dim3(NW * 64), lds,
                            stream, q, k, v, a.decay, o, nullptr, nullptr, segbuf, segl2, a.H, a.N,
                            a.dv, a.chunk, seg_tokens, p.nseg, ndvt, groups);
         hipError_t e = hipGetLastError();
@@ -668,15 +711,24 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         s_init = segbuf;
     }
     const int groups = bh * p.nseg * ndvt;
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, GATED, kFull>), dim3(groups), dim3(Waves<DVT>::kThreads), lds, stream,
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>), dim3(groups), dim3(NW * 64), lds, stream,
                        q, k, v, a.decay, o, s_init, a.state_out, nullptr, nullptr, a.H, a.N, a.dv,
                        a.chunk, seg_tokens, p.nseg, ndvt, groups);
     return hipGetLastError();
 }
 
-int pick_dvt(int dk, int dv) {
-    if (dk == 256) return 64;
-    return dv % 128 == 0 ? 128 : 64;
+// State columns per workgroup and waves per workgroup for a head shape.
+// State columns per workgroup and waves per workgroup for a head shape.  Wider column
+// tiles cut the re-reads of Q and K (from L2 and from LDS) per output column; 8 waves
+// (two per SIMD) hide LDS and matrix-core latency better than 4 wider ones.  With
+// dk = 256 a 128-column tile fills the LDS (P then lives in the K buffer) and needs the
+// registers freed by single-block chunks.
+void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
+    if (dk == 256 && !gated && dv % 128 == 0 && chunk <= kBlk) { dvt = 128; nw = 8; return; }
+    if (dk == 256) { dvt = 64; nw = 4; return; }
+    if (dv % 128 == 0) { dvt = 128; nw = 8; return; }
+    dvt = 64;
+    nw = 4;
 }
 
 }  // namespace
@@ -689,9 +741,8 @@ bool mfma_chunk_supported(int dk, int dv, int chunk, bool bf16) {
 }
 
 MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated) {
-    (void)gated;
     MfmaPlan p{};
-    p.dvt = pick_dvt(dk, dv);
+    pick_tile(dk, dv, chunk, gated, p.dvt, p.nw);
     const long bh = static_cast<long>(B) * H;
     const long base = bh * (dv / p.dvt);
     const int nchunks = (N + chunk - 1) / chunk;
@@ -710,18 +761,25 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
 
 hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     // the kernel handles any chunk in [1, 512], including chunks that are not a
-    // multiple of its 64-token blocks
-    const ChunkArgs& b = a;
-#define RETN_SHAPE(DK, DVT)                                                     \
-    if (a.dk == DK && p.dvt == DVT)                                            \
-        return a.gated ? launch_shape<DK, DVT, true>(b, p, stream)              \
-                       : launch_shape<DK, DVT, false>(b, p, stream);
-    RETN_SHAPE(64, 64)
-    RETN_SHAPE(64, 128)
-    RETN_SHAPE(128, 64)
-    RETN_SHAPE(128, 128)
-    RETN_SHAPE(256, 64)
+    // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant
+    const bool one = a.chunk <= kBlk;
+#define RETN_SHAPE(DK, DVT, NW)                                                            \
+    if (a.dk == DK && p.dvt == DVT && p.nw == NW) {                                       \
+        if (a.gated)                                                                      \
+            return one ? launch_shape<DK, DVT, NW, true, true>(a, p, stream)              \
+                       : launch_shape<DK, DVT, NW, true, false>(a, p, stream);            \
+        return one ? launch_shape<DK, DVT, NW, false, true>(a, p, stream)                 \
+                   : launch_shape<DK, DVT, NW, false, false>(a, p, stream);               \
+    }
+    RETN_SHAPE(64, 64, 4)
+    RETN_SHAPE(64, 128, 8)
+    RETN_SHAPE(128, 64, 4)
+    RETN_SHAPE(128, 128, 8)
+    RETN_SHAPE(256, 64, 4)
 #undef RETN_SHAPE
+    // the gated form's decay array does not fit beside double-buffered 256 x 128 tiles
+    if (a.dk == 256 && p.dvt == 128 && p.nw == 8 && !a.gated && one)
+        return launch_shape<256, 128, 8, false, true>(a, p, stream);
     return hipErrorInvalidValue;
 }
 

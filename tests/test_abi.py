@@ -99,7 +99,7 @@ def test_workspace_query(L):
     # fp32 and generic shapes never need workspace
     assert L.retention_workspace_bytes(1, 2, 64, 16, 16, 16, 0, 0) == 0
     # a short sequence with enough (b,h) x column tiles runs unsplit
-    assert L.retention_workspace_bytes(4, 8, 2048, 256, 512, 64, 1, 0) == 0
+    assert L.retention_workspace_bytes(16, 16, 2048, 128, 128, 64, 1, 0) == 0
     # long sequences with few heads are split; workspace holds one fp32 state per segment
     ws = L.retention_workspace_bytes(1, 16, 16384, 128, 128, 512, 1, 0)
     assert ws >= 2 * 16 * 128 * 128 * 4

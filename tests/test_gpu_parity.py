@@ -97,6 +97,9 @@ SMALL = [
     (1, 1, 90, 128, 128, 37, "bf16", True, True),
     (1, 2, 1, 128, 128, 64, "bf16", False, True),        # N = 1
     (1, 2, 40, 128, 128, 512, "bf16", False, True),      # chunk > N
+    (1, 2, 250, 256, 256, 48, "bf16", False, True),      # dk 256, 128-column tiles, short chunk
+    (1, 2, 150, 256, 64, 64, "bf16", True, True),        # dk 256 gated, one block per chunk
+    (1, 1, 170, 64, 192, 40, "bf16", False, False),
 ]
 
 
@@ -119,6 +122,32 @@ def test_segmented_sequence(gated):
     say(("segmented", gated))
     assert R().workspace_bytes(B, H, N, dk, dv, C, 1, gated) > 0
     x = I.random_case(42, B, H, N, dk, dv, dtype="bf16", gated=gated, state_in=True)
+    o, S = run_chunk(x, C, gated, state_in=True)
+    ro, rS = oracle_chunk(x, gated, state_in=True)
+    assert rel(o, ro) <= TOL["bf16"]
+    assert rel(S, rS) <= TOL["bf16"]
+
+
+STRONG = [
+    # (B, H, N, dk, dv, chunk, gated): decays strong enough that the kernels' state
+    # scale is reset often and many decay factors underflow to zero
+    (1, 2, 300, 256, 256, 64, False),
+    (1, 2, 300, 256, 128, 64, True),
+    (1, 2, 300, 128, 128, 128, True),
+    (1, 2, 200, 64, 64, 40, True),
+    (1, 2, 260, 128, 64, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", STRONG, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}{}".format(*c[:6], "g" if c[6] else ""))
+def test_strong_decay(case):
+    B, H, N, dk, dv, C, gated = case
+    say(("strong", case))
+    x = I.random_case(sum(case[:6]) + 7, B, H, N, dk, dv, dtype="bf16", gated=gated, state_in=True,
+                      gamma_lo=0.05)
+    if gated:
+        rng = np.random.default_rng(N + dk)
+        x["g"] = I.to_dtype(I.logsigmoid(rng.standard_normal((B, H, N)) * 4.0), "f32")
     o, S = run_chunk(x, C, gated, state_in=True)
     ro, rS = oracle_chunk(x, gated, state_in=True)
     assert rel(o, ro) <= TOL["bf16"]
