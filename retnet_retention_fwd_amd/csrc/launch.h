@@ -49,6 +49,9 @@ struct MfmaPlan {
     int nseg;         // segments per (b,h)
     int dvt;          // state columns per workgroup
     int nw;           // waves per workgroup
+    int pre_dkt;      // state rows per workgroup of the segment-state pre-pass
+    int pre_dvt;      // state columns per workgroup of the pre-pass
+    int fuse_scan;    // 1: the main pass composes segment entry states itself
     size_t workspace_bytes;
 };
 MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated);

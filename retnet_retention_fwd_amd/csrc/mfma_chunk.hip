@@ -53,6 +53,9 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBlk = 64;       // tokens per LDS block
 constexpr int kMaxChunk = 512;
 constexpr int kTargetGroups = 256;
+// Up to this many segments the main pass composes its entry state from the local
+// segment states itself (segment s reads s of them); beyond, a scan kernel does it.
+constexpr int kFuseScanMax = 4;
 
 __device__ __forceinline__ f32x4_t mfma16(u16x8_t a, u16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -129,6 +132,21 @@ __device__ __forceinline__ void buf2lds16(const u32x4_t& rsrc, uint32_t voffset,
                  : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
+// Same for 4 bytes per lane: lane l's dword lands at LDS byte lds_addr + 4 l.
+__device__ __forceinline__ void buf2lds4(const u32x4_t& rsrc, uint32_t voffset, uint32_t soffset,
+                                         uint32_t lds_addr) {
+    const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr)));
+    const uint32_t soff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(soffset)));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)(p)));
 }
@@ -171,21 +189,25 @@ __device__ __forceinline__ int v_off(int row, int unit) {
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64 lanes][16 B]
 
-// LDS layout: double-buffered Q, K and V blocks, the P fragments of the current block
-// pair and (gated) the chunk's log2 decays.  When the buffers leave no room for P
-// (kPInK), P is written into the current K buffer once every wave is done with K.
-template <int DK, int DVT, bool GATED>
+// LDS layout: double-buffered Q (full pass only), NST buffers of K and V blocks, per
+// stage and wave a copy of the block's decays (gated pre-pass), the P fragments of the
+// current block pair and (gated) the chunk's log2 decays.  When the buffers leave no
+// room for P (kPInK), P is written into the current K buffer once every wave is done
+// with K.
+template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW>
 struct Lds {
     static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
     static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
-    static constexpr int kQ = 0;                          // 2 buffers
-    static constexpr int kK = kQ + 2 * kQTile;            // 2 buffers
-    static constexpr int kV = kK + 2 * kKTile;            // 2 buffers
-    static constexpr int kEnd = kV + 2 * kVTile;
+    static constexpr int kQ = 0;                          // 2 buffers (none without Q)
+    static constexpr int kK = kQ + (HASQ ? 2 * kQTile : 0);   // NST buffers
+    static constexpr int kV = kK + NST * kKTile;          // NST buffers
+    static constexpr int kGd = kV + NST * kVTile;         // [NST][NW][64] floats
+    static constexpr int kEnd = kGd + (!HASQ && GATED ? NST * NW * 256 : 0);
     static constexpr int kGBytes = GATED ? kMaxChunk * 4 : 0;
-    static constexpr bool kPInK = kEnd + kPBytes + kGBytes > kLdsBytes;
+    static constexpr bool kPInK = HASQ && kEnd + kPBytes + kGBytes > kLdsBytes;
+    static constexpr int kPSize = HASQ && !kPInK ? kPBytes : 0;
     static constexpr int kP = kPInK ? 0 : kEnd;           // unused when kPInK
-    static constexpr int kG = kPInK ? kEnd : kEnd + kPBytes;
+    static constexpr int kG = kEnd + kPSize;
     static constexpr int kBytes = kG + kGBytes;
     static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
@@ -221,6 +243,9 @@ struct TileCopy {
     }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
+// K/V stages: the pre-pass has no stores in its loop, so it can keep several block loads
+// in flight and count them with vmcnt; the main pass double-buffers.
+constexpr int stages_for(int mode) { return mode == kFull ? 2 : 4; }
 
 // The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
 // 0,4,5,8,9,10,12,13,14,15, then 1,2,3,6,7,11 (one 4-bit entry per slot).
@@ -237,8 +262,8 @@ struct Step {
 // The full pass visits key blocks 0..qb for each query block; the state pre-pass only
 // the diagonal one.
 template <int MODE>
-__device__ __forceinline__ bool next_step(Step& s, int t_end, int N, int C) {
-    const int L = min(C, N - s.cs);
+__device__ __forceinline__ bool next_step(Step& s, int t_end, int C) {
+    const int L = min(C, t_end - s.cs);
     const int nb = (L + kBlk - 1) / kBlk;
     if (MODE == kFull && s.kb < s.qb) { ++s.kb; return true; }
     if (s.qb + 1 < nb) { ++s.qb; s.kb = MODE == kFull ? 0 : s.qb; return true; }
@@ -248,22 +273,50 @@ __device__ __forceinline__ bool next_step(Step& s, int t_end, int N, int C) {
     return s.cs < t_end;
 }
 
+// Kernel arguments (one struct, passed by value).
+struct KArgs {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const float* decay;      // gamma [H] or g [B,H,N]
+    bf16_t* o;
+    const float* state_in;   // [B,H,dk,dv] or null (zeros)
+    float* state_out;        // [B,H,dk,dv] or null
+    float* seg_state;        // workspace [B*H][nseg][dk][dv]: local, then (scanned) entry states
+    float* seg_log2;         // workspace [B*H][nseg]: log2 of each segment's total decay
+    int H, N, dk, dv, C;
+    int seg_tokens, nseg;    // sequence split: tokens per segment, segments per (b,h)
+    int ndvt, ndkt;          // column tiles and (pre-pass) state-row tiles per (b,h)
+    int total_groups;
+    int fuse_scan;           // main pass: compose the entry state from the local states
+};
+
 // Main kernel (MODE = kFull) and segment-state pre-pass (MODE = kStateOnly).
+//   Main pass: state rows = all dk (DK == dk); a workgroup per (b,h), segment, column
+//   tile.  Its incoming state is state_in (one segment), the scanned entry state in
+//   seg_state, or (fuse_scan) composed here from the local states of the earlier
+//   segments.
+//   Pre-pass: a workgroup per (b,h), segment 0..nseg-2, DK-row tile, column tile; it
+//   writes the segment's local final state (zero start) and its total log2 decay.
 // ONEBLK: every chunk is a single block (chunk <= 64), so each step starts a chunk and
 // the cross term can read the old state straight from the accumulators; no bf16
 // snapshot of the state is kept, which frees registers for wider column tiles.
-//   s_init: incoming state; for nseg == 1 it is state_in (may be null = zeros) with
-//           (b,h) stride dk*dv; for nseg > 1 it is the scanned workspace with
-//           (b,h, seg) stride dk*dv.  The pre-pass starts from zero.
-//   seg_out (pre-pass): local final state of each segment, same layout as s_init;
-//           seg_log2 (pre-pass): log2 of each segment's total decay.
+// The LDS footprint allows one workgroup per CU, i.e. NW/4 waves per SIMD; saying so
+// lets the compiler spend registers on keeping LDS reads in flight ahead of the matrix
+// instructions instead of minimising registers for an occupancy that cannot happen.
 template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
-__global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ decay, bf16_t* __restrict__ o, const float* __restrict__ s_init,
-    float* __restrict__ state_out, float* __restrict__ seg_out, float* __restrict__ seg_log2, int H,
-    int N, int dv, int C, int seg_tokens, int nseg, int ndvt, int total_groups) {
-    using L_ = Lds<DK, DVT, GATED>;
+__global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void chunk_kernel(
+    const KArgs ka) {
+    const bf16_t* __restrict__ q = ka.q;
+    const bf16_t* __restrict__ k = ka.k;
+    const bf16_t* __restrict__ v = ka.v;
+    const float* __restrict__ decay = ka.decay;
+    bf16_t* __restrict__ o = ka.o;
+    const int H = ka.H, N = ka.N, dv = ka.dv, C = ka.C, dk = ka.dk;
+    const int seg_tokens = ka.seg_tokens, nseg = ka.nseg, ndvt = ka.ndvt, ndkt = ka.ndkt;
+    const int total_groups = ka.total_groups;
+    constexpr int NST = stages_for(MODE);
+    using L_ = Lds<DK, DVT, GATED, MODE == kFull, NST, NW>;
     constexpr int NT = DVT / (16 * NW);   // 16-column tiles per wave
     static_assert(NT >= 1 && NT * 16 * NW == DVT && 16 % NW == 0, "bad wave split");
     constexpr int DT = DK / 16;           // 16-row tiles of the state
@@ -277,9 +330,11 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     // give each XCD a contiguous range of work so a (b,h)'s column tiles share an L2).
     int wid = blockIdx.x;
     if (total_groups % 8 == 0) wid = (wid & 7) * (total_groups >> 3) + (wid >> 3);
+    const int nseg_grid = MODE == kFull ? nseg : nseg - 1;   // the last segment's state is not needed
     const int dvt = wid % ndvt;
-    const int seg = (wid / ndvt) % nseg;
-    const int bh = wid / (ndvt * nseg);
+    const int dkt = (wid / ndvt) % ndkt;
+    const int seg = (wid / (ndvt * ndkt)) % nseg_grid;
+    const int bh = wid / (ndvt * ndkt * nseg_grid);
     const int h = bh % H;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -293,20 +348,23 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     const int t_end = min(N, t_begin + seg_tokens);
     const float lg = GATED ? 0.f : log2f(decay[h]);
 
-    const size_t qk_bh = static_cast<size_t>(bh) * N * DK;
+    // q, k rows have dk elements; this workgroup's K tile covers dims dkt*DK .. +DK
+    const size_t qk_bh = static_cast<size_t>(bh) * N * dk;
     const size_t v_bh = static_cast<size_t>(bh) * N * dv;
-    const size_t s_bh = static_cast<size_t>(bh) * DK * dv;
-    const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
+    const size_t s_bh = static_cast<size_t>(bh) * dk * dv;
+    const size_t s_stride_seg = static_cast<size_t>(dk) * dv;
+    const int srow0 = dkt * DK;                          // first state row of this tile
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
-    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * DK * 2);
-    const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
+    const u32x4_t g_rs = make_rsrc(GATED ? g_bh : decay, GATED ? static_cast<uint32_t>(N) * 4 : 4);
+    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * dk * 2);
+    const u32x4_t k_rs = make_rsrc(k + qk_bh + srow0, static_cast<uint32_t>(N) * dk * 2);
     const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
     const uint32_t lds0 = lds_addr_of(smem);
     TileCopy<QRB, false, NW> qcp;
     TileCopy<QRB, false, NW> kcp;
     TileCopy<VRB, true, NW> vcp;
-    if (MODE == kFull) qcp.init(DK * 2, wave, lane);
-    kcp.init(DK * 2, wave, lane);
+    if (MODE == kFull) qcp.init(dk * 2, wave, lane);
+    kcp.init(dk * 2, wave, lane);
     vcp.init(dv * 2, wave, lane);
 
     // State accumulator element (dt, i) of lane l holds state row srow(dt, i): tiles 2s and
@@ -320,19 +378,33 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     // ---- incoming state
     f32x4_t S[DT][NT];
     {
-        const float* src = nullptr;
-        if (MODE == kFull) {
-            if (nseg > 1) src = s_init + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg;
-            else if (s_init != nullptr) src = s_init + s_bh;
-        }
         const int cidx = col0 + wcol + l16;
+        auto load = [&](const float* src, float scale, bool add) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = src[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)];
+                        S[dt][nt][i] = add ? S[dt][nt][i] * scale + x : x;
+                    }
+        };
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[dt][nt][i] = src ? src[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)] : 0.f;
+            for (int nt = 0; nt < NT; ++nt) S[dt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (MODE == kFull) {
+            if (nseg == 1 || ka.fuse_scan) {
+                if (ka.state_in != nullptr) load(ka.state_in + s_bh, 0.f, false);
+                // entry state of segment seg: S <- 2^(l2 of segment s) S + local state of s
+                for (int sg = 0; nseg > 1 && sg < seg; ++sg)
+                    load(ka.seg_state + (static_cast<size_t>(bh) * nseg + sg) * s_stride_seg,
+                         exp2f(ka.seg_log2[static_cast<size_t>(bh) * nseg + sg]), true);
+            } else {
+                load(ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg, 0.f, false);
+            }
+        }
     }
 
     // bf16 B operand of Q S from tiles 2ks, 2ks+1 (reduction rows 32ks+8g .. +7 in order)
@@ -357,35 +429,48 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     auto l2x = [&](int j) -> float { return GATED ? gl[j] : static_cast<float>(j + 1) * lg; };
 
     // Per-head form: gamma^(j-l) splits into a per-lane factor (the lane's offsets
-    // inside a 16x16 tile) and a uniform factor (the tile/block offset).
-    float fe[4], fx[4], fz[8];
+    // inside a 16x16 tile) and a uniform factor (the tile/block offset).  Both factors
+    // are kept <= 1 (non-negative exponents) so that neither overflows for small gamma:
+    //   fe: diagonal tile, gamma^(q-k) for key offset k <= query offset q, else 0;
+    //   fo: off-diagonal tile, gamma^(16+q-k), paired with gamma^(tile offset - 16);
+    //   fx: cross term, gamma^(row offset);
+    //   fz: state update, gamma^(31 - key offset in a 32-key half), paired with
+    //       gamma^(distance from the half's last key to the chunk end).
+    float fe[4], fo[4], fx[4], fz[8];
     bool dmask[4];           // inside a diagonal 16x16 tile: key <= query
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        fe[i] = GATED ? 1.f : exp2_fast(static_cast<float>(l16 - 4 * g4 - i) * lg);
-        fx[i] = GATED ? 1.f : exp2_fast(static_cast<float>(4 * g4 + i) * lg);
         dmask[i] = 4 * g4 + i <= l16;
+        fe[i] = GATED || !dmask[i] ? 0.f : exp2_fast(static_cast<float>(l16 - 4 * g4 - i) * lg);
+        fo[i] = GATED ? 1.f : exp2_fast(static_cast<float>(16 + l16 - 4 * g4 - i) * lg);
+        fx[i] = GATED ? 1.f : exp2_fast(static_cast<float>(4 * g4 + i) * lg);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fz[i] = GATED ? 1.f : exp2_fast(-static_cast<float>(8 * g4 + i) * lg);
+    for (int i = 0; i < 8; ++i) fz[i] = GATED ? 1.f : exp2_fast(static_cast<float>(31 - 8 * g4 - i) * lg);
 
     int qbuf = 0, kvbuf = 0;
     // issue the asynchronous loads of step s into buffers (qb_, kvb_)
     auto issue = [&](const Step& s, int qb_, int kvb_) {
-        const int L = min(C, N - s.cs);
+        const int L = min(C, t_end - s.cs);
         const int k0 = s.cs + s.kb * kBlk;
         if (MODE == kFull && s.kb == 0) {
             const int q0 = s.cs + s.qb * kBlk;
-            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * DK * 2, wave);
+            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * dk * 2, wave);
         }
-        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * DK * 2, wave);
+        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * dk * 2, wave);
         vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, wave);
-        if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
+        if (GATED && MODE == kStateOnly) {
+            // the pre-pass walks single blocks: every wave copies the block's 64 decays
+            buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
+                     lds0 + L_::kGd + (kvb_ * NW + wave) * 256);
+        } else if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
             const float* gs = g_bh + s.cs;
 #pragma unroll
             for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, L - 1)];
         }
     };
+    // vector memory loads one step issues per wave (pre-pass: K, V and the decays)
+    constexpr int kLoadsPerStep = TileCopy<QRB, false, NW>::kPerWave + TileCopy<VRB, true, NW>::kPerWave + (GATED ? 1 : 0);
 
     int pend_q0 = -1, pend_nq = 0;   // rows of a finished query block not yet stored
     auto store_pending = [&]() {
@@ -418,16 +503,44 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
 
     Step cur{t_begin, 0, 0};
     issue(cur, 0, 0);
+    // steps issued beyond cur (at most NST - 2 at the top of an iteration)
+    Step ahead = cur;
+    bool more = true;
+    int inflight = 0;
+    for (int i = 0; i < NST - 2 && more; ++i) {
+        more = next_step<MODE>(ahead, t_end, C);
+        if (more) issue(ahead, 0, ++inflight);
+    }
 
     while (true) {
-        __builtin_amdgcn_s_waitcnt(0);   // this step's tiles (issued one step ago) have landed
-        __syncthreads();
-        const int L = min(C, N - cur.cs);
+        // this step's tiles have landed: the pre-pass lets the loads of the steps after it
+        // stay in flight; the main pass (whose stores also count) waits for everything
+        if (MODE == kStateOnly && NST > 2) {
+            if (inflight == NST - 2) wait_vmcnt<(NST - 2) * kLoadsPerStep>();
+            else wait_vmcnt<0>();
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        lds_barrier();
+        const int L = min(C, t_end - cur.cs);
         const int qb = ONEBLK ? 0 : cur.qb, kb = ONEBLK ? 0 : cur.kb;
         const bool diag = kb == qb;
         if (qb == 0 && kb == 0) {
             // start of a chunk: decays, bf16 snapshot of the old state, S <- 2^(G_{L-1}) S
-            if (GATED) {
+            if (GATED && MODE == kStateOnly) {
+                if (wave == 0) {
+                    // block-local inclusive prefix of the decays (wave 0's copy)
+                    const float* gb = reinterpret_cast<const float*>(smem + L_::kGd + kvbuf * NW * 256);
+                    float incl = lane < L ? gb[lane] * kLog2e : 0.f;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(incl, off, 64);
+                        if (lane >= off) incl += y;
+                    }
+                    gl[lane] = incl;
+                }
+                lds_barrier();
+            } else if (GATED) {
                 if (wave == 0) {
                     float run = 0.f, loc[8];
 #pragma unroll
@@ -460,9 +573,17 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
         }
 
         Step nxt = cur;
-        const bool has_next = next_step<MODE>(nxt, t_end, N, C);
+        const bool has_next = next_step<MODE>(nxt, t_end, C);
         const int nqbuf = (MODE == kFull && nxt.kb == 0) ? qbuf ^ 1 : qbuf;
-        if (has_next) issue(nxt, nqbuf, kvbuf ^ 1);
+        if (more) {
+            more = next_step<MODE>(ahead, t_end, C);
+            if (more) {
+                ++inflight;
+                int b = kvbuf + inflight;
+                if (b >= NST) b -= NST;
+                issue(ahead, nqbuf, b);
+            }
+        }
         store_pending();
 
         const bool fullq = (qb + 1) * kBlk <= L;     // no row of the blocks is past the chunk end
@@ -521,14 +642,15 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
                 }
                 const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
                 const bool dtile = diag && kt == qt;
-                const float sd = GATED ? 0.f : exp2_fast(static_cast<float>((qb - kb) * kBlk + (qt - kt) * 16) * lg);
+                // off-diagonal tiles: gamma^(tile offset - 16), tile offset >= 16
+                const float sd = GATED || dtile ? 0.f : exp2_fast(static_cast<float>((qb - kb) * kBlk + (qt - kt) * 16 - 16) * lg);
                 float pv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int l = kb * kBlk + kt * 16 + 4 * g4 + i;   // key (chunk-local)
                     bool keep = !dtile || dmask[i];
                     if (!(fullq && fullk)) keep = keep && l < L && j < L;
-                    const float w = GATED ? exp2_fast(l2d(j, l)) : sd * fe[i];
+                    const float w = GATED ? exp2_fast(l2d(j, l)) : (dtile ? fe[i] : sd * fo[i]);
                     pv[i] = keep ? acc[i] * w : 0.f;
                 }
                 Pr[s16] = bf4(f32x4_t{pv[0], pv[1], pv[2], pv[3]});
@@ -551,38 +673,75 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int r0 = ks * 32 + 8 * g4 + trj;
-                // zeta_l / 2^lk2: decay from key l to the chunk end, in the state's scale
-                const float sz = GATED ? 0.f : exp2_fast(static_cast<float>(L - 1 - kb * kBlk - ks * 32) * lg - lk2);
-                float z[8];
+                // zeta_l / 2^lk2: decay from key l to the chunk end, in the state's scale.
+                // Full blocks: uniform gamma^(L - 32 - 32ks - 64kb) (exponent >= 0) times
+                // fz; a partial block takes the power directly.
+                const float sz = GATED ? 0.f : exp2_fast(static_cast<float>(L - 32 - kb * kBlk - ks * 32) * lg - lk2);
+                // K^T operand of state tile dt: result lane m must receive state row
+                // srow(dt, m%4 of group m/4), so source lane (j, q) reads dims
+                // 32(dt/2) + 8q + 4((dt^q)&1) .. +3
+                auto kt_frag = [&](int dt) -> u16x8_t {
+                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * ((dt ^ trq) & 1);
+                    return cat(lds_tr(Ks, qk_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
+                               lds_tr(Ks, qk_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
+                };
+                // software pipeline: the reads of the next G operand tiles are issued
+                // before the matrix instructions on the current ones (the scheduling
+                // barriers keep the compiler from serialising reads and uses)
+                constexpr int G = DT < 4 ? DT : 4;
+                u16x8_t raw[NT], acur[G], anext[G];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
-                    z[i] = GATED ? exp2_fast(l2d(L - 1, l) - lk2) : sz * fz[i];
-                    if (!fullk && l >= L) z[i] = 0.f;
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int c0 = wcol + nt * 16 + 4 * trq;
+                    raw[nt] = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
+                                  lds_tr(Vs, v_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j) acur[j] = kt_frag(j);
+                __builtin_amdgcn_sched_barrier(0);
+                float z[8];
+                if (GATED) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
+                        z[i] = exp2_fast(l2d(L - 1, l) - lk2);
+                        if (!fullk && l >= L) z[i] = 0.f;
+                    }
+                } else if (fullk) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) z[i] = sz * fz[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int l = kb * kBlk + ks * 32 + 8 * g4 + i;
+                        z[i] = l < L ? exp2_fast(static_cast<float>(L - 1 - l) * lg - lk2) : 0.f;
+                    }
                 }
                 u16x8_t b[NT];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int c0 = wcol + nt * 16 + 4 * trq;
-                    const u16x8_t raw = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
-                                            lds_tr(Vs, v_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
                     f32x4_t lo, hi;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        lo[i] = bf16_to_f32(raw[i]) * z[i];
-                        hi[i] = bf16_to_f32(raw[i + 4]) * z[i + 4];
+                        lo[i] = bf16_to_f32(raw[nt][i]) * z[i];
+                        hi[i] = bf16_to_f32(raw[nt][i + 4]) * z[i + 4];
                     }
                     b[nt] = cat(bf4(lo), bf4(hi));
                 }
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    // result lane m must receive state row srow(dt, m%4 of group m/4):
-                    // source lane (j, q) reads dims 32(dt/2) + 8q + 4((dt^q)&1) .. +3
-                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * ((dt ^ trq) & 1);
-                    const u16x8_t a = cat(lds_tr(Ks, qk_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
-                                          lds_tr(Ks, qk_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
+                for (int g0 = 0; g0 < DT; g0 += G) {
+                    if (g0 + G < DT) {
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) S[dt][nt] = mfma16(a, b[nt], S[dt][nt]);
+                        for (int j = 0; j < G; ++j) anext[j] = kt_frag(g0 + G + j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < G; ++j)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) S[g0 + j][nt] = mfma16(acur[j], b[nt], S[g0 + j][nt]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) acur[j] = anext[j];
                 }
             }
         }
@@ -623,17 +782,18 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
         if (!has_next) break;
         cur = nxt;
         qbuf = nqbuf;
-        kvbuf ^= 1;
+        kvbuf = kvbuf + 1 == NST ? 0 : kvbuf + 1;
+        if (inflight > 0) --inflight;
     }
     store_pending();
 
     // ---- results
     float* dst = nullptr;
     if (MODE == kFull) {
-        if (seg == nseg - 1 && state_out != nullptr) dst = state_out + s_bh;
+        if (seg == nseg - 1 && ka.state_out != nullptr) dst = ka.state_out + s_bh;
     } else {
-        dst = seg_out + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg;
-        if (dvt == 0 && tid == 0) seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
+        dst = ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
+        if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
     }
     if (dst != nullptr) {
         const int cidx = col0 + wcol + l16;
@@ -650,7 +810,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
 
 // Exclusive scan of segment states, in place:  buf[seg] <- state entering seg.
 //   S = state_in (or 0); for seg: T = buf[seg]; buf[seg] = S; S = 2^(l2[seg]) S + T.
-// One thread per state element of one (b,h); blocks_per_bh blocks per (b,h).
+// The last segment's local state is never computed (nor read).  One thread per state
+// element of one (b,h); blocks_per_bh blocks per (b,h).
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ buf,
                                                            const float* __restrict__ seg_log2,
                                                            const float* __restrict__ state_in,
@@ -662,59 +823,87 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
         float s = state_in != nullptr ? state_in[bh * per_bh + e] : 0.f;
         for (int sg = 0; sg < nseg; ++sg) {
             float* p = buf + (bh * nseg + sg) * per_bh + e;
-            const float t = *p;
+            const float t = sg + 1 < nseg ? *p : 0.f;
             *p = s;
-            s = exp2f(seg_log2[bh * nseg + sg]) * s + t;
+            if (sg + 1 < nseg) s = exp2f(seg_log2[bh * nseg + sg]) * s + t;
         }
     }
 }
 
-template <int DK, int DVT, int NW, bool GATED, bool ONEBLK>
-hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
-    using L_ = Lds<DK, DVT, GATED>;
-    const int ndvt = a.dv / DVT;
-    const int bh = a.B * a.H;
-    const int seg_tokens = p.seg_chunks * a.chunk;
-    const bf16_t* q = static_cast<const bf16_t*>(a.q);
-    const bf16_t* k = static_cast<const bf16_t*>(a.k);
-    const bf16_t* v = static_cast<const bf16_t*>(a.v);
-    bf16_t* o = static_cast<bf16_t*>(a.o);
-    const size_t lds = L_::kBytes;
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
+hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
+    const size_t lds = Lds<DK, DVT, GATED, MODE == kFull, stages_for(MODE), NW>::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, kStateOnly, ONEBLK>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
-    const float* s_init = a.state_in;
-    float* segbuf = nullptr;
-    float* segl2 = nullptr;
-    if (p.nseg > 1) {
-        const size_t per_bh = static_cast<size_t>(DK) * a.dv;
-        segbuf = static_cast<float*>(a.workspace);
-        segl2 = segbuf + static_cast<size_t>(bh) * p.nseg * per_bh;
-        // pre-pass: local final state of every segment but the last is needed; the
-        // grid covers all segments so the launch shape matches the main pass.
-        const int groups = bh * p.nseg * ndvt;
-        hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, kStateOnly, ONEBLK>), dim3(groups), dim3(NW * 64), lds,
-                           stream, q, k, v, a.decay, o, nullptr, nullptr, segbuf, segl2, a.H, a.N,
-                           a.dv, a.chunk, seg_tokens, p.nseg, ndvt, groups);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 64));
-        hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
-                           stream, segbuf, segl2, a.state_in, p.nseg, per_bh, xblocks);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        s_init = segbuf;
-    }
-    const int groups = bh * p.nseg * ndvt;
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>), dim3(groups), dim3(NW * 64), lds, stream,
-                       q, k, v, a.decay, o, s_init, a.state_out, nullptr, nullptr, a.H, a.N, a.dv,
-                       a.chunk, seg_tokens, p.nseg, ndvt, groups);
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>), dim3(ka.total_groups), dim3(NW * 64), lds,
+                       stream, ka);
     return hipGetLastError();
+}
+
+// Segment-state pre-pass: state-row tile DKT (<= 128) and column tile DVT, one wave
+// per 16 columns.
+template <bool GATED>
+hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
+    ka.ndkt = ka.dk / p.pre_dkt;
+    ka.ndvt = ka.dv / p.pre_dvt;
+    const int bh = ka.total_groups;   // caller passes B*H
+    // the local state of a segment does not depend on how it is chunked: walk it in
+    // single 64-token blocks (each block its own decay step)
+    ka.C = kBlk;
+    ka.total_groups = bh * (ka.nseg - 1) * ka.ndkt * ka.ndvt;
+#define RETN_PRE(DKT, DVT)                                                                  \
+    if (p.pre_dkt == DKT && p.pre_dvt == DVT) return launch_kernel<DKT, DVT, DVT / 16, GATED, kStateOnly, true>(ka, stream);
+    RETN_PRE(64, 64)
+    RETN_PRE(64, 128)
+    RETN_PRE(128, 64)
+    RETN_PRE(128, 128)
+#undef RETN_PRE
+    return hipErrorInvalidValue;
+}
+
+template <int DK, int DVT, int NW, bool GATED, bool ONEBLK>
+hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    KArgs ka{};
+    ka.q = static_cast<const bf16_t*>(a.q);
+    ka.k = static_cast<const bf16_t*>(a.k);
+    ka.v = static_cast<const bf16_t*>(a.v);
+    ka.decay = a.decay;
+    ka.o = static_cast<bf16_t*>(a.o);
+    ka.state_in = a.state_in;
+    ka.state_out = a.state_out;
+    ka.H = a.H;
+    ka.N = a.N;
+    ka.dk = a.dk;
+    ka.dv = a.dv;
+    ka.C = a.chunk;
+    ka.seg_tokens = p.seg_chunks * a.chunk;
+    ka.nseg = p.nseg;
+    ka.fuse_scan = p.fuse_scan;
+    const int bh = a.B * a.H;
+    if (p.nseg > 1) {
+        const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
+        ka.seg_state = static_cast<float*>(a.workspace);
+        ka.seg_log2 = ka.seg_state + static_cast<size_t>(bh) * p.nseg * per_bh;
+        KArgs pre = ka;
+        pre.total_groups = bh;
+        hipError_t e = launch_pre<GATED>(pre, p, stream);
+        if (e != hipSuccess) return e;
+        if (!p.fuse_scan) {
+            const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 64));
+            hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
+                               stream, ka.seg_state, ka.seg_log2, a.state_in, p.nseg, per_bh, xblocks);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    ka.ndkt = 1;
+    ka.ndvt = a.dv / DVT;
+    ka.total_groups = bh * p.nseg * ka.ndvt;
+    return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>(ka, stream);
 }
 
 // State columns per workgroup and waves per workgroup for a head shape.
@@ -750,6 +939,9 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     want = std::min(want, std::max(1, nchunks));
     p.seg_chunks = (nchunks + want - 1) / want;
     p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;
+    p.pre_dkt = std::min(dk, 128);
+    p.pre_dvt = dv % 128 == 0 ? 128 : 64;
+    p.fuse_scan = p.nseg <= kFuseScanMax ? 1 : 0;
     if (p.nseg > 1) {
         const size_t per_bh = static_cast<size_t>(dk) * dv;
         p.workspace_bytes = (static_cast<size_t>(bh) * p.nseg * per_bh + static_cast<size_t>(bh) * p.nseg) * sizeof(float);

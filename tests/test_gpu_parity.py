@@ -154,6 +154,21 @@ def test_strong_decay(case):
     assert rel(S, rS) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("case", [(1, 2, 200, 256, 256, 64), (1, 2, 200, 128, 128, 100), (1, 2, 130, 64, 64, 64),
+                                  (1, 2, 150, 128, 64, 40)], ids=lambda c: "N{}dk{}dv{}C{}".format(*c[2:]))
+def test_tiny_gamma(case):
+    """Per-head decays far below the usual range: the decay factors the kernels split
+    into per-lane and per-tile parts must not overflow."""
+    B, H, N, dk, dv, C = case
+    say(("tiny gamma", case))
+    x = I.random_case(N + dk + dv, B, H, N, dk, dv, dtype="bf16", state_in=True)
+    x["gamma"] = I.to_dtype(np.array([0.001, 0.04]), "f32")
+    o, S = run_chunk(x, C, False, state_in=True)
+    ro, rS = oracle_chunk(x, False, state_in=True)
+    assert rel(o, ro) <= TOL["bf16"]
+    assert rel(S, rS) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ edge cases
 def test_empty_sequence_passes_state_through():
     say("N=0")
