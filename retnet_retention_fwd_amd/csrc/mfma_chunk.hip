@@ -421,7 +421,9 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     float lkx = 0.f;         // log2 of the scale of the chunk's incoming state
     float seg_l2 = 0.f;      // log2 of the decay accumulated over the segment (pre-pass)
     u16x8_t Sp[ONEBLK ? 1 : KS][NT];   // bf16 copy of the chunk's incoming state (B operand of Q S)
-    f32x4_t X[4][NT];        // output accumulators of the current query block
+    // output accumulators of the current query block, transposed: X[mt][nt] of lane
+    // (g, l%16) holds O[row mt*16 + l%16][columns wcol + nt*16 + 4g .. +3]
+    f32x4_t X[4][NT];
     float gpre[8];           // prefetched log-decays of the next chunk (wave 0, gated)
 
     // log2 of the decay over chunk positions (l, j] and over [0, j] (gated form)
@@ -433,17 +435,17 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // are kept <= 1 (non-negative exponents) so that neither overflows for small gamma:
     //   fe: diagonal tile, gamma^(q-k) for key offset k <= query offset q, else 0;
     //   fo: off-diagonal tile, gamma^(16+q-k), paired with gamma^(tile offset - 16);
-    //   fx: cross term, gamma^(row offset);
+    //   fq: cross term, gamma^(row offset l%16);
     //   fz: state update, gamma^(31 - key offset in a 32-key half), paired with
     //       gamma^(distance from the half's last key to the chunk end).
-    float fe[4], fo[4], fx[4], fz[8];
+    float fe[4], fo[4], fz[8];
+    const float fq = GATED ? 1.f : exp2_fast(static_cast<float>(l16) * lg);
     bool dmask[4];           // inside a diagonal 16x16 tile: key <= query
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         dmask[i] = 4 * g4 + i <= l16;
         fe[i] = GATED || !dmask[i] ? 0.f : exp2_fast(static_cast<float>(l16 - 4 * g4 - i) * lg);
         fo[i] = GATED ? 1.f : exp2_fast(static_cast<float>(16 + l16 - 4 * g4 - i) * lg);
-        fx[i] = GATED ? 1.f : exp2_fast(static_cast<float>(4 * g4 + i) * lg);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) fz[i] = GATED ? 1.f : exp2_fast(static_cast<float>(31 - 8 * g4 - i) * lg);
@@ -473,19 +475,20 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     constexpr int kLoadsPerStep = TileCopy<QRB, false, NW>::kPerWave + TileCopy<VRB, true, NW>::kPerWave + (GATED ? 1 : 0);
 
     int pend_q0 = -1, pend_nq = 0;   // rows of a finished query block not yet stored
+    // lane (g, l%16) stores 4 adjacent columns of row l%16 of each 16-row tile: a
+    // wave-uniform base plus a 32-bit lane offset
+    const uint32_t st_lane = static_cast<uint32_t>(l16 * dv + 4 * g4);
     auto store_pending = [&]() {
         if (MODE != kFull || pend_q0 < 0) return;
+        bf16_t* const base = o + v_bh + static_cast<size_t>(pend_q0) * dv + col0 + wcol;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+            if (pend_nq < kBlk && mt * 16 + l16 >= pend_nq) continue;   // rows past the end
+            bf16_t* const row = base + static_cast<size_t>(mt * 16) * dv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = mt * 16 + 4 * g4 + i;
-                if (row < pend_nq) {
-                    bf16_t* dst = o + v_bh + static_cast<size_t>(pend_q0 + row) * dv + col0 + wcol + l16;
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) dst[nt * 16] = bf(X[mt][nt][i]);
-                }
-            }
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<u16x4_t*>(row + st_lane + nt * 16) = bf4(X[mt][nt]);
+        }
         pend_q0 = -1;
     };
 
@@ -606,21 +609,18 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             const u16x8_t b = ONEBLK ? state_b(ks, nt) : Sp[ONEBLK ? 0 : ks][nt];
-                            X[mt][nt] = mfma16(a, b, X[mt][nt]);
+                            X[mt][nt] = mfma16(b, a, X[mt][nt]);   // transposed: (S^T Q^T)
                         }
                     }
                 }
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    const float sx = GATED ? 0.f : exp2_fast(static_cast<float>(qb * kBlk + mt * 16 + 1) * lg + lkx);
+                    const int j = qb * kBlk + mt * 16 + l16;     // this lane's query row
+                    float xi = GATED ? exp2_fast(gl[j] + lkx)
+                                     : exp2_fast(static_cast<float>(qb * kBlk + mt * 16 + 1) * lg + lkx) * fq;
+                    if (!fullq && j >= L) xi = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = qb * kBlk + mt * 16 + 4 * g4 + i;
-                        float xi = GATED ? exp2_fast(gl[j] + lkx) : sx * fx[i];
-                        if (!fullq && j >= L) xi = 0.f;
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) X[mt][nt][i] *= xi;
-                    }
+                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] *= xi;
                 }
             }
             // scores of (query block qb, key block kb): the 16 tiles (qt, kt) are listed
@@ -644,16 +644,20 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 const bool dtile = diag && kt == qt;
                 // off-diagonal tiles: gamma^(tile offset - 16), tile offset >= 16
                 const float sd = GATED || dtile ? 0.f : exp2_fast(static_cast<float>((qb - kb) * kBlk + (qt - kt) * 16 - 16) * lg);
-                float pv[4];
+                float w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int l = kb * kBlk + kt * 16 + 4 * g4 + i;   // key (chunk-local)
-                    bool keep = !dtile || dmask[i];
-                    if (!(fullq && fullk)) keep = keep && l < L && j < L;
-                    const float w = GATED ? exp2_fast(l2d(j, l)) : (dtile ? fe[i] : sd * fo[i]);
-                    pv[i] = keep ? acc[i] * w : 0.f;
+                    if (GATED) w[i] = dtile && !dmask[i] ? 0.f : exp2_fast(l2d(j, l));
+                    else w[i] = dtile ? fe[i] : sd * fo[i];
                 }
-                Pr[s16] = bf4(f32x4_t{pv[0], pv[1], pv[2], pv[3]});
+                if (!(fullq && fullk)) {
+                    // rows or keys past the chunk end (partial blocks only)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kb * kBlk + kt * 16 + 4 * g4 + i >= L || j >= L) w[i] = 0.f;
+                }
+                Pr[s16] = bf4(f32x4_t{acc[0] * w[0], acc[1] * w[1], acc[2] * w[2], acc[3] * w[3]});
             }
             if (!L_::kPInK) write_p(Pfix);
         }
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 Pf = Ks;
             }
             lds_barrier();
-            // X += P V over the 64 keys of block kb; V fragments by transpose reads:
+            // X += P V over the 64 keys of block kb (as X^T += V^T P^T); V fragments by transpose reads:
             // slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -771,7 +775,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     if (diag && 2 * ks > mt) continue;
                     const u16x8_t a = lds16(Pf, ((mt * 2 + ks) * 64 + lane) * 16);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(a, b[nt], X[mt][nt]);
+                    for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(b[nt], a, X[mt][nt]);   // (V^T P^T)
                 }
             }
         }
