@@ -41,8 +41,9 @@
  *   Sizes      B, H, N >= 0 (B*H*N = 0 is a valid empty call: state_out, if given,
  *              receives state_in or zeros); dk, dv in [1, 256] for the generic
  *              kernels; chunk >= 1.  The bf16 matrix-core path is used when dk is
- *              64, 128 or 256, dv is a multiple of 64 and chunk is 64, 128, 256 or
- *              512; every other shape in range runs on the generic kernels.
+ *              64, 128 or 256, dv is a multiple of 64 (<= 1024), chunk <= 512 and
+ *              q, k, v, o are 16-byte aligned; every other shape in range runs on the
+ *              generic kernels.
  *              A ragged last chunk (N not a multiple of chunk) is computed exactly;
  *              there is no padding.
  */
@@ -148,6 +149,23 @@ const char* retention_status_string(retn_status status);
 
 /* Version of this ABI (incremented on any signature change). */
 int retention_abi_version(void);
+
+/*
+ * Kernel timing for benchmarks (not needed for computing anything).
+ * retention_profile_enable(1) starts recording: every kernel the library launches
+ * afterwards is bracketed by two HIP events on its stream (up to 4096 launches
+ * between read-outs; later ones are counted as dropped).  The first enable creates
+ * the events on the current device; use one device and one host thread while
+ * timing.  retention_profile_enable(0) stops recording.
+ * retention_profile_read waits for the recorded launches, writes for each kernel kind
+ * i < nkinds the summed milliseconds ms[i] and the launch count count[i], writes the
+ * number of dropped launches to *dropped (if not NULL) and clears the records.
+ * Kinds: 0 matrix-core chunkwise pass, 1 its segment-state pre-pass, 2 its segment
+ * scan, 3 generic chunkwise kernel, 4 decode step, 5 state copy (empty sequence).
+ * Errors: RETN_ERR_SHAPE (nkinds < 0), RETN_ERR_NULL, RETN_ERR_HIP.
+ */
+retn_status retention_profile_enable(int on);
+retn_status retention_profile_read(double* ms, int* count, int nkinds, int* dropped);
 
 #ifdef __cplusplus
 }

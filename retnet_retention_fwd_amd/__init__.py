@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     gated_retention_chunkwise_fwd,
     gated_retention_decode_step,
     lib,
+    profile_enable,
+    profile_read,
     retention_chunkwise_fwd,
     retention_decode_step,
     workspace_bytes,
@@ -22,4 +24,6 @@ __all__ = [
     "workspace_bytes",
     "RetentionError",
     "lib",
+    "profile_enable",
+    "profile_read",
 ]

@@ -30,7 +30,12 @@ EXPORTED = (
     "retention_workspace_bytes",
     "retention_status_string",
     "retention_abi_version",
+    "retention_profile_enable",
+    "retention_profile_read",
 )
+
+# Kernel kinds reported by retention_profile_read.
+PROFILE_KINDS = ("chunk_main", "chunk_prepass", "chunk_scan", "chunk_generic", "decode", "state_copy")
 
 
 class RetentionError(RuntimeError):
@@ -69,6 +74,10 @@ def lib() -> ctypes.CDLL:
     L.retention_status_string.restype = ctypes.c_char_p
     L.retention_abi_version.argtypes = []
     L.retention_abi_version.restype = ctypes.c_int
+    L.retention_profile_enable.argtypes = [_i]
+    L.retention_profile_enable.restype = ctypes.c_int
+    L.retention_profile_read.argtypes = [_vp, _vp, _i, _vp]
+    L.retention_profile_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -222,3 +231,22 @@ def retention_decode_step(q, k, v, gamma, state, out=None, stream=None):
 def gated_retention_decode_step(q, k, v, g, state, out=None, stream=None):
     """One gated decode step with log-decay g[B,H]: state <- exp(g) state + k^T v, o = q state."""
     return _decode_call("gated_retention_decode_step", q, k, v, g, state, out, stream, True)
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) timing every kernel launch with HIP events on its stream."""
+    _check(lib().retention_profile_enable(1 if on else 0), "retention_profile_enable")
+
+
+def profile_read() -> dict:
+    """Wait for the recorded launches; per kernel kind the summed milliseconds and the
+    number of launches since the last read-out (plus the count of dropped launches)."""
+    n = len(PROFILE_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    dropped = ctypes.c_int(0)
+    _check(lib().retention_profile_read(ctypes.cast(ms, _vp), ctypes.cast(cnt, _vp), n,
+                                        ctypes.byref(dropped)), "retention_profile_read")
+    out = {k: {"ms": ms[i], "launches": cnt[i]} for i, k in enumerate(PROFILE_KINDS)}
+    out["dropped"] = dropped.value
+    return out

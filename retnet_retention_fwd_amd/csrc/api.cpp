@@ -69,6 +69,9 @@ retn_status validate_chunk(const void* q, const void* k, const void* v, const fl
 // Chunks longer than the sequence are one chunk of N tokens.
 int effective_chunk(int N, int chunk) { return N > 0 ? (chunk < N ? chunk : N) : 1; }
 
+// The matrix-core kernels move 16-byte units of q, k, v and store 8-byte units of o.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 bool use_mfma(int dk, int dv, int eff_chunk, retn_dtype dt) {
     return retn::mfma_chunk_supported(dk, dv, eff_chunk, dt == RETN_BF16);
 }
@@ -87,7 +90,8 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
                                     dt, gated);
     if (st != RETN_OK) return st;
     const int eff_chunk = effective_chunk(N, chunk);
-    const bool mfma = use_mfma(dk, dv, eff_chunk, dt);
+    const bool mfma = use_mfma(dk, dv, eff_chunk, dt) && aligned16(q) && aligned16(k) && aligned16(v) &&
+                      aligned16(o);
     // The generic kernel keeps a gated chunk's cumulative decays in LDS.
     if (!mfma && gated && eff_chunk > kGenericMaxGatedChunk) return RETN_ERR_UNSUPPORTED;
     size_t need = 0;
@@ -194,5 +198,15 @@ const char* retention_status_string(retn_status status) {
 }
 
 int retention_abi_version(void) { return 1; }
+
+retn_status retention_profile_enable(int on) {
+    return retn::prof_enable(on != 0) == hipSuccess ? RETN_OK : RETN_ERR_HIP;
+}
+
+retn_status retention_profile_read(double* ms, int* count, int nkinds, int* dropped) {
+    if (nkinds < 0) return RETN_ERR_SHAPE;
+    if (nkinds > 0 && (ms == nullptr || count == nullptr)) return RETN_ERR_NULL;
+    return retn::prof_read(ms, count, nkinds, dropped) == hipSuccess ? RETN_OK : RETN_ERR_HIP;
+}
 
 }  // extern "C"

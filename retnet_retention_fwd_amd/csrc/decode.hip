@@ -152,6 +152,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
     T* o = static_cast<T*>(a.o);
+    ProfScope prof(kProfDecode, stream);
     if (a.dv == 128 && a.dk == 128) {
         hipLaunchKernelGGL((decode_vec_kernel<T, GATED, 128, 128>), grid, block, 0, stream, q, k, v,
                            a.decay, a.state, o, a.H, a.dk);

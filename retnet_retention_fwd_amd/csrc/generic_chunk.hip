@@ -208,6 +208,7 @@ hipError_t launch_generic_chunk(const ChunkArgs& a, hipStream_t stream) {
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),                   \
                        static_cast<const T*>(a.v), a.decay, static_cast<T*>(a.o), a.state_in,    \
                        a.state_out, a.H, a.N, a.dk, a.dv, a.chunk)
+    ProfScope prof(kProfGeneric, stream);
     if (a.bf16) {
         if (a.gated) { RETN_LAUNCH(bf16_t, true); } else { RETN_LAUNCH(bf16_t, false); }
     } else {
@@ -220,6 +221,7 @@ hipError_t launch_generic_chunk(const ChunkArgs& a, hipStream_t stream) {
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t stream) {
     if (n == 0 || dst == nullptr) return hipSuccess;
     const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
+    ProfScope prof(kProfCopy, stream);
     hipLaunchKernelGGL(copy_state_kernel, dim3(blocks), dim3(256), 0, stream, src, dst, n);
     return hipGetLastError();
 }

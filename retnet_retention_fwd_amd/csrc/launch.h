@@ -60,4 +60,24 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Optional per-kernel timing (HIP events around each launch, see profile.cpp).
+enum ProfKind { kProfMain = 0, kProfPre = 1, kProfScan = 2, kProfGeneric = 3, kProfDecode = 4, kProfCopy = 5,
+                kProfKinds = 6 };
+bool prof_enabled();
+hipError_t prof_enable(bool on);
+hipError_t prof_read(double* ms, int* count, int nkinds, int* dropped);
+// Records a begin event at construction and an end event at destruction when timing
+// is on; place it around one kernel launch.
+class ProfScope {
+public:
+    ProfScope(int kind, hipStream_t stream);
+    ~ProfScope();
+    ProfScope(const ProfScope&) = delete;
+    ProfScope& operator=(const ProfScope&) = delete;
+
+private:
+    int slot_;
+    hipStream_t stream_;
+};
+
 }  // namespace retn

@@ -843,6 +843,7 @@ hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
+    ProfScope prof(MODE == kFull ? kProfMain : kProfPre, stream);
     hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>), dim3(ka.total_groups), dim3(NW * 64), lds,
                        stream, ka);
     return hipGetLastError();
@@ -898,6 +899,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         if (e != hipSuccess) return e;
         if (!p.fuse_scan) {
             const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 64));
+            ProfScope prof(kProfScan, stream);
             hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
                                stream, ka.seg_state, ka.seg_log2, a.state_in, p.nseg, per_bh, xblocks);
             e = hipGetLastError();

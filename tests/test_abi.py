@@ -107,6 +107,12 @@ def test_workspace_query(L):
     assert L.retention_workspace_bytes(-1, 2, 64, 16, 16, 16, 0, 0) == 0
 
 
+def test_profile_read_validation(L):
+    assert L.retention_profile_read(None, None, -1, None) == ERR_SHAPE
+    assert L.retention_profile_read(None, None, 2, None) == ERR_NULL
+    assert L.retention_profile_read(None, None, 0, None) == OK     # nothing recorded
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     from retnet_retention_fwd_amd import retention_chunkwise_fwd

@@ -169,6 +169,25 @@ def test_tiny_gamma(case):
     assert rel(S, rS) <= TOL["bf16"]
 
 
+def test_kernel_timing_records_every_launch():
+    """The library's event timing sees each launch of a split-sequence call once."""
+    say("kernel timing")
+    x = I.random_case(77, 1, 2, 4000, 128, 128, dtype="bf16")
+    R().profile_enable(True)
+    try:
+        o, _ = run_chunk(x, 64, False)
+        p = R().profile_read()
+    finally:
+        R().profile_enable(False)
+    assert p["dropped"] == 0
+    for kind in ("chunk_main", "chunk_prepass", "chunk_scan"):
+        assert p[kind]["launches"] == 1, (kind, p)
+        assert p[kind]["ms"] > 0.0
+    assert p["decode"]["launches"] == 0
+    ro, _ = oracle_chunk(x, False)
+    assert rel(o, ro) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ edge cases
 def test_empty_sequence_passes_state_through():
     say("N=0")
