@@ -95,6 +95,20 @@ __device__ __forceinline__ u16x4_t lds_tr(const char* base, int byte_off) {
     return __builtin_bit_cast(u16x4_t, r);
 }
 
+// Reads at an absolute LDS byte address (the compiler folds constant additions into
+// the instruction's offset field).
+typedef __attribute__((address_space(3))) u16x8_t lds_u16x8_t;
+__device__ __forceinline__ u16x8_t lds16a(uint32_t addr) { return *(const lds_u16x8_t*)(addr); }
+__device__ __forceinline__ u16x4_t lds_tra(uint32_t addr) {
+    return __builtin_bit_cast(u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(addr)));
+}
+// Hides how a value was computed, so the compiler keeps it in one register instead of
+// re-deriving it from its parts at every use.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
 // s_barrier.  (__syncthreads() also waits for outstanding global loads, which would
 // stall on the asynchronous prefetch of the next block.)  The memory clobber keeps the
@@ -189,27 +203,27 @@ __device__ __forceinline__ int v_off(int row, int unit) {
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64 lanes][16 B]
 
-// LDS layout: double-buffered Q (full pass only), NST buffers of K and V blocks, per
-// stage and wave a copy of the block's decays (gated pre-pass), the P fragments of the
-// current block pair and (gated) the chunk's log2 decays.  When the buffers leave no
-// room for P (kPInK), P is written into the current K buffer once every wave is done
-// with K.
+// LDS layout: NST stages of Q (full pass only), K and V blocks and of the decays the
+// block's step loads (gated: the pre-pass copies its block's 64 decays once per wave,
+// the full pass the chunk's decays at a chunk start), the P fragments of the current
+// block pair and (gated) the chunk's log2 decays.  When the buffers leave no room for P
+// (kPInK), P is written into the current K buffer once every wave is done with K.
 template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW>
 struct Lds {
     static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
     static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
-    static constexpr int kQ = 0;                          // 2 buffers (none without Q)
-    static constexpr int kK = kQ + (HASQ ? 2 * kQTile : 0);   // NST buffers
+    static constexpr int kQ = 0;                          // NST buffers (none without Q)
+    static constexpr int kK = kQ + (HASQ ? NST * kQTile : 0);   // NST buffers
     static constexpr int kV = kK + NST * kKTile;          // NST buffers
-    static constexpr int kGd = kV + NST * kVTile;         // [NST][NW][64] floats
-    static constexpr int kEnd = kGd + (!HASQ && GATED ? NST * NW * 256 : 0);
+    static constexpr int kGdStage = !GATED ? 0 : (HASQ ? (NST == 3 ? kMaxChunk * 4 : 0) : NW * 256);
+    static constexpr int kGd = kV + NST * kVTile;         // NST stages of decays
+    static constexpr int kEnd = kGd + NST * kGdStage;
     static constexpr int kGBytes = GATED ? kMaxChunk * 4 : 0;
     static constexpr bool kPInK = HASQ && kEnd + kPBytes + kGBytes > kLdsBytes;
     static constexpr int kPSize = HASQ && !kPInK ? kPBytes : 0;
     static constexpr int kP = kPInK ? 0 : kEnd;           // unused when kPInK
     static constexpr int kG = kEnd + kPSize;
     static constexpr int kBytes = kG + kGBytes;
-    static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
 
 // Asynchronous copy of one 64-row tile (row bytes RB) of a row-major matrix with row
@@ -243,9 +257,13 @@ struct TileCopy {
     }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
-// K/V stages: the pre-pass has no stores in its loop, so it can keep several block loads
-// in flight and count them with vmcnt; the main pass double-buffers.
-constexpr int stages_for(int mode) { return mode == kFull ? 2 : 4; }
+// Pipeline stages: the pre-pass keeps four blocks in flight.  The full pass
+// double-buffers: a third stage (which fits for d_k <= 128) measured 4-8% slower on
+// every such workload -- their loads are bandwidth-, not latency-limited.
+template <int DK, int DVT, bool GATED, int MODE, int NW>
+constexpr int stages_for() {
+    return MODE != kFull ? 4 : 2;
+}
 
 // The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
 // 0,4,5,8,9,10,12,13,14,15, then 1,2,3,6,7,11 (one 4-bit entry per slot).
@@ -315,8 +333,9 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int H = ka.H, N = ka.N, dv = ka.dv, C = ka.C, dk = ka.dk;
     const int seg_tokens = ka.seg_tokens, nseg = ka.nseg, ndvt = ka.ndvt, ndkt = ka.ndkt;
     const int total_groups = ka.total_groups;
-    constexpr int NST = stages_for(MODE);
+    constexpr int NST = stages_for<DK, DVT, GATED, MODE, NW>();
     using L_ = Lds<DK, DVT, GATED, MODE == kFull, NST, NW>;
+    static_assert(L_::kBytes <= kLdsBytes, "LDS layout too large");
     constexpr int NT = DVT / (16 * NW);   // 16-column tiles per wave
     static_assert(NT >= 1 && NT * 16 * NW == DVT && 16 % NW == 0, "bad wave split");
     constexpr int DT = DK / 16;           // 16-row tiles of the state
@@ -413,6 +432,48 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         return (g4 & 1) ? cat(b, a) : cat(a, b);
     };
 
+    // ---- LDS read addresses.  Every fragment read of a step is one of a few per-lane
+    // patterns plus the current buffer's base plus a compile-time offset (row tile,
+    // reduction step, high bits of the swizzled unit):
+    //   Q/K rows (row tile t, reduction step ks): pq[ks%4] + t*16*QRB + (ks/4)*256, where
+    //     unit 4ks+g (+) s(l%16) = 4(ks (+) s/4) + (g (+) s%4) splits into the pattern and
+    //     a multiple of 256 bytes;
+    //   K^T transposed reads (state tile dt, rows r0 and r0+4, reduction half ks):
+    //     pkt[plus][(dt/2)%4][dt%2] + ks*32*QRB + (dt/8)*256;
+    //   V transposed reads: pvp[nt] + (ks*32 + 16 half)*VRB (P V), pvs[plus][nt] + ks*32*VRB
+    //     (state update).
+    constexpr int KL = KS < 4 ? KS : 4;            // distinct row-read patterns
+    constexpr int SL = DK / 32 < 4 ? DK / 32 : 4;  // distinct K^T patterns per row and half
+    uint32_t pq[KL], pkt[2][SL][2], pvp[NT], pvs[2][NT];
+    {
+        const int s = swz_qk<QRB / 16>(l16);
+#pragma unroll
+        for (int kl = 0; kl < KL; ++kl)
+            pq[kl] = static_cast<uint32_t>(l16 * QRB + 16 * (4 * (kl ^ (s >> 2)) + (g4 ^ (s & 3))));
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+            const int rb = 8 * g4 + trj + 4 * pl;
+            const int w = swz_qk<QRB / 16>(rb);
+#pragma unroll
+            for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+                    pkt[pl][sl][hb] = static_cast<uint32_t>(rb * QRB + 16 * (4 * (sl ^ (w >> 2)) + (trq ^ (w & 3))) +
+                                                            8 * (hb ^ (trq & 1)));
+            const int sv = swz_v<VRB / 16>(rb);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                pvs[pl][nt] = static_cast<uint32_t>(rb * VRB + 16 * (2 * ((wave * NT + nt) ^ (sv >> 1)) + (trq >> 1)) +
+                                                    8 * (trq & 1));
+        }
+        const int rbp = 4 * g4 + trj;
+        const int svp = swz_v<VRB / 16>(rbp);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            pvp[nt] = static_cast<uint32_t>(rbp * VRB + 16 * (2 * ((wave * NT + nt) ^ (svp >> 1)) + (trq >> 1)) +
+                                            8 * (trq & 1));
+    }
+
     // The state registers hold S / 2^lk2: the chunk decay is applied by moving lk2 (a
     // uniform scalar) instead of rescaling every element; new contributions are
     // multiplied by 2^-lk2 and the query-side factor by 2^lkx.  When lk2 drops below
@@ -424,7 +485,6 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // output accumulators of the current query block, transposed: X[mt][nt] of lane
     // (g, l%16) holds O[row mt*16 + l%16][columns wcol + nt*16 + 4g .. +3]
     f32x4_t X[4][NT];
-    float gpre[8];           // prefetched log-decays of the next chunk (wave 0, gated)
 
     // log2 of the decay over chunk positions (l, j] and over [0, j] (gated form)
     auto l2d = [&](int j, int l) -> float { return gl[j] - gl[l]; };
@@ -450,10 +510,11 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
     for (int i = 0; i < 8; ++i) fz[i] = GATED ? 1.f : exp2_fast(static_cast<float>(31 - 8 * g4 - i) * lg);
 
+    float gpre[8];           // two stages: wave 0's prefetch of the next chunk's decays
     int qbuf = 0, kvbuf = 0;
+    constexpr int kGLoads = (kMaxChunk / 64 + NW - 1) / NW;   // full pass: decay copies per wave
     // issue the asynchronous loads of step s into buffers (qb_, kvb_)
     auto issue = [&](const Step& s, int qb_, int kvb_) {
-        const int L = min(C, t_end - s.cs);
         const int k0 = s.cs + s.kb * kBlk;
         if (MODE == kFull && s.kb == 0) {
             const int q0 = s.cs + s.qb * kBlk;
@@ -464,15 +525,32 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         if (GATED && MODE == kStateOnly) {
             // the pre-pass walks single blocks: every wave copies the block's 64 decays
             buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
-                     lds0 + L_::kGd + (kvb_ * NW + wave) * 256);
-        } else if (GATED && s.qb == 0 && s.kb == 0 && wave == 0) {
-            const float* gs = g_bh + s.cs;
+                     lds0 + L_::kGd + kvb_ * L_::kGdStage + wave * 256);
+        } else if (GATED && s.qb == 0 && s.kb == 0) {
+            // chunk start: the chunk's decays.  Two stages: wave 0 prefetches them into
+            // registers (8 per lane).  Three stages: every wave copies 64 per instruction
+            // into the stage's LDS slot, so that every wave issues the same loads.
+            if (NST == 2) {
+                if (wave == 0) {
+                    const float* gs = g_bh + s.cs;
+                    const int lim = min(C, t_end - s.cs) - 1;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, L - 1)];
+                    for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, lim)];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kGLoads; ++i)
+                    buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u,
+                             static_cast<uint32_t>(s.cs + 64 * (wave + i * NW)) * 4u,
+                             lds0 + L_::kGd + kvb_ * L_::kGdStage + (wave + i * NW) * 256);
+            }
         }
     };
-    // vector memory loads one step issues per wave (pre-pass: K, V and the decays)
-    constexpr int kLoadsPerStep = TileCopy<QRB, false, NW>::kPerWave + TileCopy<VRB, true, NW>::kPerWave + (GATED ? 1 : 0);
+    // vector memory loads one step issues per wave: K and V, Q when a query block starts,
+    // the decays (pre-pass: every block; full pass: chunk starts)
+    constexpr int kLoadsKV = TileCopy<QRB, false, NW>::kPerWave + TileCopy<VRB, true, NW>::kPerWave;
+    constexpr int kLoadsQ = TileCopy<QRB, false, NW>::kPerWave;
+    constexpr int kLoadsPerStep = kLoadsKV + (GATED ? 1 : 0);   // pre-pass
 
     int pend_q0 = -1, pend_nq = 0;   // rows of a finished query block not yet stored
     // lane (g, l%16) stores 4 adjacent columns of row l%16 of each 16-row tile: a
@@ -504,15 +582,32 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
     };
 
+    // Ring bookkeeping (wave-uniform, 2 bits per K/V stage): the Q stage a step reads and
+    // which optional loads (bit 0: Q, bit 1: decays) it issued.
+    int qlast = NST - 1;       // Q stage of the most recent Q load
+    uint32_t qof = 0, ldof = 0;
+    auto issue_step = [&](const Step& s, int b) {
+        const bool needq = MODE == kFull && s.kb == 0;
+        const bool needg = GATED && MODE == kFull && NST == 3 && s.qb == 0 && s.kb == 0;
+        if (needq) qlast = qlast + 1 == NST ? 0 : qlast + 1;
+        issue(s, qlast, b);
+        qof = (qof & ~(3u << (2 * b))) | (static_cast<uint32_t>(qlast) << (2 * b));
+        ldof = (ldof & ~(3u << (2 * b))) | ((needq ? 1u : 0u) | (needg ? 2u : 0u)) << (2 * b);
+    };
+
+    // Drain the loads of the incoming state before the first asynchronous copy: the
+    // compiler does not count the copies, so a load it still tracked inside the loop
+    // would make it wait there for them.
+    __builtin_amdgcn_s_waitcnt(0);
     Step cur{t_begin, 0, 0};
-    issue(cur, 0, 0);
+    issue_step(cur, 0);
     // steps issued beyond cur (at most NST - 2 at the top of an iteration)
     Step ahead = cur;
     bool more = true;
     int inflight = 0;
     for (int i = 0; i < NST - 2 && more; ++i) {
         more = next_step<MODE>(ahead, t_end, C);
-        if (more) issue(ahead, 0, ++inflight);
+        if (more) issue_step(ahead, ++inflight);
     }
 
     while (true) {
@@ -521,10 +616,25 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         if (MODE == kStateOnly && NST > 2) {
             if (inflight == NST - 2) wait_vmcnt<(NST - 2) * kLoadsPerStep>();
             else wait_vmcnt<0>();
+        } else if (MODE == kFull && NST == 3) {
+            // The full pass issues its output stores before its loads, so the youngest
+            // operations are the next step's loads; loads complete in order.
+            if (inflight == 1) {
+                const int nb = kvbuf + 1 == NST ? 0 : kvbuf + 1;
+                switch ((ldof >> (2 * nb)) & 3u) {
+                    case 0: wait_vmcnt<kLoadsKV>(); break;
+                    case 1: wait_vmcnt<kLoadsKV + kLoadsQ>(); break;
+                    case 2: wait_vmcnt<kLoadsKV + kGLoads>(); break;
+                    default: wait_vmcnt<kLoadsKV + kLoadsQ + kGLoads>(); break;
+                }
+            } else {
+                wait_vmcnt<0>();
+            }
         } else {
             __builtin_amdgcn_s_waitcnt(0);
         }
         lds_barrier();
+        qbuf = static_cast<int>((qof >> (2 * kvbuf)) & 3u);
         const int L = min(C, t_end - cur.cs);
         const int qb = ONEBLK ? 0 : cur.qb, kb = ONEBLK ? 0 : cur.kb;
         const bool diag = kb == qb;
@@ -533,7 +643,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             if (GATED && MODE == kStateOnly) {
                 if (wave == 0) {
                     // block-local inclusive prefix of the decays (wave 0's copy)
-                    const float* gb = reinterpret_cast<const float*>(smem + L_::kGd + kvbuf * NW * 256);
+                    const float* gb = reinterpret_cast<const float*>(smem + L_::kGd + kvbuf * L_::kGdStage);
                     float incl = lane < L ? gb[lane] * kLog2e : 0.f;
 #pragma unroll
                     for (int off = 1; off < 64; off <<= 1) {
@@ -545,10 +655,12 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 lds_barrier();
             } else if (GATED) {
                 if (wave == 0) {
+                    const float* gc = reinterpret_cast<const float*>(smem + L_::kGd + kvbuf * L_::kGdStage);
                     float run = 0.f, loc[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        run += lane * 8 + i < L ? gpre[i] * kLog2e : 0.f;
+                        const float gv = NST == 2 ? gpre[i] : gc[lane * 8 + i];
+                        run += lane * 8 + i < L ? gv * kLog2e : 0.f;
                         loc[i] = run;
                     }
                     float incl = run;
@@ -577,23 +689,26 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
         Step nxt = cur;
         const bool has_next = next_step<MODE>(nxt, t_end, C);
-        const int nqbuf = (MODE == kFull && nxt.kb == 0) ? qbuf ^ 1 : qbuf;
+        // With three stages the output stores must precede the loads (see the wait
+        // above); with two, the loads go first so that they start earlier.
+        if (NST == 3) store_pending();
         if (more) {
             more = next_step<MODE>(ahead, t_end, C);
             if (more) {
                 ++inflight;
                 int b = kvbuf + inflight;
                 if (b >= NST) b -= NST;
-                issue(ahead, nqbuf, b);
+                issue_step(ahead, b);
             }
         }
-        store_pending();
+        if (NST != 3) store_pending();
 
         const bool fullq = (qb + 1) * kBlk <= L;     // no row of the blocks is past the chunk end
         const bool fullk = (kb + 1) * kBlk <= L;
-        const char* Qs = smem + L_::kQ + qbuf * L_::kQTile;
         const char* Ks = smem + L_::kK + kvbuf * L_::kKTile;
-        const char* Vs = smem + L_::kV + kvbuf * L_::kVTile;
+        const uint32_t qbase = lds0 + L_::kQ + qbuf * L_::kQTile;
+        const uint32_t kbase = lds0 + L_::kK + kvbuf * L_::kKTile;
+        const uint32_t vbase = lds0 + L_::kV + kvbuf * L_::kVTile;
         if (MODE == kFull) {
             if (kb == 0) {
                 // cross-chunk term X = diag(2^G) (Q S_prev), rows of block qb
@@ -601,11 +716,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) X[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                uint32_t cq[KL];
+#pragma unroll
+                for (int kl = 0; kl < KL; ++kl) cq[kl] = opaque(pq[kl] + qbase);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) {
-                        const u16x8_t a = lds16(Qs, qk_off<QRB>(mt * 16 + l16, ks * 4 + g4));
+                        const u16x8_t a = lds16a(cq[ks % KL] + mt * 16 * QRB + (ks / KL) * 256);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             const u16x8_t b = ONEBLK ? state_b(ks, nt) : Sp[ONEBLK ? 0 : ks][nt];
@@ -634,10 +752,16 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 Pr[s16] = u16x4_t{};
                 if (diag && kt > qt) continue;
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                uint32_t ck[KL], cq[KL];
+#pragma unroll
+                for (int kl = 0; kl < KL; ++kl) {
+                    ck[kl] = opaque(pq[kl] + kbase + kt * 16 * QRB);
+                    cq[kl] = opaque(pq[kl] + qbase + qt * 16 * QRB);
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const u16x8_t a = lds16(Ks, qk_off<QRB>(kt * 16 + l16, ks * 4 + g4));
-                    const u16x8_t b = lds16(Qs, qk_off<QRB>(qt * 16 + l16, ks * 4 + g4));
+                    const u16x8_t a = lds16a(ck[ks % KL] + (ks / KL) * 256);
+                    const u16x8_t b = lds16a(cq[ks % KL] + (ks / KL) * 256);
                     acc = mfma16(a, b, acc);
                 }
                 const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
@@ -676,7 +800,6 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             // 32ks + 8g .. 32ks + 8g + 7, gathered by transpose reads of K and V
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int r0 = ks * 32 + 8 * g4 + trj;
                 // zeta_l / 2^lk2: decay from key l to the chunk end, in the state's scale.
                 // Full blocks: uniform gamma^(L - 32 - 32ks - 64kb) (exponent >= 0) times
                 // fz; a partial block takes the power directly.
@@ -684,22 +807,26 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 // K^T operand of state tile dt: result lane m must receive state row
                 // srow(dt, m%4 of group m/4), so source lane (j, q) reads dims
                 // 32(dt/2) + 8q + 4((dt^q)&1) .. +3
+                uint32_t ckt[2][SL][2];
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                    for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb) ckt[pl][sl][hb] = opaque(pkt[pl][sl][hb] + kbase + ks * 32 * QRB);
                 auto kt_frag = [&](int dt) -> u16x8_t {
-                    const int d0 = 32 * (dt >> 1) + 8 * trq + 4 * ((dt ^ trq) & 1);
-                    return cat(lds_tr(Ks, qk_off<QRB>(r0, d0 >> 3) + (d0 & 7) * 2),
-                               lds_tr(Ks, qk_off<QRB>(r0 + 4, d0 >> 3) + (d0 & 7) * 2));
+                    const int sd = dt >> 1;
+                    return cat(lds_tra(ckt[0][sd % SL][dt & 1] + (sd / SL) * 256),
+                               lds_tra(ckt[1][sd % SL][dt & 1] + (sd / SL) * 256));
                 };
                 // software pipeline: the reads of the next G operand tiles are issued
                 // before the matrix instructions on the current ones (the scheduling
                 // barriers keep the compiler from serialising reads and uses)
-                constexpr int G = DT < 4 ? DT : 4;
+                constexpr int G = DT < 4 ? DT : (DT >= 16 && NW == 8 ? 2 : 4);
                 u16x8_t raw[NT], acur[G], anext[G];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int c0 = wcol + nt * 16 + 4 * trq;
-                    raw[nt] = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
-                                  lds_tr(Vs, v_off<VRB>(r0 + 4, c0 >> 3) + (c0 & 7) * 2));
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    raw[nt] = cat(lds_tra(vbase + pvs[0][nt] + ks * 32 * VRB), lds_tra(vbase + pvs[1][nt] + ks * 32 * VRB));
 #pragma unroll
                 for (int j = 0; j < G; ++j) acur[j] = kt_frag(j);
                 __builtin_amdgcn_sched_barrier(0);
@@ -765,10 +892,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 u16x8_t b[NT];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int c0 = wcol + nt * 16 + 4 * trq;      // this lane's 4 source columns
-                    const int r0 = ks * 32 + 4 * g4 + trj;
-                    b[nt] = cat(lds_tr(Vs, v_off<VRB>(r0, c0 >> 3) + (c0 & 7) * 2),
-                                lds_tr(Vs, v_off<VRB>(r0 + 16, c0 >> 3) + (c0 & 7) * 2));
+                    const uint32_t va = opaque(vbase + pvp[nt]);
+                    b[nt] = cat(lds_tra(va + ks * 32 * VRB), lds_tra(va + (ks * 32 + 16) * VRB));
                 }
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -785,7 +910,6 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
         if (!has_next) break;
         cur = nxt;
-        qbuf = nqbuf;
         kvbuf = kvbuf + 1 == NST ? 0 : kvbuf + 1;
         if (inflight > 0) --inflight;
     }
@@ -836,7 +960,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
 
 template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
-    const size_t lds = Lds<DK, DVT, GATED, MODE == kFull, stages_for(MODE), NW>::kBytes;
+    const size_t lds = Lds<DK, DVT, GATED, MODE == kFull, stages_for<DK, DVT, GATED, MODE, NW>(), NW>::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>),
