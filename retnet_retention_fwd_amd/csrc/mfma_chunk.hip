@@ -262,7 +262,9 @@ enum Mode { kFull = 0, kStateOnly = 1 };
 // every such workload -- their loads are bandwidth-, not latency-limited.
 template <int DK, int DVT, bool GATED, int MODE, int NW>
 constexpr int stages_for() {
-    return MODE != kFull ? 4 : 2;
+    if (MODE == kFull) return 2;
+    return Lds<DK, DVT, GATED, false, 4, NW>::kBytes <= kLdsBytes ? 4
+         : Lds<DK, DVT, GATED, false, 3, NW>::kBytes <= kLdsBytes ? 3 : 2;
 }
 
 // The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
@@ -719,17 +721,29 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 uint32_t cq[KL];
 #pragma unroll
                 for (int kl = 0; kl < KL; ++kl) cq[kl] = opaque(pq[kl] + qbase);
+                // Q fragments of reduction step ks+1 are read while step ks multiplies
+                // (the scheduling barriers keep the compiler from serialising them)
+                u16x8_t qa[4], qn[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) qa[mt] = lds16a(cq[0] + mt * 16 * QRB);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const u16x8_t a = lds16a(cq[ks % KL] + mt * 16 * QRB + (ks / KL) * 256);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            const u16x8_t b = ONEBLK ? state_b(ks, nt) : Sp[ONEBLK ? 0 : ks][nt];
-                            X[mt][nt] = mfma16(b, a, X[mt][nt]);   // transposed: (S^T Q^T)
-                        }
+                        for (int mt = 0; mt < 4; ++mt)
+                            qn[mt] = lds16a(cq[(ks + 1) % KL] + mt * 16 * QRB + ((ks + 1) / KL) * 256);
                     }
+                    u16x8_t b[NT];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) b[nt] = ONEBLK ? state_b(ks, nt) : Sp[ONEBLK ? 0 : ks][nt];
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(b[nt], qa[mt], X[mt][nt]);   // (S^T Q^T)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) qa[mt] = qn[mt];
                 }
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -758,11 +772,22 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     ck[kl] = opaque(pq[kl] + kbase + kt * 16 * QRB);
                     cq[kl] = opaque(pq[kl] + qbase + qt * 16 * QRB);
                 }
+                // two reduction steps of fragments in flight ahead of the products
+                u16x8_t ka[KS], qv[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS && ks < 2; ++ks) {
+                    ka[ks] = lds16a(ck[ks % KL] + (ks / KL) * 256);
+                    qv[ks] = lds16a(cq[ks % KL] + (ks / KL) * 256);
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const u16x8_t a = lds16a(ck[ks % KL] + (ks / KL) * 256);
-                    const u16x8_t b = lds16a(cq[ks % KL] + (ks / KL) * 256);
-                    acc = mfma16(a, b, acc);
+                    if (ks + 2 < KS) {
+                        ka[ks + 2] = lds16a(ck[(ks + 2) % KL] + ((ks + 2) / KL) * 256);
+                        qv[ks + 2] = lds16a(cq[(ks + 2) % KL] + ((ks + 2) / KL) * 256);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc = mfma16(ka[ks], qv[ks], acc);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 const int j = qb * kBlk + qt * 16 + l16;      // query (chunk-local)
                 const bool dtile = diag && kt == qt;
@@ -990,6 +1015,9 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     RETN_PRE(64, 128)
     RETN_PRE(128, 64)
     RETN_PRE(128, 128)
+#ifdef PRE256
+    RETN_PRE(64, 256)
+#endif
 #undef RETN_PRE
     return hipErrorInvalidValue;
 }
@@ -1071,6 +1099,12 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;
     p.pre_dkt = std::min(dk, 128);
     p.pre_dvt = dv % 128 == 0 ? 128 : 64;
+#ifdef PRE_B
+    if (dv % 256 == 0) { p.pre_dkt = 64; p.pre_dvt = 256; }
+#endif
+#ifdef PRE_C
+    p.pre_dkt = 64;
+#endif
     p.fuse_scan = p.nseg <= kFuseScanMax ? 1 : 0;
     if (p.nseg > 1) {
         const size_t per_bh = static_cast<size_t>(dk) * dv;
