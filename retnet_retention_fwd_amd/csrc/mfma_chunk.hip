@@ -338,8 +338,13 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     constexpr int NST = stages_for<DK, DVT, GATED, MODE, NW>();
     using L_ = Lds<DK, DVT, GATED, MODE == kFull, NST, NW>;
     static_assert(L_::kBytes <= kLdsBytes, "LDS layout too large");
-    constexpr int NT = DVT / (16 * NW);   // 16-column tiles per wave
-    static_assert(NT >= 1 && NT * 16 * NW == DVT && 16 % NW == 0, "bad wave split");
+    // The pre-pass splits each 64-token block between two halves of the waves (keys
+    // 0..31 and 32..63): each wave then owns twice the columns, which halves the K^T
+    // reads per matrix instruction; the two partial states are summed at the end.
+    constexpr bool SPLITK = MODE == kStateOnly && NW >= 2;
+    constexpr int NWC = SPLITK ? NW / 2 : NW;     // waves across the columns
+    constexpr int NT = DVT / (16 * NWC);          // 16-column tiles per wave
+    static_assert(NT >= 1 && NT * 16 * NWC == DVT && 16 % NW == 0, "bad wave split");
     constexpr int DT = DK / 16;           // 16-row tiles of the state
     constexpr int KS = DK / 32;           // reduction steps over DK
     constexpr int QRB = L_::kQRow, VRB = L_::kVRow;
@@ -361,7 +366,9 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int col0 = dvt * DVT;                         // first column of this tile
-    const int wcol = wave * 16 * NT;                    // wave's first column in the tile
+    const int cwave = SPLITK ? wave % NWC : wave;       // column position of this wave
+    const int khalf = SPLITK ? wave / NWC : 0;         // pre-pass: the block half it sums
+    const int wcol = cwave * 16 * NT;                   // wave's first column in the tile
     // transpose-read source coordinates of this lane within its 16-lane group
     const int trj = l16 >> 2, trq = l16 & 3;
 
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             pq[kl] = static_cast<uint32_t>(l16 * QRB + 16 * (4 * (kl ^ (s >> 2)) + (g4 ^ (s & 3))));
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
-            const int rb = 8 * g4 + trj + 4 * pl;
+            const int rb = 32 * khalf + 8 * g4 + trj + 4 * pl;
             const int w = swz_qk<QRB / 16>(rb);
 #pragma unroll
             for (int sl = 0; sl < SL; ++sl)
@@ -465,14 +472,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             const int sv = swz_v<VRB / 16>(rb);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-                pvs[pl][nt] = static_cast<uint32_t>(rb * VRB + 16 * (2 * ((wave * NT + nt) ^ (sv >> 1)) + (trq >> 1)) +
+                pvs[pl][nt] = static_cast<uint32_t>(rb * VRB + 16 * (2 * ((cwave * NT + nt) ^ (sv >> 1)) + (trq >> 1)) +
                                                     8 * (trq & 1));
         }
         const int rbp = 4 * g4 + trj;
         const int svp = swz_v<VRB / 16>(rbp);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            pvp[nt] = static_cast<uint32_t>(rbp * VRB + 16 * (2 * ((wave * NT + nt) ^ (svp >> 1)) + (trq >> 1)) +
+            pvp[nt] = static_cast<uint32_t>(rbp * VRB + 16 * (2 * ((cwave * NT + nt) ^ (svp >> 1)) + (trq >> 1)) +
                                             8 * (trq & 1));
     }
 
@@ -824,7 +831,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             // S += K^T (V (.) zeta) over the keys of block qb; slots are keys
             // 32ks + 8g .. 32ks + 8g + 7, gathered by transpose reads of K and V
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int kh = 0; kh < (SPLITK ? 1 : 2); ++kh) {
+                // key half ks of the block (the patterns already hold the pre-pass
+                // wave's half; ks only enters the decays and the key indices)
+                const int ks = SPLITK ? khalf : kh;
                 // zeta_l / 2^lk2: decay from key l to the chunk end, in the state's scale.
                 // Full blocks: uniform gamma^(L - 32 - 32ks - 64kb) (exponent >= 0) times
                 // fz; a partial block takes the power directly.
@@ -838,7 +848,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
                     for (int sl = 0; sl < SL; ++sl)
 #pragma unroll
-                        for (int hb = 0; hb < 2; ++hb) ckt[pl][sl][hb] = opaque(pkt[pl][sl][hb] + kbase + ks * 32 * QRB);
+                        for (int hb = 0; hb < 2; ++hb) ckt[pl][sl][hb] = opaque(pkt[pl][sl][hb] + kbase + kh * 32 * QRB);
                 auto kt_frag = [&](int dt) -> u16x8_t {
                     const int sd = dt >> 1;
                     return cat(lds_tra(ckt[0][sd % SL][dt & 1] + (sd / SL) * 256),
@@ -851,7 +861,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 u16x8_t raw[NT], acur[G], anext[G];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    raw[nt] = cat(lds_tra(vbase + pvs[0][nt] + ks * 32 * VRB), lds_tra(vbase + pvs[1][nt] + ks * 32 * VRB));
+                    raw[nt] = cat(lds_tra(vbase + pvs[0][nt] + kh * 32 * VRB), lds_tra(vbase + pvs[1][nt] + kh * 32 * VRB));
 #pragma unroll
                 for (int j = 0; j < G; ++j) acur[j] = kt_frag(j);
                 __builtin_amdgcn_sched_barrier(0);
@@ -940,6 +950,33 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     }
     store_pending();
 
+    if (SPLITK) {
+        // sum the two key halves: the second half's waves park their partial states in
+        // LDS (the tile buffers are free once every wave is past the loop)
+        float* red = reinterpret_cast<float*>(smem);
+        static_assert(DK * DVT * 4 <= L_::kGd, "reduction area exceeds the tile buffers");
+        const int cidx = wcol + l16;
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (khalf == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[srow(dt, i) * DVT + cidx + nt * 16] = S[dt][nt][i];
+        }
+        lds_barrier();
+        if (khalf == 0) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[dt][nt][i] += red[srow(dt, i) * DVT + cidx + nt * 16];
+        }
+    }
+
     // ---- results
     float* dst = nullptr;
     if (MODE == kFull) {
@@ -948,7 +985,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         dst = ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
         if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
     }
-    if (dst != nullptr) {
+    if (dst != nullptr && (!SPLITK || khalf == 0)) {
         const int cidx = col0 + wcol + l16;
         const float r = exp2_fast(lk2);
 #pragma unroll
@@ -1015,9 +1052,6 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     RETN_PRE(64, 128)
     RETN_PRE(128, 64)
     RETN_PRE(128, 128)
-#ifdef PRE256
-    RETN_PRE(64, 256)
-#endif
 #undef RETN_PRE
     return hipErrorInvalidValue;
 }
@@ -1099,12 +1133,6 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     p.nseg = (nchunks + p.seg_chunks - 1) / p.seg_chunks;
     p.pre_dkt = std::min(dk, 128);
     p.pre_dvt = dv % 128 == 0 ? 128 : 64;
-#ifdef PRE_B
-    if (dv % 256 == 0) { p.pre_dkt = 64; p.pre_dvt = 256; }
-#endif
-#ifdef PRE_C
-    p.pre_dkt = 64;
-#endif
     p.fuse_scan = p.nseg <= kFuseScanMax ? 1 : 0;
     if (p.nseg > 1) {
         const size_t per_bh = static_cast<size_t>(dk) * dv;
