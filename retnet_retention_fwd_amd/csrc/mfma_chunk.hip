@@ -255,6 +255,10 @@ struct TileCopy {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) buf2lds16(rsrc, voff[i], row0_bytes, base + i * NW * 1024u);
     }
+    // copy i of this wave alone; wbase = tile_lds + 1024 * wave
+    __device__ __forceinline__ void issue_one(int i, uint32_t wbase, const u32x4_t& rsrc, uint32_t row0_bytes) const {
+        buf2lds16(rsrc, voff[i], row0_bytes, wbase + i * NW * 1024u);
+    }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
 // Pipeline stages: the pre-pass keeps four blocks in flight.  The full pass
@@ -388,10 +392,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const u32x4_t k_rs = make_rsrc(k + qk_bh + srow0, static_cast<uint32_t>(N) * dk * 2);
     const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
     const uint32_t lds0 = lds_addr_of(smem);
-    TileCopy<QRB, false, NW> qcp;
-    TileCopy<QRB, false, NW> kcp;
+    TileCopy<QRB, false, NW> kcp;   // Q and K tiles (same row length and swizzle)
     TileCopy<VRB, true, NW> vcp;
-    if (MODE == kFull) qcp.init(dk * 2, wave, lane);
     kcp.init(dk * 2, wave, lane);
     vcp.init(dv * 2, wave, lane);
 
@@ -523,14 +525,43 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     int qbuf = 0, kvbuf = 0;
     constexpr int kGLoads = (kMaxChunk / 64 + NW - 1) / NW;   // full pass: decay copies per wave
     // issue the asynchronous loads of step s into buffers (qb_, kvb_)
-    auto issue = [&](const Step& s, int qb_, int kvb_) {
-        const int k0 = s.cs + s.kb * kBlk;
-        if (MODE == kFull && s.kb == 0) {
-            const int q0 = s.cs + s.qb * kBlk;
-            qcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * dk * 2, wave);
+    // Deferred copies (full pass, two stages): a step's successor tiles are issued one
+    // instruction at a time between the matrix instructions of the cross term, so the
+    // copies of the eight waves do not queue up at the memory pipeline all at once.
+    constexpr bool kSpread = MODE == kFull && NST == 2;
+    constexpr int kNQ = TileCopy<QRB, false, NW>::kPerWave, kNV = TileCopy<VRB, true, NW>::kPerWave;
+    constexpr int kNOps = 2 * kNQ + kNV;       // Q, K, V copies of one step
+    bool dq = false, dkv = false;              // pending: Q tile, K and V tiles
+    uint32_t dq_lds = 0, dk_lds = 0, dv_lds = 0, dq_off = 0, dk_off = 0, dv_off = 0;
+    auto deferred_op = [&](int i) {
+        if (i < kNQ) {
+            if (dq) kcp.issue_one(i, dq_lds, q_rs, dq_off);
+        } else if (i < 2 * kNQ) {
+            if (dkv) kcp.issue_one(i - kNQ, dk_lds, k_rs, dk_off);
+        } else if (dkv) {
+            vcp.issue_one(i - 2 * kNQ, dv_lds, v_rs, dv_off);
         }
-        kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * dk * 2, wave);
-        vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, wave);
+    };
+    auto issue = [&](const Step& s, int qb_, int kvb_, bool defer) {
+        const int k0 = s.cs + s.kb * kBlk;
+        const uint32_t wofs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+        if (kSpread && defer) {
+            dq = s.kb == 0;
+            dkv = true;
+            dq_lds = lds0 + L_::kQ + qb_ * L_::kQTile + wofs;
+            dk_lds = lds0 + L_::kK + kvb_ * L_::kKTile + wofs;
+            dv_lds = lds0 + L_::kV + kvb_ * L_::kVTile + wofs;
+            dq_off = static_cast<uint32_t>(s.cs + s.qb * kBlk) * dk * 2;
+            dk_off = static_cast<uint32_t>(k0) * dk * 2;
+            dv_off = static_cast<uint32_t>(k0) * dv * 2;
+        } else {
+            if (MODE == kFull && s.kb == 0) {
+                const int q0 = s.cs + s.qb * kBlk;
+                kcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * dk * 2, wave);
+            }
+            kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * dk * 2, wave);
+            vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, wave);
+        }
         if (GATED && MODE == kStateOnly) {
             // the pre-pass walks single blocks: every wave copies the block's 64 decays
             buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
@@ -562,6 +593,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     constexpr int kLoadsPerStep = kLoadsKV + (GATED ? 1 : 0);   // pre-pass
 
     int pend_q0 = -1, pend_nq = 0;   // rows of a finished query block not yet stored
+    int st_last = 0;                 // stores issued by the last step: 0 none, 1 4*NT, 2 fewer
     // lane (g, l%16) stores 4 adjacent columns of row l%16 of each 16-row tile: a
     // wave-uniform base plus a 32-bit lane offset
     const uint32_t st_lane = static_cast<uint32_t>(l16 * dv + 4 * g4);
@@ -595,11 +627,11 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // which optional loads (bit 0: Q, bit 1: decays) it issued.
     int qlast = NST - 1;       // Q stage of the most recent Q load
     uint32_t qof = 0, ldof = 0;
-    auto issue_step = [&](const Step& s, int b) {
+    auto issue_step = [&](const Step& s, int b, bool defer) {
         const bool needq = MODE == kFull && s.kb == 0;
         const bool needg = GATED && MODE == kFull && NST == 3 && s.qb == 0 && s.kb == 0;
         if (needq) qlast = qlast + 1 == NST ? 0 : qlast + 1;
-        issue(s, qlast, b);
+        issue(s, qlast, b, defer);
         qof = (qof & ~(3u << (2 * b))) | (static_cast<uint32_t>(qlast) << (2 * b));
         ldof = (ldof & ~(3u << (2 * b))) | ((needq ? 1u : 0u) | (needg ? 2u : 0u)) << (2 * b);
     };
@@ -609,14 +641,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // would make it wait there for them.
     __builtin_amdgcn_s_waitcnt(0);
     Step cur{t_begin, 0, 0};
-    issue_step(cur, 0);
+    issue_step(cur, 0, false);
     // steps issued beyond cur (at most NST - 2 at the top of an iteration)
     Step ahead = cur;
     bool more = true;
     int inflight = 0;
     for (int i = 0; i < NST - 2 && more; ++i) {
         more = next_step<MODE>(ahead, t_end, C);
-        if (more) issue_step(ahead, ++inflight);
+        if (more) issue_step(ahead, ++inflight, false);
     }
 
     while (true) {
@@ -639,6 +671,9 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             } else {
                 wait_vmcnt<0>();
             }
+        } else if (kSpread && st_last == 1) {
+            // the youngest operations are the previous step's output stores
+            wait_vmcnt<4 * NT>();
         } else {
             __builtin_amdgcn_s_waitcnt(0);
         }
@@ -707,7 +742,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 ++inflight;
                 int b = kvbuf + inflight;
                 if (b >= NST) b -= NST;
-                issue_step(ahead, b);
+                // deferred to the cross term when this step has one
+                issue_step(ahead, b, kb == 0);
             }
         }
         if (NST != 3) store_pending();
@@ -748,10 +784,15 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(b[nt], qa[mt], X[mt][nt]);   // (S^T Q^T)
+                    if (kSpread) {
+#pragma unroll
+                        for (int i = ks * kNOps / KS; i < (ks + 1) * kNOps / KS; ++i) deferred_op(i);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) qa[mt] = qn[mt];
                 }
+                dq = dkv = false;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const int j = qb * kBlk + mt * 16 + l16;     // this lane's query row
@@ -942,6 +983,12 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         if (MODE == kFull && diag) {
             pend_q0 = cur.cs + qb * kBlk;
             pend_nq = min(kBlk, L - qb * kBlk);
+        }
+        if (kSpread) {
+            // two stages: a finished block is stored at once (the next step's wait
+            // skips these stores)
+            st_last = pend_q0 < 0 ? 0 : pend_nq == kBlk ? 1 : 2;
+            store_pending();
         }
         if (!has_next) break;
         cur = nxt;
