@@ -41,6 +41,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace retn {
 
 namespace {
@@ -203,26 +205,29 @@ __device__ __forceinline__ int v_off(int row, int unit) {
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64 lanes][16 B]
 
-// LDS layout: NST stages of Q (full pass only), K and V blocks and of the decays the
-// block's step loads (gated: the pre-pass copies its block's 64 decays once per wave,
-// the full pass the chunk's decays at a chunk start), the P fragments of the current
-// block pair and (gated) the chunk's log2 decays.  When the buffers leave no room for P
-// (kPInK), P is written into the current K buffer once every wave is done with K.
-template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW>
+// LDS layout: QS stages of Q (full pass only), NST stages of K and V blocks and of the
+// decays the block's step loads (gated: the pre-pass copies its block's 64 decays once
+// per wave, the full pass the chunk's decays at a chunk start), the P fragments of the
+// current block pair, optionally (XST) a staging area for one 64-row output block, and
+// (gated) the chunk's log2 decays.  When the buffers leave no room for P (kPInK), P is
+// written into the current K buffer once every wave is done with K.
+template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW, int QS = NST, bool XST = false>
 struct Lds {
     static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
     static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
-    static constexpr int kQ = 0;                          // NST buffers (none without Q)
-    static constexpr int kK = kQ + (HASQ ? NST * kQTile : 0);   // NST buffers
+    static constexpr int kQ = 0;                          // QS buffers (none without Q)
+    static constexpr int kK = kQ + (HASQ ? QS * kQTile : 0);   // NST buffers
     static constexpr int kV = kK + NST * kKTile;          // NST buffers
     static constexpr int kGdStage = !GATED ? 0 : (HASQ ? (NST == 3 ? kMaxChunk * 4 : 0) : NW * 256);
     static constexpr int kGd = kV + NST * kVTile;         // NST stages of decays
     static constexpr int kEnd = kGd + NST * kGdStage;
     static constexpr int kGBytes = GATED ? kMaxChunk * 4 : 0;
-    static constexpr bool kPInK = HASQ && kEnd + kPBytes + kGBytes > kLdsBytes;
+    static constexpr int kXBytes = HASQ && XST ? kBlk * kVRow : 0;
+    static constexpr bool kPInK = HASQ && kEnd + kPBytes + kXBytes + kGBytes > kLdsBytes;
     static constexpr int kPSize = HASQ && !kPInK ? kPBytes : 0;
     static constexpr int kP = kPInK ? 0 : kEnd;           // unused when kPInK
-    static constexpr int kG = kEnd + kPSize;
+    static constexpr int kX = kEnd + kPSize;
+    static constexpr int kG = kX + kXBytes;
     static constexpr int kBytes = kG + kGBytes;
 };
 
@@ -270,6 +275,23 @@ constexpr int stages_for() {
     return Lds<DK, DVT, GATED, false, 4, NW>::kBytes <= kLdsBytes ? 4
          : Lds<DK, DVT, GATED, false, 3, NW>::kBytes <= kLdsBytes ? 3 : 2;
 }
+
+// Layout of the full pass with two stages: each finished output block is staged in LDS
+// so that it leaves in whole 128-byte lines (one wave alone owns 32 bytes of a row).
+// Q keeps two stages when that fits; otherwise single-block chunks keep one Q stage,
+// refilled once every wave is past the scores.  Other shapes store from registers.
+template <int DK, int DVT, bool GATED, int MODE, int NW, bool ONEBLK>
+struct Plan {
+    static constexpr int NST = stages_for<DK, DVT, GATED, MODE, NW>();
+    static constexpr bool kFull2 = MODE == kFull && NST == 2;
+    using L2 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, NST, true>;
+    using L1 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, 1, true>;
+    static constexpr bool kQ2 = kFull2 && !L2::kPInK && L2::kBytes <= kLdsBytes;
+    static constexpr bool kQ1 = kFull2 && !kQ2 && ONEBLK && !L1::kPInK && L1::kBytes <= kLdsBytes;
+    static constexpr bool kStage = kQ2 || kQ1;
+    static constexpr int QS = kQ1 ? 1 : NST;
+    using L = std::conditional_t<kQ1, L1, std::conditional_t<kQ2, L2, Lds<DK, DVT, GATED, MODE == kFull, NST, NW>>>;
+};
 
 // The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
 // 0,4,5,8,9,10,12,13,14,15, then 1,2,3,6,7,11 (one 4-bit entry per slot).
@@ -339,9 +361,12 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int H = ka.H, N = ka.N, dv = ka.dv, C = ka.C, dk = ka.dk;
     const int seg_tokens = ka.seg_tokens, nseg = ka.nseg, ndvt = ka.ndvt, ndkt = ka.ndkt;
     const int total_groups = ka.total_groups;
-    constexpr int NST = stages_for<DK, DVT, GATED, MODE, NW>();
-    using L_ = Lds<DK, DVT, GATED, MODE == kFull, NST, NW>;
+    using PL = Plan<DK, DVT, GATED, MODE, NW, ONEBLK>;
+    constexpr int NST = PL::NST;
+    using L_ = typename PL::L;
     static_assert(L_::kBytes <= kLdsBytes, "LDS layout too large");
+    constexpr bool kStage = PL::kStage;   // output blocks leave through the LDS staging area
+    constexpr bool kQ1 = PL::kQ1;         // one Q stage, refilled after the P barrier
     // The pre-pass splits each 64-token block between two halves of the waves (keys
     // 0..31 and 32..63): each wave then owns twice the columns, which halves the K^T
     // reads per matrix instruction; the two partial states are summed at the end.
@@ -610,6 +635,37 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
         pend_q0 = -1;
     };
+    // Staged output: a finished block goes to LDS as bf16, row-major [64][DVT] with the
+    // 16-byte units of row r rotated by XOR with r (no bank conflicts either way); after
+    // the next step's barrier the workgroup stores it in whole rows, 16 bytes per lane.
+    constexpr int kXU = DVT / 8;                 // 16-byte units per staged row
+    constexpr int kXRounds = kBlk * kXU / (NW * 64);
+    static_assert(!kStage || kXRounds * NW * 64 == kBlk * kXU, "staged rows must split evenly");
+    int xs_q0 = -1;                              // first row of the staged block
+    auto stage_write = [&]() {
+        char* const xs = smem + L_::kX;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int row = mt * 16 + l16;
+                const int u = (wcol + nt * 16) / 8 + (g4 >> 1);
+                *reinterpret_cast<u16x4_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16 + (g4 & 1) * 8) =
+                    bf4(X[mt][nt]);
+            }
+    };
+    auto stage_store = [&]() {
+        const char* const xs = smem + L_::kX;
+        bf16_t* const base = o + v_bh + static_cast<size_t>(xs_q0) * dv + col0;
+#pragma unroll
+        for (int r = 0; r < kXRounds; ++r) {
+            const int e = r * NW * 64 + tid;
+            const int row = e / kXU, u = e % kXU;
+            const u16x8_t val = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16);
+            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = val;
+        }
+        xs_q0 = -1;
+    };
 
     // bf16 score tiles of this wave (slot s16 holds tile tile_order(wave + s16 NW)),
     // written to LDS as P fragments [qt][key pair][lane][16 B]
@@ -625,12 +681,12 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
     // Ring bookkeeping (wave-uniform, 2 bits per K/V stage): the Q stage a step reads and
     // which optional loads (bit 0: Q, bit 1: decays) it issued.
-    int qlast = NST - 1;       // Q stage of the most recent Q load
+    int qlast = PL::QS - 1;    // Q stage of the most recent Q load
     uint32_t qof = 0, ldof = 0;
     auto issue_step = [&](const Step& s, int b, bool defer) {
         const bool needq = MODE == kFull && s.kb == 0;
         const bool needg = GATED && MODE == kFull && NST == 3 && s.qb == 0 && s.kb == 0;
-        if (needq) qlast = qlast + 1 == NST ? 0 : qlast + 1;
+        if (needq) qlast = qlast + 1 == PL::QS ? 0 : qlast + 1;
         issue(s, qlast, b, defer);
         qof = (qof & ~(3u << (2 * b))) | (static_cast<uint32_t>(qlast) << (2 * b));
         ldof = (ldof & ~(3u << (2 * b))) | ((needq ? 1u : 0u) | (needg ? 2u : 0u)) << (2 * b);
@@ -747,6 +803,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             }
         }
         if (NST != 3) store_pending();
+        // the previous block, staged before this step's barrier
+        if (kStage && xs_q0 >= 0) stage_store();
 
         const bool fullq = (qb + 1) * kBlk <= L;     // no row of the blocks is past the chunk end
         const bool fullk = (kb + 1) * kBlk <= L;
@@ -785,14 +843,17 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(b[nt], qa[mt], X[mt][nt]);   // (S^T Q^T)
                     if (kSpread) {
+                        // (one Q stage: the Q copy waits for the P barrier)
+                        constexpr int first = kQ1 ? kNQ : 0, nops = kNOps - first;
 #pragma unroll
-                        for (int i = ks * kNOps / KS; i < (ks + 1) * kNOps / KS; ++i) deferred_op(i);
+                        for (int i = ks * nops / KS; i < (ks + 1) * nops / KS; ++i) deferred_op(first + i);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) qa[mt] = qn[mt];
                 }
-                dq = dkv = false;
+                dkv = false;
+                if (!kQ1) dq = false;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const int j = qb * kBlk + mt * 16 + l16;     // this lane's query row
@@ -857,6 +918,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 Pr[s16] = bf4(f32x4_t{acc[0] * w[0], acc[1] * w[1], acc[2] * w[2], acc[3] * w[3]});
             }
             if (!L_::kPInK) write_p(Pfix);
+            // one Q stage: every wave is past its Q reads here, and P is complete
+            if (kQ1) lds_barrier();
         }
         if (qb == 0 && kb == 0 && lk2 < -64.f) {
             // rescale the registers once the state scale gets small (after the cross
@@ -946,12 +1009,20 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     for (int j = 0; j < G; ++j)
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) S[g0 + j][nt] = mfma16(acur[j], b[nt], S[g0 + j][nt]);
+                    if (kQ1 && kh == 0) {
+                        // one Q stage: the next block's Q copies go out here
+                        constexpr int NG = DT / G;
+                        const int gi = g0 / G;
+#pragma unroll
+                        for (int i = gi * kNQ / NG; i < (gi + 1) * kNQ / NG; ++i) deferred_op(i);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int j = 0; j < G; ++j) acur[j] = anext[j];
                 }
             }
         }
+        if (kQ1) dq = false;
         if (MODE == kFull) {
             // P goes to its own LDS area, or into the K buffer once no wave reads K
             const char* Pf = Pfix;
@@ -960,7 +1031,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 write_p(const_cast<char*>(Ks));
                 Pf = Ks;
             }
-            lds_barrier();
+            if (!kQ1) lds_barrier();
             // X += P V over the 64 keys of block kb (as X^T += V^T P^T); V fragments by transpose reads:
             // slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
 #pragma unroll
@@ -984,7 +1055,13 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             pend_q0 = cur.cs + qb * kBlk;
             pend_nq = min(kBlk, L - qb * kBlk);
         }
-        if (kSpread) {
+        if (kStage && pend_q0 >= 0 && has_next && pend_nq == kBlk) {
+            // full block with steps to come: staged, stored after the next barrier
+            stage_write();
+            xs_q0 = pend_q0;
+            pend_q0 = -1;
+            st_last = 0;
+        } else if (kSpread) {
             // two stages: a finished block is stored at once (the next step's wait
             // skips these stores)
             st_last = pend_q0 < 0 ? 0 : pend_nq == kBlk ? 1 : 2;
@@ -996,6 +1073,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         if (inflight > 0) --inflight;
     }
     store_pending();
+    if (kStage && xs_q0 >= 0) {   // (the last step stores from registers; kept for safety)
+        lds_barrier();
+        stage_store();
+    }
 
     if (SPLITK) {
         // sum the two key halves: the second half's waves park their partial states in
@@ -1069,7 +1150,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
 
 template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
-    const size_t lds = Lds<DK, DVT, GATED, MODE == kFull, stages_for<DK, DVT, GATED, MODE, NW>(), NW>::kBytes;
+    const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK>::L::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>),
