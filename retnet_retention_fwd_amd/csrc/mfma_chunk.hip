@@ -654,15 +654,25 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     bf4(X[mt][nt]);
             }
     };
-    auto stage_store = [&]() {
+    // the reads right after the barrier, the stores a little later (between the first
+    // matrix instructions of the cross term, when the step has one)
+    u16x8_t xv[kStage ? kXRounds : 1];
+    auto stage_load = [&]() {
         const char* const xs = smem + L_::kX;
+#pragma unroll
+        for (int r = 0; r < kXRounds; ++r) {
+            const int e = r * NW * 64 + tid;
+            const int row = e / kXU, u = e % kXU;
+            xv[r] = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16);
+        }
+    };
+    auto stage_emit = [&]() {
         bf16_t* const base = o + v_bh + static_cast<size_t>(xs_q0) * dv + col0;
 #pragma unroll
         for (int r = 0; r < kXRounds; ++r) {
             const int e = r * NW * 64 + tid;
             const int row = e / kXU, u = e % kXU;
-            const u16x8_t val = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16);
-            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = val;
+            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = xv[r];
         }
         xs_q0 = -1;
     };
@@ -734,6 +744,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             __builtin_amdgcn_s_waitcnt(0);
         }
         lds_barrier();
+        if (kStage && xs_q0 >= 0) stage_load();
         qbuf = static_cast<int>((qof >> (2 * kvbuf)) & 3u);
         const int L = min(C, t_end - cur.cs);
         const int qb = ONEBLK ? 0 : cur.qb, kb = ONEBLK ? 0 : cur.kb;
@@ -803,8 +814,9 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             }
         }
         if (NST != 3) store_pending();
-        // the previous block, staged before this step's barrier
-        if (kStage && xs_q0 >= 0) stage_store();
+        // the previous block, staged before this step's barrier (steps without a cross
+        // term store it here)
+        if (kStage && xs_q0 >= 0 && kb != 0) stage_emit();
 
         const bool fullq = (qb + 1) * kBlk <= L;     // no row of the blocks is past the chunk end
         const bool fullk = (kb + 1) * kBlk <= L;
@@ -842,6 +854,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) X[mt][nt] = mfma16(b[nt], qa[mt], X[mt][nt]);   // (S^T Q^T)
+                    if (kStage && ks == 0 && xs_q0 >= 0) stage_emit();
                     if (kSpread) {
                         // (one Q stage: the Q copy waits for the P barrier)
                         constexpr int first = kQ1 ? kNQ : 0, nops = kNOps - first;
@@ -1075,7 +1088,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     store_pending();
     if (kStage && xs_q0 >= 0) {   // (the last step stores from registers; kept for safety)
         lds_barrier();
-        stage_store();
+        stage_load();
+        stage_emit();
     }
 
     if (SPLITK) {
