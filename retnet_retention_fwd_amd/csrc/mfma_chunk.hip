@@ -702,12 +702,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         ldof = (ldof & ~(3u << (2 * b))) | ((needq ? 1u : 0u) | (needg ? 2u : 0u)) << (2 * b);
     };
 
-    // Drain the loads of the incoming state before the first asynchronous copy: the
-    // compiler does not count the copies, so a load it still tracked inside the loop
-    // would make it wait there for them.
-    __builtin_amdgcn_s_waitcnt(0);
+    // Drain the loads of the incoming state before the loop: the compiler does not count
+    // the asynchronous copies, so a load it still tracked inside the loop would make it
+    // wait there for them.  The full pass issues its first copies before the drain, so
+    // that the two latencies overlap.
     Step cur{t_begin, 0, 0};
-    issue_step(cur, 0, false);
+    if (MODE == kFull) issue_step(cur, 0, false);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (MODE != kFull) issue_step(cur, 0, false);
     // steps issued beyond cur (at most NST - 2 at the top of an iteration)
     Step ahead = cur;
     bool more = true;
@@ -1127,37 +1129,66 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         dst = ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
         if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
     }
-    if (dst != nullptr && (!SPLITK || khalf == 0)) {
-        const int cidx = col0 + wcol + l16;
+    if (dst != nullptr) {
+        // the tile goes out through LDS as well, in whole rows of 16-byte stores
+        float* const st = reinterpret_cast<float*>(smem);
         const float r = exp2_fast(lk2);
+        wait_vmcnt<0>();
+        lds_barrier();   // every wave is done with the tile buffers
+        if (!SPLITK || khalf == 0) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dst[static_cast<uint32_t>(srow(dt, i) * dv + cidx + nt * 16)] = S[dt][nt][i] * r;
+                    for (int i = 0; i < 4; ++i) st[srow(dt, i) * DVT + wcol + nt * 16 + l16] = S[dt][nt][i] * r;
+        }
+        lds_barrier();
+        constexpr int kU = DVT / 4;                          // 16-byte units per row
+        constexpr int kRounds = DK * kU / (NW * 64);
+        static_assert(kRounds * NW * 64 == DK * kU, "state rows must split evenly");
+#pragma unroll
+        for (int rr = 0; rr < kRounds; ++rr) {
+            const int e = rr * NW * 64 + tid;
+            const int row = e / kU, u = e % kU;
+            *reinterpret_cast<f32x4_t*>(dst + static_cast<size_t>(row) * dv + col0 + u * 4) =
+                *reinterpret_cast<const f32x4_t*>(st + row * DVT + u * 4);
+        }
     }
 }
 
 // Exclusive scan of segment states, in place:  buf[seg] <- state entering seg.
 //   S = state_in (or 0); for seg: T = buf[seg]; buf[seg] = S; S = 2^(l2[seg]) S + T.
 // The last segment's local state is never computed (nor read).  One thread per state
-// element of one (b,h); blocks_per_bh blocks per (b,h).
+// element of one (b,h); blocks_per_bh blocks per (b,h).  The local states of 8
+// segments are loaded before any of them is replaced, so a batch's loads are in flight
+// together (the kernel is bound by memory latency, not bandwidth).
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ buf,
                                                            const float* __restrict__ seg_log2,
                                                            const float* __restrict__ state_in,
                                                            int nseg, size_t per_bh, int blocks_per_bh) {
+    constexpr int kBatch = 8;
     const size_t bh = blockIdx.x / blocks_per_bh;
     const int xb = blockIdx.x % blocks_per_bh;
+    const float* const l2 = seg_log2 + bh * nseg;
     for (size_t e = xb * static_cast<size_t>(blockDim.x) + threadIdx.x; e < per_bh;
          e += static_cast<size_t>(blocks_per_bh) * blockDim.x) {
         float s = state_in != nullptr ? state_in[bh * per_bh + e] : 0.f;
-        for (int sg = 0; sg < nseg; ++sg) {
-            float* p = buf + (bh * nseg + sg) * per_bh + e;
-            const float t = sg + 1 < nseg ? *p : 0.f;
-            *p = s;
-            if (sg + 1 < nseg) s = exp2f(seg_log2[bh * nseg + sg]) * s + t;
+        for (int sg0 = 0; sg0 < nseg; sg0 += kBatch) {
+            float t[kBatch], f[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                t[j] = sg0 + j + 1 < nseg ? buf[(bh * nseg + sg0 + j) * per_bh + e] : 0.f;
+                f[j] = sg0 + j + 1 < nseg ? l2[sg0 + j] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int sg = sg0 + j;
+                if (sg < nseg) {
+                    buf[(bh * nseg + sg) * per_bh + e] = s;
+                    s = exp2f(f[j]) * s + t[j];
+                }
+            }
         }
     }
 }
@@ -1226,7 +1257,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         hipError_t e = launch_pre<GATED>(pre, p, stream);
         if (e != hipSuccess) return e;
         if (!p.fuse_scan) {
-            const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 64));
+            const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 256));
             ProfScope prof(kProfScan, stream);
             hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
                                stream, ka.seg_state, ka.seg_log2, a.state_in, p.nseg, per_bh, xblocks);
