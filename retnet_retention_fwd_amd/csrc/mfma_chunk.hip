@@ -451,9 +451,17 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             for (int nt = 0; nt < NT; ++nt) S[dt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (MODE == kFull) {
             if (nseg == 1 || ka.fuse_scan) {
-                if (ka.state_in != nullptr) load(ka.state_in + s_bh, 0.f, false);
-                // entry state of segment seg: S <- 2^(l2 of segment s) S + local state of s
-                for (int sg = 0; nseg > 1 && sg < seg; ++sg)
+                // entry state of segment seg: S <- 2^(l2 of segment s) S + local state of s.
+                // The first source is loaded straight into the accumulators (all loads in
+                // flight together; the adding form needs temporaries and goes slower).
+                int sg0 = 0;
+                if (ka.state_in != nullptr) {
+                    load(ka.state_in + s_bh, 0.f, false);
+                } else if (seg > 0) {
+                    load(ka.seg_state + static_cast<size_t>(bh) * nseg * s_stride_seg, 0.f, false);
+                    sg0 = 1;
+                }
+                for (int sg = sg0; nseg > 1 && sg < seg; ++sg)
                     load(ka.seg_state + (static_cast<size_t>(bh) * nseg + sg) * s_stride_seg,
                          exp2f(ka.seg_log2[static_cast<size_t>(bh) * nseg + sg]), true);
             } else {
