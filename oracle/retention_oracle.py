@@ -41,6 +41,12 @@ design notes):
 * An optional initial state S0 is decayed like any state at the first step.
 * No key scaling and no normalisation inside the operator.
 * d_k may differ from d_v; S has shape d_k x d_v.
+* Backward: the pages name a backward recurrence for the chunked kernels and check its
+  gradients against a naive loop ("unilm RetNet 技术指南", section Triton 内核与自校验
+  测试) but print no formula.  The oracle applies the chain rule to the recurrence of
+  record (the adjoint recurrence below); the tests pin it to central finite
+  differences of the forward oracle.  The loss whose gradients are returned is
+  L = <dO, o> + <dS, S_N>.
 """
 from __future__ import annotations
 
@@ -55,6 +61,8 @@ __all__ = [
     "gated_retention_chunkwise",
     "retention_decode_step",
     "gated_retention_decode_step",
+    "retention_recurrent_bwd",
+    "gated_retention_recurrent_bwd",
 ]
 
 
@@ -267,3 +275,97 @@ def gated_retention_chunkwise(q, k, v, g, chunk, state_in=None):
     q, k, v = _check_qkv(q, k, v)
     g = _f64(g)
     return _chunkwise(q, k, v, lambda a, b: _weights_gated(g, a, b), int(chunk), state_in)
+
+
+# ---------------------------------------------------------------------------------
+# Backward of the recurrent form: the chain rule applied to the recurrence of record.
+# ---------------------------------------------------------------------------------
+
+def _recurrence_bwd(q, k, v, lam, state_in, do, dstate, want_dlam, ckpt=64):
+    """Gradients of L = <dO, o> + <dS, S_{N-1}> for S_n = lam_n S_{n-1} + k_n^T v_n,
+    o_n = q_n S_n, S_{-1} = S0 ("RetNet retention mechanism" tutorial, section 递归推理).
+
+    The adjoint U_n = dL/dS_n collects every later use of S_n:
+        U_{N-1} = q_{N-1}^T dO_{N-1} + dS,     U_n = q_n^T dO_n + lam_{n+1} U_{n+1},
+    and then  dq_n = S_n dO_n,  dk_n = U_n v_n,  dv_n = U_n^T k_n,  dS0 = lam_0 U_0,
+    dlam_n = <U_n, S_{n-1}>.  The forward sweep yields dq and keeps every ckpt-th state;
+    when dlam is wanted the backward sweep recomputes each block's states from its
+    checkpoint.  Returns (dq, dk, dv, dS0, dlam or None).
+    """
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    S = _initial_state(state_in, B, H, dk, dv)
+    dq = np.zeros((B, H, N, dk), dtype=np.float64)
+    ckpts = {}
+    for n in range(N):
+        if want_dlam and n % ckpt == 0:
+            ckpts[n] = S.copy()                      # S_{n-1}
+        S *= lam[:, :, n, None, None]
+        S += k[:, :, n, :, None] * v[:, :, n, None, :]
+        dq[:, :, n, :] = np.einsum("bhij,bhj->bhi", S, do[:, :, n, :])
+    dkk = np.zeros((B, H, N, dk), dtype=np.float64)
+    dvv = np.zeros((B, H, N, dv), dtype=np.float64)
+    dlam = np.zeros((B, H, N), dtype=np.float64) if want_dlam else None
+    U = np.zeros((B, H, dk, dv), dtype=np.float64) if dstate is None else _f64(dstate).copy()
+    prev = {}
+    for n in range(N - 1, -1, -1):
+        if want_dlam and (n + 1) % ckpt == 0 or (want_dlam and n == N - 1):
+            # states S_{m-1} for m in this checkpoint block, recomputed from its start
+            c0 = (n // ckpt) * ckpt
+            Sb = ckpts[c0].copy()
+            prev = {}
+            for m in range(c0, n + 1):
+                prev[m] = Sb.copy()
+                Sb *= lam[:, :, m, None, None]
+                Sb += k[:, :, m, :, None] * v[:, :, m, None, :]
+        U += q[:, :, n, :, None] * do[:, :, n, None, :]          # U_n
+        dkk[:, :, n, :] = np.einsum("bhij,bhj->bhi", U, v[:, :, n, :])
+        dvv[:, :, n, :] = np.einsum("bhij,bhi->bhj", U, k[:, :, n, :])
+        if want_dlam:
+            dlam[:, :, n] = np.einsum("bhij,bhij->bh", U, prev[n])
+        U *= lam[:, :, n, None, None]                             # lam_n U_n, toward U_{n-1}
+    return dq, dkk, dvv, U, dlam
+
+
+def _check_bwd(q, do, dstate, B, H, N, dk, dv):
+    do = _f64(do)
+    if do.shape != (B, H, N, dv):
+        raise ValueError(f"do must be [B,H,N,dv]={B,H,N,dv}; got {do.shape}")
+    if dstate is not None and _f64(dstate).shape != (B, H, dk, dv):
+        raise ValueError(f"dstate must be [B,H,dk,dv]={B,H,dk,dv}")
+    return do
+
+
+def retention_recurrent_bwd(q, k, v, gamma, do, state_in=None, dstate=None):
+    """Backward of retention_recurrent for L = <do, o> + <dstate, state_out>.
+
+    Returns (dq, dk, dv, dstate_in) in float64; dstate_in = gamma U_0 is the gradient
+    with respect to state_in (zeros when no state was given, as for a zero state).
+    """
+    q, k, v = _check_qkv(q, k, v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    do = _check_bwd(q, do, dstate, B, H, N, dk, dv)
+    gamma = _f64(gamma).reshape(H)
+    lam = np.broadcast_to(gamma[None, :, None], (B, H, N))
+    dq, dkk, dvv, dS0, _ = _recurrence_bwd(q, k, v, lam, state_in, do, dstate, False)
+    if N == 0 and dstate is not None:
+        dS0 = _f64(dstate).copy()
+    return dq, dkk, dvv, dS0
+
+
+def gated_retention_recurrent_bwd(q, k, v, g, do, state_in=None, dstate=None):
+    """Backward of gated_retention_recurrent: returns (dq, dk, dv, dg, dstate_in), with
+    dg_n = exp(g_n) <U_n, S_{n-1}> (the multiplier is exp(g_n))."""
+    q, k, v = _check_qkv(q, k, v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    do = _check_bwd(q, do, dstate, B, H, N, dk, dv)
+    g = _f64(g)
+    if g.shape != (B, H, N):
+        raise ValueError(f"g must be [B,H,N]={B,H,N}; got {g.shape}")
+    lam = np.exp(g)
+    dq, dkk, dvv, dS0, dlam = _recurrence_bwd(q, k, v, lam, state_in, do, dstate, True)
+    if N == 0 and dstate is not None:
+        dS0 = _f64(dstate).copy()
+    return dq, dkk, dvv, lam * dlam, dS0

@@ -230,8 +230,68 @@ def pin_N1(mod):
     assert _rel(o[0, 0, 0], exp) < 1e-15
 
 
+def _loss(mod, gated, q, k, v, dec, S0, do, dS):
+    """L = <do, o> + <dS, S_N>, through the forward oracle."""
+    f = mod.gated_retention_recurrent if gated else mod.retention_recurrent
+    o, S = f(q, k, v, dec, S0)
+    return float(np.sum(do * o) + np.sum(dS * S))
+
+
+def pin_bwd_finite_difference(mod):
+    """Backward pinned to central differences of the forward oracle (brute force on tiny
+    inputs): every element of q, k, v, the initial state and, gated, g."""
+    rng = np.random.default_rng(11)
+    B, H, N, dk, dv = 1, 2, 6, 3, 2
+    q, k = rng.standard_normal((2, B, H, N, dk))
+    v, do = rng.standard_normal((2, B, H, N, dv))
+    S0, dS = rng.standard_normal((2, B, H, dk, dv))
+    h = 1e-6
+    for gated in (False, True):
+        dec = -0.4 * np.abs(rng.standard_normal((B, H, N))) if gated else np.array([0.8, 0.55])
+        if gated:
+            dq, dk_, dv_, dg, dS0 = mod.gated_retention_recurrent_bwd(q, k, v, dec, do, S0, dS)
+            inputs = dict(q=(q, dq), k=(k, dk_), v=(v, dv_), dec=(dec, dg), S0=(S0, dS0))
+        else:
+            dq, dk_, dv_, dS0 = mod.retention_recurrent_bwd(q, k, v, dec, do, S0, dS)
+            inputs = dict(q=(q, dq), k=(k, dk_), v=(v, dv_), S0=(S0, dS0))
+        for name, (x, grad) in inputs.items():
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                args = dict(q=q, k=k, v=v, dec=dec, S0=S0)
+                xp = x.copy(); xp[idx] += h
+                xm = x.copy(); xm[idx] -= h
+                args[name] = xp
+                lp = _loss(mod, gated, args["q"], args["k"], args["v"], args["dec"], args["S0"], do, dS)
+                args[name] = xm
+                lm = _loss(mod, gated, args["q"], args["k"], args["v"], args["dec"], args["S0"], do, dS)
+                fd[idx] = (lp - lm) / (2 * h)
+            assert _rel(grad, fd) < 1e-6, (gated, name, _rel(grad, fd))
+
+
+def pin_bwd_N1(mod):
+    """One token, by hand: S = lam S0 + k^T v, o = q S, U = q^T dO + dS;
+    dq = S dO, dk = U v, dv = U^T k, dS0 = lam U, dg = lam <U, S0>."""
+    rng = np.random.default_rng(12)
+    q, k = rng.standard_normal((2, 1, 1, 1, 3))
+    v, do = rng.standard_normal((2, 1, 1, 1, 2))
+    S0, dS = rng.standard_normal((2, 1, 1, 3, 2))
+    lam = 0.6
+    S = lam * S0[0, 0] + np.outer(k[0, 0, 0], v[0, 0, 0])
+    U = np.outer(q[0, 0, 0], do[0, 0, 0]) + dS[0, 0]
+    exp = dict(dq=S @ do[0, 0, 0], dk=U @ v[0, 0, 0], dv=U.T @ k[0, 0, 0], dS0=lam * U,
+               dg=lam * np.sum(U * S0[0, 0]))
+    dq, dk_, dv_, dS0 = mod.retention_recurrent_bwd(q, k, v, np.array([lam]), do, S0, dS)
+    got = dict(dq=dq[0, 0, 0], dk=dk_[0, 0, 0], dv=dv_[0, 0, 0], dS0=dS0[0, 0])
+    gq, gk, gv, gg, gS0 = mod.gated_retention_recurrent_bwd(q, k, v, np.log([[[lam]]]), do, S0, dS)
+    for name in got:
+        assert _rel(got[name], exp[name]) < 1e-14, name
+    for name, val in dict(dq=gq[0, 0, 0], dk=gk[0, 0, 0], dv=gv[0, 0, 0], dS0=gS0[0, 0], dg=gg[0, 0, 0]).items():
+        assert _rel(val, exp[name]) < 1e-14, ("gated", name)
+
+
 ALL_PINS = [pin_golden, pin_exact_rational, pin_gated_exact, pin_closed_form_all_ones,
-            pin_gamma_one_linear_attention, pin_decay_matrix, pin_N1]
+            pin_gamma_one_linear_attention, pin_decay_matrix, pin_N1,
+            pin_bwd_finite_difference, pin_bwd_N1]
 
 
 # ------------------------------------------------------------------------- the tests
@@ -413,6 +473,25 @@ MUTANTS = {
     "chunk_no_zeta": [("\"bhld,bhlv->bhdv\", Kc, Vc * zeta[..., None])", "\"bhld,bhlv->bhdv\", Kc, Vc)")],
     # chunkwise: state carried without the chunk decay
     "chunk_no_carry_decay": [("        S = Gam[:, :, -1, None, None] * S + ", "        S = S + ")],
+    # backward: adjoint state not decayed between tokens
+    "bwd_no_adjoint_decay": [("        U *= lam[:, :, n, None, None]                             # lam_n U_n, toward U_{n-1}\n", "")],
+    # backward: dq from the state before the token's update
+    "bwd_dq_old_state": [(
+        "        S *= lam[:, :, n, None, None]\n        S += k[:, :, n, :, None] * v[:, :, n, None, :]\n"
+        "        dq[:, :, n, :] = np.einsum(\"bhij,bhj->bhi\", S, do[:, :, n, :])\n",
+        "        dq[:, :, n, :] = np.einsum(\"bhij,bhj->bhi\", S, do[:, :, n, :])\n"
+        "        S *= lam[:, :, n, None, None]\n        S += k[:, :, n, :, None] * v[:, :, n, None, :]\n")],
+    # backward: dv contracted with q instead of k
+    "bwd_dv_uses_q": [("dvv[:, :, n, :] = np.einsum(\"bhij,bhi->bhj\", U, k[:, :, n, :])",
+                       "dvv[:, :, n, :] = np.einsum(\"bhij,bhi->bhj\", U, q[:, :, n, :])")],
+    # backward: gate gradient against S_n instead of S_{n-1}
+    "bwd_dlam_new_state": [("                prev[m] = Sb.copy()\n                Sb *= lam[:, :, m, None, None]\n"
+                            "                Sb += k[:, :, m, :, None] * v[:, :, m, None, :]\n",
+                            "                Sb *= lam[:, :, m, None, None]\n"
+                            "                Sb += k[:, :, m, :, None] * v[:, :, m, None, :]\n                prev[m] = Sb.copy()\n")],
+    # backward: final-state gradient ignored
+    "bwd_no_dstate": [("    U = np.zeros((B, H, dk, dv), dtype=np.float64) if dstate is None else _f64(dstate).copy()",
+                       "    U = np.zeros((B, H, dk, dv), dtype=np.float64)")],
 }
 
 
@@ -432,3 +511,66 @@ def test_unmutated_copy_passes_all_pins():
     mod = _mutant([])
     for pin in ALL_PINS:
         pin(mod)
+
+
+# ------------------------------------------------------------------ backward structure
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_bwd_checkpoint_blocks(gated):
+    """The gate gradient's recomputation from checkpoints does not depend on the block."""
+    rng = np.random.default_rng(21)
+    B, H, N, dk, dv = 1, 2, 23, 4, 3
+    q, k = rng.standard_normal((2, B, H, N, dk))
+    v, do = rng.standard_normal((2, B, H, N, dv))
+    lam = np.exp(-0.3 * np.abs(rng.standard_normal((B, H, N))))
+    ref = RO._recurrence_bwd(q, k, v, lam, None, do, None, True, ckpt=64)
+    for c in (1, 3, 7, 23):
+        got = RO._recurrence_bwd(q, k, v, lam, None, do, None, True, ckpt=c)
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
+
+
+def _flip(x):
+    return np.ascontiguousarray(x[:, :, ::-1])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_bwd_as_forward_passes(gated):
+    """The identities the GPU backward is built on, checked on the oracle alone:
+    dq is a forward pass with (q, k, v) -> (do, v, k) and initial state S0^T; dv and dk
+    are forward passes over the time-reversed sequence, (k, q, do) and (v, do, q), whose
+    initial state is dS (scaled by 1/gamma, or with a reversed gate shifted by one
+    whose first entry is 0), and dS0 is gamma (or exp(g_0)) times the state the dv pass
+    ends with; gated, dg is the reversed cumulative sum of q.dq - k.dk plus <dS, S_N>."""
+    rng = np.random.default_rng(22)
+    B, H, N, dk, dv = 2, 2, 37, 5, 4
+    q, k = rng.standard_normal((2, B, H, N, dk))
+    v, do = rng.standard_normal((2, B, H, N, dv))
+    S0, dS = rng.standard_normal((2, B, H, dk, dv))
+    T = lambda S: np.ascontiguousarray(np.swapaxes(S, -1, -2))  # noqa: E731
+    if gated:
+        g = -0.3 * np.abs(rng.standard_normal((B, H, N)))
+        dq, dk_, dv_, dg, dS0 = oracle.gated_retention_recurrent_bwd(q, k, v, g, do, S0, dS)
+        gr = np.concatenate([np.zeros((B, H, 1)), g[:, :, :0:-1]], axis=-1)
+        fq, S_fin_t = oracle.gated_retention_recurrent(do, v, k, g, T(S0))
+        fv, U0 = oracle.gated_retention_recurrent(_flip(k), _flip(q), _flip(do), gr, dS)
+        fk, _ = oracle.gated_retention_recurrent(_flip(v), _flip(do), _flip(q), gr, T(dS))
+        lam0 = np.exp(g[:, :, 0])[..., None, None]
+    else:
+        gm = np.array([0.9, 0.45])
+        dq, dk_, dv_, dS0 = oracle.retention_recurrent_bwd(q, k, v, gm, do, S0, dS)
+        sc = (1.0 / gm)[None, :, None, None]
+        fq, S_fin_t = oracle.retention_recurrent(do, v, k, gm, T(S0))
+        fv, U0 = oracle.retention_recurrent(_flip(k), _flip(q), _flip(do), gm, dS * sc)
+        fk, _ = oracle.retention_recurrent(_flip(v), _flip(do), _flip(q), gm, T(dS * sc))
+        lam0 = gm[None, :, None, None]
+    assert _rel(fq, dq) < 1e-12
+    assert _rel(_flip(fv), dv_) < 1e-12
+    assert _rel(_flip(fk), dk_) < 1e-12
+    assert _rel(lam0 * U0, dS0) < 1e-12
+    if gated:
+        _, S_fin = oracle.gated_retention_recurrent(q, k, v, g, S0)
+        assert _rel(T(S_fin_t), S_fin) < 1e-12
+        dG = np.sum(q * dq, -1) - np.sum(k * dk_, -1)
+        dG[:, :, -1] += np.sum(dS * S_fin, axis=(-1, -2))
+        assert _rel(np.cumsum(dG[:, :, ::-1], -1)[:, :, ::-1], dg) < 1e-10
