@@ -137,6 +137,57 @@ retn_status gated_retention_decode_step(const void* q, const void* k, const void
                                         retn_dtype dtype, void* stream);
 
 /*
+ * Backward of retention_chunkwise_fwd: the gradients of
+ *     L = <grad_o, o> + <grad_state_out, state_out>
+ * with respect to q, k, v and state_in, for the recurrence S_n = gamma S_{n-1} + k_n^T v_n,
+ * o_n = q_n S_n (tutorial, section 递归推理; the chain rule on that recurrence, which the
+ * pwwt.cn guide, section Triton 内核与自校验测试, runs as a backward recurrence).
+ *   q, k, v, gamma, state_in   the forward call's inputs (state_in NULL = zeros)
+ *   grad_o          [B,H,N,dv], element type `dtype`
+ *   grad_state_out  optional [B,H,dk,dv] fp32 (NULL = zeros)
+ *   grad_q, grad_k  [B,H,N,dk] and grad_v [B,H,N,dv], element type `dtype`
+ *   grad_state_in   optional [B,H,dk,dv] fp32 (NULL = not written)
+ *   chunk           chunk size of the passes (changes rounding only)
+ *   workspace       16-byte aligned scratch of at least retention_bwd_workspace_bytes(...)
+ *                   bytes; contents need not be initialised
+ * Outputs must not overlap any input or each other (RETN_ERR_ALIAS).  Computed as
+ * forward passes of the chunkwise kernels: grad_q is a forward pass over (grad_o, v, k),
+ * grad_v and grad_k are forward passes over the time-reversed (k, q, grad_o) and
+ * (v, grad_o, q).  Shapes as the forward; for dv > 256 (bf16 only) dv must be a multiple
+ * of 64 and the tensors 16-byte aligned, else RETN_ERR_UNSUPPORTED.
+ */
+retn_status retention_chunkwise_bwd(const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* state_in,
+                                    const void* grad_o, const float* grad_state_out,
+                                    void* grad_q, void* grad_k, void* grad_v,
+                                    float* grad_state_in,
+                                    int B, int H, int N, int dk, int dv, int chunk,
+                                    retn_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of gated_retention_chunkwise_fwd; additionally writes grad_g [B,H,N] fp32,
+ * the gradient with respect to the log-decays g (required).  Other arguments as
+ * retention_chunkwise_bwd.
+ */
+retn_status gated_retention_chunkwise_bwd(const void* q, const void* k, const void* v,
+                                          const float* g, const float* state_in,
+                                          const void* grad_o, const float* grad_state_out,
+                                          void* grad_q, void* grad_k, void* grad_v,
+                                          float* grad_g, float* grad_state_in,
+                                          int B, int H, int N, int dk, int dv, int chunk,
+                                          retn_dtype dtype, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace the backward entry points need for these sizes (sized for an
+ * initial state and a final-state gradient being given); 0 for invalid or unsupported
+ * sizes, which the entry point then reports.
+ */
+size_t retention_bwd_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk,
+                                     retn_dtype dtype, int gated);
+
+/*
  * Bytes of workspace the chunkwise entry points need for these sizes (0 when the
  * sequence is not split across workgroups).  gated: 0 = per-head gamma, 1 = gated.
  * Returns 0 for invalid sizes as well; the entry point then reports the error.

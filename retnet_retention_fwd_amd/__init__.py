@@ -1,4 +1,4 @@
-"""MI355X-native retention operator: chunkwise forward, decode step, gated forward.
+"""MI355X-native retention operator: chunkwise forward and backward, decode step, gated variants.
 
 The operator runs in libretention_fwd.so (hand-written HIP kernels for gfx950) behind
 the C ABI in include/retention.h; this package is its Python binding.  Importing the
@@ -6,11 +6,14 @@ package does not load the library; the first call does, and raises if it is miss
 """
 from ._lib import (  # noqa: F401
     RetentionError,
+    bwd_workspace_bytes,
+    gated_retention_chunkwise_bwd,
     gated_retention_chunkwise_fwd,
     gated_retention_decode_step,
     lib,
     profile_enable,
     profile_read,
+    retention_chunkwise_bwd,
     retention_chunkwise_fwd,
     retention_decode_step,
     workspace_bytes,
@@ -18,6 +21,9 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "retention_chunkwise_fwd",
+    "retention_chunkwise_bwd",
+    "gated_retention_chunkwise_bwd",
+    "bwd_workspace_bytes",
     "gated_retention_chunkwise_fwd",
     "retention_decode_step",
     "gated_retention_decode_step",

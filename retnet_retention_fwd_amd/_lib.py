@@ -32,6 +32,9 @@ EXPORTED = (
     "retention_abi_version",
     "retention_profile_enable",
     "retention_profile_read",
+    "retention_chunkwise_bwd",
+    "gated_retention_chunkwise_bwd",
+    "retention_bwd_workspace_bytes",
 )
 
 # Kernel kinds reported by retention_profile_read.
@@ -78,6 +81,12 @@ def lib() -> ctypes.CDLL:
     L.retention_profile_enable.restype = ctypes.c_int
     L.retention_profile_read.argtypes = [_vp, _vp, _i, _vp]
     L.retention_profile_read.restype = ctypes.c_int
+    L.retention_chunkwise_bwd.argtypes = [_vp] * 11 + [_i] * 7 + [_vp, _sz, _vp]
+    L.retention_chunkwise_bwd.restype = ctypes.c_int
+    L.gated_retention_chunkwise_bwd.argtypes = [_vp] * 12 + [_i] * 7 + [_vp, _sz, _vp]
+    L.gated_retention_chunkwise_bwd.restype = ctypes.c_int
+    L.retention_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    L.retention_bwd_workspace_bytes.restype = _sz
     _lib = L
     return L
 
@@ -194,6 +203,77 @@ def gated_retention_chunkwise_fwd(q, k, v, g, chunk, state_in=None, return_state
     """Gated chunkwise retention forward with per-token log-decays g[B,H,N] (fp32, <= 0)."""
     return _chunk_call("gated_retention_chunkwise_fwd", q, k, v, g, chunk, state_in, return_state, out,
                        state_out, stream, workspace, True)
+
+
+def bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:
+    return int(lib().retention_bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, 1 if gated else 0))
+
+
+def _bwd_call(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
+              workspace, gated):
+    torch = _torch()
+    L = lib()
+    _require(q, "q")
+    dev = q.device
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(grad_o, "grad_o", q.dtype, dev)
+    _require(decay, "g" if gated else "gamma", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"expected q,k [B,H,N,dk] and v [B,H,N,dv]; got {tuple(q.shape)} "
+                         f"{tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(grad_o.shape) != (B, H, N, dv):
+        raise ValueError("grad_o must be [B,H,N,dv]")
+    exp_decay = (B, H, N) if gated else (H,)
+    if tuple(decay.shape) != exp_decay:
+        raise ValueError(f"decay must have shape {exp_decay}, got {tuple(decay.shape)}")
+    for name, t in (("state_in", state_in), ("grad_state_out", grad_state_out)):
+        if t is not None:
+            _require(t, name, torch.float32, dev)
+            if tuple(t.shape) != (B, H, dk, dv):
+                raise ValueError(f"{name} must be [B,H,dk,dv]")
+    gq = torch.empty_like(q)
+    gk = torch.empty_like(k)
+    gv = torch.empty_like(v)
+    gg = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gated else None
+    gs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if return_grad_state_in else None
+    code = _dtype_code(q)
+    ws_need = bwd_workspace_bytes(B, H, N, dk, dv, chunk, code, gated)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gated:
+        st = L.gated_retention_chunkwise_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state_in), _ptr(grad_o),
+                                             _ptr(grad_state_out), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gg), _ptr(gs),
+                                             B, H, N, dk, dv, int(chunk), code, _ptr(workspace), ws_bytes,
+                                             _stream(stream))
+        _check(st, "gated_retention_chunkwise_bwd")
+        return (gq, gk, gv, gg, gs) if return_grad_state_in else (gq, gk, gv, gg)
+    st = L.retention_chunkwise_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state_in), _ptr(grad_o),
+                                   _ptr(grad_state_out), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gs), B, H, N, dk, dv,
+                                   int(chunk), code, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "retention_chunkwise_bwd")
+    return (gq, gk, gv, gs) if return_grad_state_in else (gq, gk, gv)
+
+
+def retention_chunkwise_bwd(q, k, v, gamma, grad_o, chunk, state_in=None, grad_state_out=None,
+                            return_grad_state_in=False, stream=None, workspace=None):
+    """Backward of retention_chunkwise_fwd for L = <grad_o, o> + <grad_state_out, state_out>.
+
+    Returns (grad_q, grad_k, grad_v), plus grad_state_in [B,H,dk,dv] fp32 when
+    return_grad_state_in is set.
+    """
+    return _bwd_call(q, k, v, gamma, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
+                     workspace, False)
+
+
+def gated_retention_chunkwise_bwd(q, k, v, g, grad_o, chunk, state_in=None, grad_state_out=None,
+                                  return_grad_state_in=False, stream=None, workspace=None):
+    """Backward of gated_retention_chunkwise_fwd: (grad_q, grad_k, grad_v, grad_g[, grad_state_in])."""
+    return _bwd_call(q, k, v, g, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
+                     workspace, True)
 
 
 def _decode_call(fn_name, q, k, v, decay, state, out, stream, gated):

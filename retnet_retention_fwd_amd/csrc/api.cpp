@@ -141,6 +141,47 @@ retn_status decode_common(const void* q, const void* k, const void* v, const flo
     return e == hipSuccess ? RETN_OK : RETN_ERR_HIP;
 }
 
+// Shared validation and dispatch of the backward entry points.
+retn_status bwd_common(const void* q, const void* k, const void* v, const float* decay, const float* state_in,
+                       const void* grad_o, const float* grad_state_out, void* grad_q, void* grad_k, void* grad_v,
+                       float* grad_state_in, float* grad_g, int B, int H, int N, int dk, int dv, int chunk,
+                       retn_dtype dt, void* workspace, size_t workspace_bytes, void* stream, bool gated) {
+    if (!valid_dtype(dt)) return RETN_ERR_DTYPE;
+    if (B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1 || chunk < 1) return RETN_ERR_SHAPE;
+    if (dk > kMaxDk || dv > kMaxDv) return RETN_ERR_UNSUPPORTED;
+    const size_t bh = static_cast<size_t>(B) * H;
+    if (bh > static_cast<size_t>(INT32_MAX)) return RETN_ERR_SHAPE;
+    const size_t tokens = bh * N;
+    if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || decay == nullptr || grad_o == nullptr ||
+                       grad_q == nullptr || grad_k == nullptr || grad_v == nullptr || (gated && grad_g == nullptr)))
+        return RETN_ERR_NULL;
+    const size_t es = elem_bytes(dt);
+    const size_t sbytes = bh * dk * dv * sizeof(float);
+    const Range in[] = {span(q, tokens * dk * es), span(k, tokens * dk * es), span(v, tokens * dv * es),
+                        span(decay, (gated ? tokens : static_cast<size_t>(H)) * sizeof(float)),
+                        span(state_in, state_in ? sbytes : 0), span(grad_o, tokens * dv * es),
+                        span(grad_state_out, grad_state_out ? sbytes : 0)};
+    const Range out[] = {span(grad_q, tokens * dk * es), span(grad_k, tokens * dk * es),
+                         span(grad_v, tokens * dv * es), span(grad_state_in, grad_state_in ? sbytes : 0),
+                         span(grad_g, gated && grad_g ? tokens * sizeof(float) : 0)};
+    for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+        for (const Range& r : in)
+            if (overlaps(out[i], r)) return RETN_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(out) / sizeof(out[0]); ++j)
+            if (overlaps(out[i], out[j])) return RETN_ERR_ALIAS;
+    }
+    const retn::BwdShape sh{B, H, N, dk, dv, effective_chunk(N, chunk), dt == RETN_BF16, gated,
+                            state_in != nullptr, grad_state_out != nullptr};
+    const retn::BwdPtrs x{q, k, v, decay, state_in, grad_o, grad_state_out, grad_q, grad_k, grad_v,
+                          grad_state_in, grad_g};
+    const retn::BwdPlan plan = retn::bwd_plan(sh, &x);
+    if (!plan.ok) return RETN_ERR_UNSUPPORTED;
+    if (plan.total > 0 && (workspace == nullptr || workspace_bytes < plan.total || !aligned16(workspace)))
+        return RETN_ERR_WORKSPACE;
+    const hipError_t e = retn::run_backward(sh, x, plan, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RETN_OK : RETN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +222,35 @@ size_t retention_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk,
         dk > kMaxDk || dv > kMaxDv)
         return 0;
     return workspace_for(B, H, N, dk, dv, chunk, dtype, gated != 0);
+}
+
+retn_status retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* gamma,
+                                    const float* state_in, const void* grad_o, const float* grad_state_out,
+                                    void* grad_q, void* grad_k, void* grad_v, float* grad_state_in, int B, int H,
+                                    int N, int dk, int dv, int chunk, retn_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, gamma, state_in, grad_o, grad_state_out, grad_q, grad_k, grad_v, grad_state_in,
+                      nullptr, B, H, N, dk, dv, chunk, dtype, workspace, workspace_bytes, stream, false);
+}
+
+retn_status gated_retention_chunkwise_bwd(const void* q, const void* k, const void* v, const float* g,
+                                          const float* state_in, const void* grad_o, const float* grad_state_out,
+                                          void* grad_q, void* grad_k, void* grad_v, float* grad_g,
+                                          float* grad_state_in, int B, int H, int N, int dk, int dv, int chunk,
+                                          retn_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+    return bwd_common(q, k, v, g, state_in, grad_o, grad_state_out, grad_q, grad_k, grad_v, grad_state_in, grad_g,
+                      B, H, N, dk, dv, chunk, dtype, workspace, workspace_bytes, stream, true);
+}
+
+size_t retention_bwd_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, retn_dtype dtype,
+                                     int gated) {
+    if (!valid_dtype(dtype) || B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1 || chunk < 1 ||
+        dk > kMaxDk || dv > kMaxDv)
+        return 0;
+    const retn::BwdShape sh{B, H, N, dk, dv, effective_chunk(N, chunk), dtype == RETN_BF16, gated != 0, true, true};
+    const retn::BwdPlan plan = retn::bwd_plan(sh, nullptr);
+    return plan.ok ? plan.total : 0;
 }
 
 const char* retention_status_string(retn_status status) {

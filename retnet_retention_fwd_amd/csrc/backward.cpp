@@ -1,0 +1,263 @@
+// Backward of the chunkwise retention forward, as forward passes of the same kernels.
+//
+// The loss is L = <dO, o> + <dS, S_N> for the recurrence S_n = lam_n S_{n-1} + k_n^T v_n,
+// o_n = q_n S_n, S_{-1} = S0 ("RetNet retention mechanism" tutorial, section 递归推理; the
+// gated multiplier lam_n = exp(g_n) as in "unilm RetNet 技术指南", section 三种计算路径与增量
+// 状态).  The chain rule gives the adjoint U_n = dL/dS_n,
+//     U_{N-1} = q_{N-1}^T dO_{N-1} + dS,   U_n = q_n^T dO_n + lam_{n+1} U_{n+1},
+// and dq_n = S_n dO_n, dk_n = U_n v_n, dv_n = U_n^T k_n, dS0 = lam_0 U_0,
+// dg_n = lam_n <U_n, S_{n-1}>.  Each of these is a retention forward pass:
+//   * dq: the forward recurrence with (q, k, v) -> (dO, v, k) and initial state S0^T
+//     (its state is S_n^T, so its outputs are dO_n S_n^T = dq_n^T, and its final state
+//     is S_N^T);
+//   * dv, dk: the adjoint recurrence run forward over the time-reversed sequence, with
+//     (q, k, v) -> (k, q, dO) for dv and (v, dO, q) for dk.  Its step m applies the decay
+//     of original token N-m: per head that is gamma again, with initial state dS/gamma;
+//     gated it is the reversed gate shifted by one, whose first entry is 0, with
+//     initial state dS.  The dv pass ends with state U_0, so dS0 = lam_0 times it;
+//   * dg (gated): dg_n = sum_{p >= n} (q_p . dq_p - k_p . dk_p) + <dS, S_N>, since the
+//     log-decay enters only through the cumulative sums G.
+// When d_v exceeds the widest score width of the kernels (256), the dq and dk passes
+// (whose scores run over d_v) are split into column slices of d_v, read in place with a
+// row stride, and their outputs summed.
+
+#include "launch.h"
+
+#include <stdint.h>
+
+namespace retn {
+
+// bandwidth kernels (bwd_kernels.hip)
+hipError_t launch_rows_combine(const void* a, const void* b, void* out, size_t bh, int N, int w, bool bf16,
+                               bool flip, hipStream_t s, bool in_f32 = false, bool out_f32 = false);
+hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts,
+                                  const float* inv_gamma, int H, hipStream_t s);
+hipError_t launch_state_scale(const float* src, float* dst, size_t bh, size_t per_bh, const float* decay, int H,
+                              int N, int mode, hipStream_t s);
+hipError_t launch_reverse_gate(const float* g, float* gr, size_t bh, int N, hipStream_t s);
+hipError_t launch_state_dot(const float* dS, const float* sfin_t, float* c, size_t bh, int dk, int dv, int parts,
+                            hipStream_t s);
+hipError_t launch_gate_grad(const void* q, const void* dq, const void* k, const void* dkk, const float* c,
+                            float* dG, float* dg, size_t bh, int N, int dk, bool bf16, bool grads_f32, bool flip_dk,
+                            hipStream_t s);
+
+namespace {
+
+constexpr int kMaxScoreWidth = 256;       // widest d_k of the forward kernels
+constexpr int kGenericMaxDk = 256;
+constexpr int kGenericMaxGatedChunk = 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Which kernel runs a forward pass of score width dkp and value width dvp.
+enum PassKind { kNone = 0, kMfma = 1, kGeneric = 2 };
+
+PassKind pass_kind(const BwdShape& s, int dkp, int dvp, bool strided, bool aligned) {
+    if (s.bf16 && mfma_chunk_supported(dkp, dvp, s.chunk, true) && aligned) return kMfma;
+    if (strided) return kNone;
+    if (dkp > kGenericMaxDk) return kNone;
+    if (s.gated && s.chunk > kGenericMaxGatedChunk) return kNone;
+    return kGeneric;
+}
+
+int split_parts(int dv) {
+    if (dv <= kMaxScoreWidth) return 1;
+    for (int w : {256, 128, 64})
+        if (dv % w == 0) return dv / w;
+    return 0;
+}
+
+}  // namespace
+
+BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
+    BwdPlan p{};
+    p.ok = false;
+    const size_t bh = static_cast<size_t>(s.B) * s.H;
+    const size_t tokens = bh * s.N;
+    const size_t es = s.bf16 ? 2 : 4;
+    p.parts = split_parts(s.dv);
+    if (p.parts == 0) return p;
+    p.w = s.dv / p.parts;
+    const bool strided = p.parts > 1;
+    // user tensors read or written by the matrix-core passes must be 16-byte aligned
+    bool aligned = true;
+    if (ptrs != nullptr) {
+        const void* const all[] = {ptrs->q, ptrs->k, ptrs->v, ptrs->dout, ptrs->dq, ptrs->dk, ptrs->dv};
+        for (const void* x : all) aligned = aligned && al16(x);
+    }
+    p.kind_q = pass_kind(s, p.w, s.dk, strided, aligned);     // dq: scores over d_v
+    p.kind_v = pass_kind(s, s.dk, s.dv, false, aligned);      // dv: scores over d_k
+    p.kind_k = pass_kind(s, p.w, s.dk, strided, aligned);     // dk: scores over d_v
+    if (p.kind_q == kNone || p.kind_v == kNone || p.kind_k == kNone) return p;
+    size_t fwd = 0;
+    if (s.N > 0 && bh > 0) {
+        if (p.kind_q == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
+        if (p.kind_v == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, s.dk, s.dv, s.chunk, s.gated).workspace_bytes);
+        if (p.kind_k == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t sbytes = bh * s.dk * s.dv * sizeof(float);
+    if (tokens == 0) {   // no passes run
+        p.ok = true;
+        return p;
+    }
+    p.off_fwd = take(fwd);
+    p.fwd_bytes = fwd;
+    p.off_qr = take(tokens * s.dk * es);
+    p.off_kr = take(tokens * s.dk * es);
+    p.off_vr = take(tokens * s.dv * es);
+    p.off_dor = take(tokens * s.dv * es);
+    p.off_dvr = take(tokens * s.dv * es);
+    p.off_dkr = take(tokens * s.dk * es);
+    p.off_part = take(p.parts > 1 ? tokens * s.dk * es : 0);
+    p.off_s0t = take(s.has_s0 ? sbytes : 0);
+    p.off_dss = take(s.has_ds && !s.gated ? sbytes : 0);
+    p.off_dst = take(s.has_ds ? sbytes : 0);
+    p.off_gr = take(s.gated ? tokens * sizeof(float) : 0);
+    p.off_sfin = take(s.gated && s.has_ds ? sbytes : 0);
+    p.off_c = take(s.gated && s.has_ds ? bh * sizeof(float) : 0);
+    p.off_dG = take(s.gated ? tokens * sizeof(float) : 0);
+    // gated bf16 on the matrix cores: dq and dk are accumulated in fp32, since the gate
+    // gradient subtracts their dot products with q and k
+    p.f32acc = s.gated && s.bf16 && p.kind_q == kMfma && p.kind_k == kMfma;
+    p.off_dqf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
+    p.off_dkf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
+    p.off_partf = take(p.f32acc && p.parts > 1 ? tokens * s.dk * sizeof(float) : 0);
+    p.total = off;
+    p.ok = true;
+    return p;
+}
+
+namespace {
+
+// One forward pass on the kernel the plan chose.
+hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
+                        const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
+                        int ldqk, int ldv, void* ws, size_t ws_bytes, hipStream_t st, bool out_f32 = false) {
+    ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
+                ws_bytes};
+    a.ldqk = ldqk;
+    a.ldv = ldv;
+    a.out_f32 = out_f32;
+    if (kind == kMfma) return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H, s.N, dkp, dvp, s.chunk, s.gated), st);
+    return launch_generic_chunk(a, st);
+}
+
+}  // namespace
+
+hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, void* workspace, hipStream_t st) {
+    const size_t bh = static_cast<size_t>(s.B) * s.H;
+    if (bh == 0) return hipSuccess;
+    const size_t sper = static_cast<size_t>(s.dk) * s.dv;
+    if (s.N == 0) {   // no tokens: S_N = S0, so dS0 = dS
+        if (x.dstate_in == nullptr) return hipSuccess;
+        return launch_copy_state(x.dstate_out, x.dstate_in, bh * sper, st);
+    }
+    char* ws = static_cast<char*>(workspace);
+    void* fws = ws + p.off_fwd;
+    void *qr = ws + p.off_qr, *kr = ws + p.off_kr, *vr = ws + p.off_vr, *dor = ws + p.off_dor;
+    void *dvr = ws + p.off_dvr, *dkr = ws + p.off_dkr, *part = ws + p.off_part;
+    float* s0t = reinterpret_cast<float*>(ws + p.off_s0t);
+    float* dss = reinterpret_cast<float*>(ws + p.off_dss);
+    float* dst = reinterpret_cast<float*>(ws + p.off_dst);
+    float* gr = reinterpret_cast<float*>(ws + p.off_gr);
+    float* sfin = reinterpret_cast<float*>(ws + p.off_sfin);
+    float* cdot = reinterpret_cast<float*>(ws + p.off_c);
+    float* dG = reinterpret_cast<float*>(ws + p.off_dG);
+    const size_t es = s.bf16 ? 2 : 4;
+    const size_t tok = static_cast<size_t>(s.N);
+    const int P = p.parts, w = p.w;
+    const bool has_s0 = x.state_in != nullptr, has_ds = x.dstate_out != nullptr;
+    const float* inv = s.gated ? nullptr : x.decay;   // per head: dS / gamma
+    hipError_t e;
+#define RETN_TRY(call)             \
+    do {                           \
+        e = (call);                \
+        if (e != hipSuccess) return e; \
+    } while (0)
+
+    // states: S0^T (dq pass), dS/gamma (dv pass), (dS/gamma)^T (dk pass)
+    if (has_s0) RETN_TRY(launch_state_transpose(x.state_in, s0t, bh, s.dk, s.dv, P, nullptr, s.H, st));
+    if (has_ds) {
+        RETN_TRY(launch_state_transpose(x.dstate_out, dst, bh, s.dk, s.dv, P, inv, s.H, st));
+        if (!s.gated) RETN_TRY(launch_state_scale(x.dstate_out, dss, bh, sper, x.decay, s.H, s.N, 1, st));
+    }
+    const float* dv_in = has_ds ? (s.gated ? x.dstate_out : dss) : nullptr;
+    const size_t spart = bh * static_cast<size_t>(w) * s.dk;   // floats per part block
+
+    const bool f32 = p.f32acc;
+    void* dqf = ws + p.off_dqf;
+    void* dkf = ws + p.off_dkf;
+    void* partf = ws + p.off_partf;
+
+    // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS)
+    void* dq_acc = f32 ? dqf : x.dq;
+    void* dq_part = f32 ? partf : part;
+    for (int pi = 0; pi < P; ++pi) {
+        const char* dop = static_cast<const char*>(x.dout) + static_cast<size_t>(pi) * w * es;
+        const char* vp = static_cast<const char*>(x.v) + static_cast<size_t>(pi) * w * es;
+        void* out = pi == 0 ? dq_acc : dq_part;
+        RETN_TRY(forward_pass(s, p.kind_q, dop, vp, x.k, x.decay, out, has_s0 ? s0t + pi * spart : nullptr,
+                              s.gated && has_ds ? sfin + pi * spart : nullptr, w, s.dk, P > 1 ? s.dv : 0,
+                              0, fws, p.fwd_bytes, st, f32));
+        if (pi > 0) RETN_TRY(launch_rows_combine(dq_acc, dq_part, dq_acc, bh, s.N, s.dk, s.bf16, false, st, f32, f32));
+    }
+    if (f32) RETN_TRY(launch_rows_combine(dqf, nullptr, x.dq, bh, s.N, s.dk, s.bf16, false, st, true, false));
+
+    // ---- time-reversed inputs and the gate of the adjoint recurrence
+    RETN_TRY(launch_rows_combine(x.q, nullptr, qr, bh, s.N, s.dk, s.bf16, true, st));
+    RETN_TRY(launch_rows_combine(x.k, nullptr, kr, bh, s.N, s.dk, s.bf16, true, st));
+    RETN_TRY(launch_rows_combine(x.v, nullptr, vr, bh, s.N, s.dv, s.bf16, true, st));
+    RETN_TRY(launch_rows_combine(x.dout, nullptr, dor, bh, s.N, s.dv, s.bf16, true, st));
+    const float* dec_r = x.decay;
+    if (s.gated) {
+        RETN_TRY(launch_reverse_gate(x.decay, gr, bh, s.N, st));
+        dec_r = gr;
+    }
+
+    // ---- dv = reversed forward(k, q, dO) from dS (/gamma); it ends with U_0
+    RETN_TRY(forward_pass(s, p.kind_v, kr, qr, dor, dec_r, dvr, dv_in, x.dstate_in, s.dk, s.dv, 0, 0, fws,
+                          p.fwd_bytes, st));
+    RETN_TRY(launch_rows_combine(dvr, nullptr, x.dv, bh, s.N, s.dv, s.bf16, true, st));
+    if (x.dstate_in != nullptr)   // dS0 = lam_0 U_0
+        RETN_TRY(launch_state_scale(x.dstate_in, x.dstate_in, bh, sper, x.decay, s.H, s.N, s.gated ? 2 : 0, st));
+
+    // ---- dk = reversed forward(v, dO, q) from (dS (/gamma))^T
+    void* dk_acc = f32 ? dkf : dkr;
+    void* dk_part = f32 ? partf : part;
+    for (int pi = 0; pi < P; ++pi) {
+        const char* vp = static_cast<const char*>(vr) + static_cast<size_t>(pi) * w * es;
+        const char* dop = static_cast<const char*>(dor) + static_cast<size_t>(pi) * w * es;
+        void* out = pi == 0 ? dk_acc : dk_part;
+        RETN_TRY(forward_pass(s, p.kind_k, vp, dop, qr, dec_r, out, has_ds ? dst + pi * spart : nullptr, nullptr,
+                              w, s.dk, P > 1 ? s.dv : 0, 0, fws, p.fwd_bytes, st, f32));
+        // (the last slice is added by the final reversal, except when dk stays in fp32)
+        if (pi > 0 && (f32 || pi + 1 < P))
+            RETN_TRY(launch_rows_combine(dk_acc, dk_part, dk_acc, bh, s.N, s.dk, s.bf16, false, st, f32, f32));
+    }
+    if (f32) RETN_TRY(launch_rows_combine(dkf, nullptr, x.dk, bh, s.N, s.dk, s.bf16, true, st, true, false));
+    else RETN_TRY(launch_rows_combine(dkr, P > 1 ? part : nullptr, x.dk, bh, s.N, s.dk, s.bf16, true, st));
+
+    // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N>
+    if (s.gated) {
+        if (has_ds) RETN_TRY(launch_state_dot(x.dstate_out, sfin, cdot, bh, s.dk, s.dv, P, st));
+        if (f32)   // fp32 dq, and dk still time-reversed
+            RETN_TRY(launch_gate_grad(x.q, dqf, x.k, dkf, has_ds ? cdot : nullptr, dG, x.dg, bh, s.N, s.dk, s.bf16,
+                                      true, true, st));
+        else
+            RETN_TRY(launch_gate_grad(x.q, x.dq, x.k, x.dk, has_ds ? cdot : nullptr, dG, x.dg, bh, s.N, s.dk, s.bf16,
+                                      false, false, st));
+    }
+#undef RETN_TRY
+    (void)tok;
+    return hipSuccess;
+}
+
+}  // namespace retn

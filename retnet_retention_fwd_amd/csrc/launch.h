@@ -22,6 +22,12 @@ struct ChunkArgs {
     bool gated;
     void* workspace;
     size_t workspace_bytes;
+    // Row strides in elements of q and k (shared) and of v; 0 = contiguous (dk, dv).
+    // Only the matrix-core path takes other strides (column slices of wider rows).
+    int ldqk = 0;
+    int ldv = 0;
+    // Matrix-core path, gated shapes: write o as fp32 instead of bf16.
+    bool out_f32 = false;
 };
 
 struct DecodeArgs {
@@ -59,6 +65,36 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream
 
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Backward of the chunkwise forward (backward.cpp): forward passes plus bandwidth kernels.
+struct BwdShape {
+    int B, H, N, dk, dv, chunk;   // chunk already clipped to N
+    bool bf16, gated;
+    bool has_s0, has_ds;          // an initial state / a final-state gradient is given
+};
+struct BwdPtrs {
+    const void *q, *k, *v;
+    const float* decay;           // gamma [H] or g [B,H,N]
+    const float* state_in;        // may be null
+    const void* dout;
+    const float* dstate_out;      // may be null
+    void *dq, *dk, *dv;
+    float* dstate_in;             // may be null
+    float* dg;                    // gated only
+};
+struct BwdPlan {
+    bool ok;                      // every forward pass has a kernel
+    int parts, w;                 // split of d_v for the passes whose scores run over d_v
+    int kind_q, kind_v, kind_k;   // kernel of each pass (1 matrix-core, 2 generic)
+    size_t fwd_bytes;             // workspace of the largest forward pass
+    bool f32acc;                  // gated bf16: the dq and dk passes write fp32 (for dg)
+    size_t off_fwd, off_qr, off_kr, off_vr, off_dor, off_dvr, off_dkr, off_part, off_s0t, off_dss, off_dst,
+        off_gr, off_sfin, off_c, off_dG, off_dqf, off_dkf, off_partf;
+    size_t total;                 // workspace bytes
+};
+// ptrs may be null (workspace query): matrix-core passes then assume aligned tensors.
+BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs);
+hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, void* workspace, hipStream_t st);
 
 // Optional per-kernel timing (HIP events around each launch, see profile.cpp).
 enum ProfKind { kProfMain = 0, kProfPre = 1, kProfScan = 2, kProfGeneric = 3, kProfDecode = 4, kProfCopy = 5,

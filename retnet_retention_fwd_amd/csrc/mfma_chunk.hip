@@ -211,7 +211,7 @@ constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64
 // current block pair, optionally (XST) a staging area for one 64-row output block, and
 // (gated) the chunk's log2 decays.  When the buffers leave no room for P (kPInK), P is
 // written into the current K buffer once every wave is done with K.
-template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW, int QS = NST, bool XST = false>
+template <int DK, int DVT, bool GATED, bool HASQ, int NST, int NW, int QS = NST, bool XST = false, int XE = 2>
 struct Lds {
     static constexpr int kQRow = DK * 2, kVRow = DVT * 2;
     static constexpr int kQTile = kBlk * kQRow, kKTile = kBlk * kQRow, kVTile = kBlk * kVRow;
@@ -222,7 +222,7 @@ struct Lds {
     static constexpr int kGd = kV + NST * kVTile;         // NST stages of decays
     static constexpr int kEnd = kGd + NST * kGdStage;
     static constexpr int kGBytes = GATED ? kMaxChunk * 4 : 0;
-    static constexpr int kXBytes = HASQ && XST ? kBlk * kVRow : 0;
+    static constexpr int kXBytes = HASQ && XST ? kBlk * DVT * XE : 0;   // XE bytes per staged element
     static constexpr bool kPInK = HASQ && kEnd + kPBytes + kXBytes + kGBytes > kLdsBytes;
     static constexpr int kPSize = HASQ && !kPInK ? kPBytes : 0;
     static constexpr int kP = kPInK ? 0 : kEnd;           // unused when kPInK
@@ -280,12 +280,12 @@ constexpr int stages_for() {
 // so that it leaves in whole 128-byte lines (one wave alone owns 32 bytes of a row).
 // Q keeps two stages when that fits; otherwise single-block chunks keep one Q stage,
 // refilled once every wave is past the scores.  Other shapes store from registers.
-template <int DK, int DVT, bool GATED, int MODE, int NW, bool ONEBLK>
+template <int DK, int DVT, bool GATED, int MODE, int NW, bool ONEBLK, bool OF32 = false>
 struct Plan {
     static constexpr int NST = stages_for<DK, DVT, GATED, MODE, NW>();
     static constexpr bool kFull2 = MODE == kFull && NST == 2;
-    using L2 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, NST, true>;
-    using L1 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, 1, true>;
+    using L2 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, NST, true, OF32 ? 4 : 2>;
+    using L1 = Lds<DK, DVT, GATED, MODE == kFull, NST, NW, 1, true, OF32 ? 4 : 2>;
     static constexpr bool kQ2 = kFull2 && !L2::kPInK && L2::kBytes <= kLdsBytes;
     static constexpr bool kQ1 = kFull2 && !kQ2 && ONEBLK && !L1::kPInK && L1::kBytes <= kLdsBytes;
     static constexpr bool kStage = kQ2 || kQ1;
@@ -325,12 +325,13 @@ struct KArgs {
     const bf16_t* k;
     const bf16_t* v;
     const float* decay;      // gamma [H] or g [B,H,N]
-    bf16_t* o;
+    void* o;                 // bf16, or fp32 for the fp32-output variant
     const float* state_in;   // [B,H,dk,dv] or null (zeros)
     float* state_out;        // [B,H,dk,dv] or null
     float* seg_state;        // workspace [B*H][nseg][dk][dv]: local, then (scanned) entry states
     float* seg_log2;         // workspace [B*H][nseg]: log2 of each segment's total decay
     int H, N, dk, dv, C;
+    int ldqk, ldv;           // row strides (elements) of q and k, and of v; o is contiguous
     int seg_tokens, nseg;    // sequence split: tokens per segment, segments per (b,h)
     int ndvt, ndkt;          // column tiles and (pre-pass) state-row tiles per (b,h)
     int total_groups;
@@ -350,18 +351,20 @@ struct KArgs {
 // The LDS footprint allows one workgroup per CU, i.e. NW/4 waves per SIMD; saying so
 // lets the compiler spend registers on keeping LDS reads in flight ahead of the matrix
 // instructions instead of minimising registers for an occupancy that cannot happen.
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void chunk_kernel(
     const KArgs ka) {
     const bf16_t* __restrict__ q = ka.q;
     const bf16_t* __restrict__ k = ka.k;
     const bf16_t* __restrict__ v = ka.v;
     const float* __restrict__ decay = ka.decay;
-    bf16_t* __restrict__ o = ka.o;
+    // output elements: bf16, or fp32 (OF32, for callers that keep full precision)
+    typedef std::conditional_t<OF32, float, bf16_t> out_t;
+    out_t* __restrict__ o = static_cast<out_t*>(ka.o);
     const int H = ka.H, N = ka.N, dv = ka.dv, C = ka.C, dk = ka.dk;
     const int seg_tokens = ka.seg_tokens, nseg = ka.nseg, ndvt = ka.ndvt, ndkt = ka.ndkt;
     const int total_groups = ka.total_groups;
-    using PL = Plan<DK, DVT, GATED, MODE, NW, ONEBLK>;
+    using PL = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>;
     constexpr int NST = PL::NST;
     using L_ = typename PL::L;
     static_assert(L_::kBytes <= kLdsBytes, "LDS layout too large");
@@ -406,21 +409,24 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const float lg = GATED ? 0.f : log2f(decay[h]);
 
     // q, k rows have dk elements; this workgroup's K tile covers dims dkt*DK .. +DK
-    const size_t qk_bh = static_cast<size_t>(bh) * N * dk;
-    const size_t v_bh = static_cast<size_t>(bh) * N * dv;
+    const int ldqk = ka.ldqk, ldv = ka.ldv;
+    const size_t qk_bh = static_cast<size_t>(bh) * N * ldqk;
+    const size_t v_bh = static_cast<size_t>(bh) * N * ldv;
+    const size_t o_bh = static_cast<size_t>(bh) * N * dv;
     const size_t s_bh = static_cast<size_t>(bh) * dk * dv;
     const size_t s_stride_seg = static_cast<size_t>(dk) * dv;
     const int srow0 = dkt * DK;                          // first state row of this tile
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
     const u32x4_t g_rs = make_rsrc(GATED ? g_bh : decay, GATED ? static_cast<uint32_t>(N) * 4 : 4);
-    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * dk * 2);
-    const u32x4_t k_rs = make_rsrc(k + qk_bh + srow0, static_cast<uint32_t>(N) * dk * 2);
-    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>(N) * dv * 2);
+    // ranges end with the last row's own columns; rows past N read as zeros
+    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + dk) * 2);
+    const u32x4_t k_rs = make_rsrc(k + qk_bh + srow0, static_cast<uint32_t>((N - 1) * ldqk + dk - srow0) * 2);
+    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>((N - 1) * ldv + dv - col0) * 2);
     const uint32_t lds0 = lds_addr_of(smem);
     TileCopy<QRB, false, NW> kcp;   // Q and K tiles (same row length and swizzle)
     TileCopy<VRB, true, NW> vcp;
-    kcp.init(dk * 2, wave, lane);
-    vcp.init(dv * 2, wave, lane);
+    kcp.init(ldqk * 2, wave, lane);
+    vcp.init(ldv * 2, wave, lane);
 
     // State accumulator element (dt, i) of lane l holds state row srow(dt, i): tiles 2s and
     // 2s+1 together cover rows 32s..32s+31, with lane group g holding rows 32s+8g..32s+8g+7
@@ -584,16 +590,16 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             dq_lds = lds0 + L_::kQ + qb_ * L_::kQTile + wofs;
             dk_lds = lds0 + L_::kK + kvb_ * L_::kKTile + wofs;
             dv_lds = lds0 + L_::kV + kvb_ * L_::kVTile + wofs;
-            dq_off = static_cast<uint32_t>(s.cs + s.qb * kBlk) * dk * 2;
-            dk_off = static_cast<uint32_t>(k0) * dk * 2;
-            dv_off = static_cast<uint32_t>(k0) * dv * 2;
+            dq_off = static_cast<uint32_t>(s.cs + s.qb * kBlk) * ldqk * 2;
+            dk_off = static_cast<uint32_t>(k0) * ldqk * 2;
+            dv_off = static_cast<uint32_t>(k0) * ldv * 2;
         } else {
             if (MODE == kFull && s.kb == 0) {
                 const int q0 = s.cs + s.qb * kBlk;
-                kcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * dk * 2, wave);
+                kcp.issue(lds0 + L_::kQ + qb_ * L_::kQTile, q_rs, static_cast<uint32_t>(q0) * ldqk * 2, wave);
             }
-            kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * dk * 2, wave);
-            vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * dv * 2, wave);
+            kcp.issue(lds0 + L_::kK + kvb_ * L_::kKTile, k_rs, static_cast<uint32_t>(k0) * ldqk * 2, wave);
+            vcp.issue(lds0 + L_::kV + kvb_ * L_::kVTile, v_rs, static_cast<uint32_t>(k0) * ldv * 2, wave);
         }
         if (GATED && MODE == kStateOnly) {
             // the pre-pass walks single blocks: every wave copies the block's 64 decays
@@ -632,21 +638,25 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const uint32_t st_lane = static_cast<uint32_t>(l16 * dv + 4 * g4);
     auto store_pending = [&]() {
         if (MODE != kFull || pend_q0 < 0) return;
-        bf16_t* const base = o + v_bh + static_cast<size_t>(pend_q0) * dv + col0 + wcol;
+        out_t* const base = o + o_bh + static_cast<size_t>(pend_q0) * dv + col0 + wcol;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (pend_nq < kBlk && mt * 16 + l16 >= pend_nq) continue;   // rows past the end
-            bf16_t* const row = base + static_cast<size_t>(mt * 16) * dv;
+            out_t* const row = base + static_cast<size_t>(mt * 16) * dv;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                *reinterpret_cast<u16x4_t*>(row + st_lane + nt * 16) = bf4(X[mt][nt]);
+            for (int nt = 0; nt < NT; ++nt) {
+                if constexpr (OF32) *reinterpret_cast<f32x4_t*>(row + st_lane + nt * 16) = X[mt][nt];
+                else *reinterpret_cast<u16x4_t*>(row + st_lane + nt * 16) = bf4(X[mt][nt]);
+            }
         }
         pend_q0 = -1;
     };
-    // Staged output: a finished block goes to LDS as bf16, row-major [64][DVT] with the
-    // 16-byte units of row r rotated by XOR with r (no bank conflicts either way); after
-    // the next step's barrier the workgroup stores it in whole rows, 16 bytes per lane.
-    constexpr int kXU = DVT / 8;                 // 16-byte units per staged row
+    // Staged output: a finished block goes to LDS in the output type, row-major [64][DVT]
+    // with the 16-byte units of row r rotated by XOR with r (no bank conflicts either
+    // way); after the next step's barrier the workgroup stores it in whole rows, 16
+    // bytes per lane.
+    constexpr int kXE = OF32 ? 4 : 2;            // bytes per output element
+    constexpr int kXU = DVT * kXE / 16;          // 16-byte units per staged row
     constexpr int kXRounds = kBlk * kXU / (NW * 64);
     static_assert(!kStage || kXRounds * NW * 64 == kBlk * kXU, "staged rows must split evenly");
     int xs_q0 = -1;                              // first row of the staged block
@@ -657,9 +667,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int row = mt * 16 + l16;
-                const int u = (wcol + nt * 16) / 8 + (g4 >> 1);
-                *reinterpret_cast<u16x4_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16 + (g4 & 1) * 8) =
-                    bf4(X[mt][nt]);
+                if constexpr (OF32) {
+                    const int u = (wcol + nt * 16) / 4 + g4;
+                    *reinterpret_cast<f32x4_t*>(xs + row * (DVT * 4) + (u ^ (row & (kXU - 1))) * 16) = X[mt][nt];
+                } else {
+                    const int u = (wcol + nt * 16) / 8 + (g4 >> 1);
+                    *reinterpret_cast<u16x4_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16 + (g4 & 1) * 8) =
+                        bf4(X[mt][nt]);
+                }
             }
     };
     // the reads right after the barrier, the stores a little later (between the first
@@ -671,16 +686,16 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         for (int r = 0; r < kXRounds; ++r) {
             const int e = r * NW * 64 + tid;
             const int row = e / kXU, u = e % kXU;
-            xv[r] = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * 2) + (u ^ (row & (kXU - 1))) * 16);
+            xv[r] = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * kXE) + (u ^ (row & (kXU - 1))) * 16);
         }
     };
     auto stage_emit = [&]() {
-        bf16_t* const base = o + v_bh + static_cast<size_t>(xs_q0) * dv + col0;
+        out_t* const base = o + o_bh + static_cast<size_t>(xs_q0) * dv + col0;
 #pragma unroll
         for (int r = 0; r < kXRounds; ++r) {
             const int e = r * NW * 64 + tid;
             const int row = e / kXU, u = e % kXU;
-            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = xv[r];
+            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * (16 / kXE))) = xv[r];
         }
         xs_q0 = -1;
     };
@@ -1201,18 +1216,18 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
     }
 }
 
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK>
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32 = false>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
-    const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK>::L::kBytes;
+    const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>::L::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
     ProfScope prof(MODE == kFull ? kProfMain : kProfPre, stream);
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK>), dim3(ka.total_groups), dim3(NW * 64), lds,
-                       stream, ka);
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32>), dim3(ka.total_groups), dim3(NW * 64),
+                       lds, stream, ka);
     return hipGetLastError();
 }
 
@@ -1237,20 +1252,22 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int DK, int DVT, int NW, bool GATED, bool ONEBLK>
+template <int DK, int DVT, int NW, bool GATED, bool ONEBLK, bool OF32 = false>
 hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     KArgs ka{};
     ka.q = static_cast<const bf16_t*>(a.q);
     ka.k = static_cast<const bf16_t*>(a.k);
     ka.v = static_cast<const bf16_t*>(a.v);
     ka.decay = a.decay;
-    ka.o = static_cast<bf16_t*>(a.o);
+    ka.o = a.o;
     ka.state_in = a.state_in;
     ka.state_out = a.state_out;
     ka.H = a.H;
     ka.N = a.N;
     ka.dk = a.dk;
     ka.dv = a.dv;
+    ka.ldqk = a.ldqk > 0 ? a.ldqk : a.dk;
+    ka.ldv = a.ldv > 0 ? a.ldv : a.dv;
     ka.C = a.chunk;
     ka.seg_tokens = p.seg_chunks * a.chunk;
     ka.nseg = p.nseg;
@@ -1276,7 +1293,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
     ka.ndkt = 1;
     ka.ndvt = a.dv / DVT;
     ka.total_groups = bh * p.nseg * ka.ndvt;
-    return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK>(ka, stream);
+    return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK, OF32>(ka, stream);
 }
 
 // State columns per workgroup and waves per workgroup for a head shape.
@@ -1328,8 +1345,13 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t 
     // the kernel handles any chunk in [1, 512], including chunks that are not a
     // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant
     const bool one = a.chunk <= kBlk;
+    // fp32 outputs: gated shapes only (the gated backward's gate gradient needs them)
+    if (a.out_f32 && !a.gated) return hipErrorInvalidValue;
 #define RETN_SHAPE(DK, DVT, NW)                                                            \
     if (a.dk == DK && p.dvt == DVT && p.nw == NW) {                                       \
+        if (a.gated && a.out_f32)                                                         \
+            return one ? launch_shape<DK, DVT, NW, true, true, true>(a, p, stream)        \
+                       : launch_shape<DK, DVT, NW, true, false, true>(a, p, stream);      \
         if (a.gated)                                                                      \
             return one ? launch_shape<DK, DVT, NW, true, true>(a, p, stream)              \
                        : launch_shape<DK, DVT, NW, true, false>(a, p, stream);            \

@@ -165,3 +165,14 @@ def random_case(seed, B, H, N, dk, dv, dtype="bf16", gated=False, state_in=False
     if state_in:
         out["state_in"] = to_dtype(rng.standard_normal((B, H, dk, dv)) * 0.1, "f32")
     return out
+
+
+def backward_grads(seed, B, H, N, dk, dv, dtype="bf16", state=False):
+    """Upstream gradients for backward tests: grad_o ~ N(0,1) [B,H,N,dv] in the workload
+    dtype, then (if state) grad_state_out ~ N(0, 0.1^2) [B,H,dk,dv] fp32.  Own generator
+    (seed), drawn in that order; returns dict name -> (torch CPU tensor, float64)."""
+    rng = np.random.default_rng(seed)
+    out = {"grad_o": to_dtype(rng.standard_normal((B, H, N, dv)), dtype)}
+    if state:
+        out["grad_state_out"] = to_dtype(rng.standard_normal((B, H, dk, dv)) * 0.1, "f32")
+    return out

@@ -107,6 +107,50 @@ def test_workspace_query(L):
     assert L.retention_workspace_bytes(-1, 2, 64, 16, 16, 16, 0, 0) == 0
 
 
+def bwd(L, gated=False, q=FAKE, k=FAKE + 64 * MB, v=FAKE + 128 * MB, d=FAKE + 192 * MB, si=None,
+        go=FAKE + 256 * MB, gso=None, gq=FAKE + 320 * MB, gk=FAKE + 384 * MB, gv=FAKE + 448 * MB,
+        gg=FAKE + 512 * MB, gsi=None, B=1, H=2, N=64, dk=16, dv=16, C=16, dt=0, ws=None, wsb=0):
+    if gated:
+        return L.gated_retention_chunkwise_bwd(q, k, v, d, si, go, gso, gq, gk, gv, gg, gsi, B, H, N, dk, dv, C, dt,
+                                               ws, wsb, None)
+    return L.retention_chunkwise_bwd(q, k, v, d, si, go, gso, gq, gk, gv, gsi, B, H, N, dk, dv, C, dt, ws, wsb,
+                                     None)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_validation(L, gated):
+    c = lambda **kw: bwd(L, gated=gated, **kw)  # noqa: E731
+    assert c(dt=9) == ERR_DTYPE
+    assert c(N=-1) == ERR_SHAPE
+    assert c(dk=300) == ERR_UNSUPPORTED
+    assert c(go=None) == ERR_NULL
+    assert c(gq=None) == ERR_NULL
+    if gated:
+        assert c(gg=None) == ERR_NULL
+    assert c(gq=FAKE + 100) == ERR_ALIAS                     # grad_q over q
+    assert c(gv=FAKE + 320 * MB) == ERR_ALIAS                # grad_v over grad_q
+    assert c(gsi=FAKE + 256 * MB) == ERR_ALIAS               # grad_state_in over grad_o
+    # fp32 with d_v above the score width of the kernels
+    assert c(dv=512) == ERR_UNSUPPORTED
+    # bf16 needs workspace for the reversed copies
+    need = L.retention_bwd_workspace_bytes(1, 2, 64, 16, 16, 16, 1, int(gated))
+    assert need > 0
+    assert c(dt=1) == ERR_WORKSPACE
+    assert c(dt=1, ws=FAKE + 600 * MB, wsb=16) == ERR_WORKSPACE
+    assert c(dt=1, ws=FAKE + 600 * MB + 4, wsb=need) == ERR_WORKSPACE   # 16-byte alignment
+    assert c(B=0) == OK                                                   # nothing to do
+
+
+def test_backward_workspace_query(L):
+    # the d_v split needs a partial-sum buffer; every size is positive for a real shape
+    a = L.retention_bwd_workspace_bytes(4, 8, 2048, 256, 512, 64, 1, 0)
+    b = L.retention_bwd_workspace_bytes(4, 8, 2048, 256, 256, 64, 1, 0)
+    assert a > b > 0
+    assert L.retention_bwd_workspace_bytes(1, 1, 64, 16, 512, 16, 0, 0) == 0   # fp32, d_v > 256
+    assert L.retention_bwd_workspace_bytes(-1, 1, 64, 16, 16, 16, 0, 0) == 0
+    assert L.retention_bwd_workspace_bytes(1, 1, 0, 16, 16, 16, 1, 1) == 0     # no tokens
+
+
 def test_profile_read_validation(L):
     assert L.retention_profile_read(None, None, -1, None) == ERR_SHAPE
     assert L.retention_profile_read(None, None, 2, None) == ERR_NULL
