@@ -14,7 +14,9 @@ over from the previous step.
 
 Secondary lines (same JSON object, "secondary"): the recurrent decode step (batch
 128, H=32, d=128, 1024 consecutive steps, GB/s of the fp32 state stream), the
-long-sequence workload at chunk 128/256/512 and the gated workload.
+long-sequence workload at chunk 128/256/512, the gated workload, and the backward
+of the train and gated workloads (with an initial state and a final-state gradient;
+GB/s counts Q, K, V, dO read and dQ, dK, dV written once).
 
 "roofline" describes the dominant kernel of the headline step, the matrix-core
 chunkwise pass (a step also runs the segment-state pre-pass): algorithmic bytes (Q, K,
@@ -140,6 +142,43 @@ def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps,
     }
 
 
+def alg_bytes_bwd(B, H, N, dk, dv, gated=False, elem=2):
+    """Backward: Q, K, V, dO read once; dQ, dK, dV written once (plus g read, dg written)."""
+    return B * H * N * ((4 * dk + 3 * dv) * elem + (8 if gated else 0))
+
+
+def run_bwd_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps, warmup, seed):
+    """Backward of a chunkwise workload with an initial state and a final-state gradient."""
+    data = chunk_inputs(torch, B, H, N, dk, dv, gated, 2, seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 100)
+    grads = [torch.randn(B, H, N, dv, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2)]
+    s0 = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.1
+    ds = torch.randn(B, H, dk, dv, device="cuda", generator=g) * 0.1
+    gm = torch.tensor(gammas, device="cuda", dtype=torch.float32) if not gated else None
+    ws = torch.empty(max(R.bwd_workspace_bytes(B, H, N, dk, dv, C, 1, gated), 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q, k, v, d, _ = data[i % 2]
+        if gated:
+            R.gated_retention_chunkwise_bwd(q, k, v, d, grads[i % 2], C, state_in=s0, grad_state_out=ds,
+                                            return_grad_state_in=True, workspace=ws)
+        else:
+            R.retention_chunkwise_bwd(q, k, v, gm, grads[i % 2], C, state_in=s0, grad_state_out=ds,
+                                      return_grad_state_in=True, workspace=ws)
+
+    t, wall = time_steps(step, steps, warmup, torch)
+    per = t / steps
+    nb = alg_bytes_bwd(B, H, N, dk, dv, gated)
+    fl = 3 * alg_flops(B, H, N, dk, dv, C)
+    return {
+        "workload": name + " backward", "B": B, "H": H, "N": N, "dk": dk, "dv": dv, "chunk": C,
+        "us_per_step": per * 1e6, "tokens_per_s": B * N / per,
+        "alg_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS,
+        "pass_TFLOPs": fl / per / 1e12, "wall_s": wall,
+    }
+
+
 def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4):
     """Recurrent decode: batch 128, H=32, d=128; S0 ~ N(0, 0.1^2) fp32; fresh bf16
     q,k,v per step (pre-generated on the GPU); gamma_h = 1 - 2^(-5 - 7h/31)."""
@@ -259,6 +298,10 @@ def main():
                                                               False, 50, 5, seed=3)
         secondary["gated_bf16"] = run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
                                                      True, 50, 5, seed=5)
+        secondary["train_bf16_backward"] = run_bwd_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h,
+                                                            False, 20, 3, seed=6)
+        secondary["gated_bf16_backward"] = run_bwd_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
+                                                            True, 20, 3, seed=7)
 
     main_us = head["kernels"]["chunk_main"]["avg_us"]
     nb = alg_bytes(4, 8, 2048, 256, 512)
