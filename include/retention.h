@@ -152,8 +152,8 @@ retn_status gated_retention_decode_step(const void* q, const void* k, const void
  *                   bytes; contents need not be initialised
  * Outputs must not overlap any input or each other (RETN_ERR_ALIAS).  Computed as
  * forward passes of the chunkwise kernels: grad_q is a forward pass over (grad_o, v, k),
- * grad_v and grad_k are forward passes over the time-reversed (k, q, grad_o) and
- * (v, grad_o, q).  Shapes as the forward; for dv > 256 (bf16 only) dv must be a multiple
+ * grad_v and grad_k are forward passes that walk (k, q, grad_o) and (v, grad_o, q) from
+ * the last token to the first, in place.  Shapes as the forward; for dv > 256 (bf16 only) dv must be a multiple
  * of 64 and the tensors 16-byte aligned, else RETN_ERR_UNSUPPORTED.
  */
 retn_status retention_chunkwise_bwd(const void* q, const void* k, const void* v,

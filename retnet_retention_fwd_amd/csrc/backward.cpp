@@ -10,11 +10,10 @@
 //   * dq: the forward recurrence with (q, k, v) -> (dO, v, k) and initial state S0^T
 //     (its state is S_n^T, so its outputs are dO_n S_n^T = dq_n^T, and its final state
 //     is S_N^T);
-//   * dv, dk: the adjoint recurrence run forward over the time-reversed sequence, with
-//     (q, k, v) -> (k, q, dO) for dv and (v, dO, q) for dk.  Its step m applies the decay
-//     of original token N-m: per head that is gamma again, with initial state dS/gamma;
-//     gated it is the reversed gate shifted by one, whose first entry is 0, with
-//     initial state dS.  The dv pass ends with state U_0, so dS0 = lam_0 times it;
+//   * dv, dk: the adjoint recurrence, a forward walk over the time-reversed sequence
+//     (the kernels' reversed mode: walk position m is token N-1-m and decays by lam of
+//     token N-m), with (q, k, v) -> (k, q, dO) for dv and (v, dO, q) for dk, starting
+//     from dS (dS^T for dk).  The dv pass ends with U_0 and writes lam_0 U_0 = dS0;
 //   * dg (gated): dg_n = sum_{p >= n} (q_p . dq_p - k_p . dk_p) + <dS, S_N>, since the
 //     log-decay enters only through the cumulative sums G.
 // When d_v exceeds the widest score width of the kernels (256), the dq and dk passes
@@ -29,17 +28,17 @@ namespace retn {
 
 // bandwidth kernels (bwd_kernels.hip)
 hipError_t launch_rows_combine(const void* a, const void* b, void* out, size_t bh, int N, int w, bool bf16,
-                               bool flip, hipStream_t s, bool in_f32 = false, bool out_f32 = false);
-hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts,
-                                  const float* inv_gamma, int H, hipStream_t s);
-hipError_t launch_state_scale(const float* src, float* dst, size_t bh, size_t per_bh, const float* decay, int H,
-                              int N, int mode, hipStream_t s);
-hipError_t launch_reverse_gate(const float* g, float* gr, size_t bh, int N, hipStream_t s);
-hipError_t launch_state_dot(const float* dS, const float* sfin_t, float* c, size_t bh, int dk, int dv, int parts,
+                               hipStream_t s, bool in_f32 = false, bool out_f32 = false);
+bool convert_dot_supported(int w, const void* g, const void* g2, const void* x, const void* out);
+hipError_t launch_convert_dot(const float* g, const float* g2, const void* x, void* out, float* dG, size_t bh, int N,
+                              int w, float sign, bool accumulate, hipStream_t s);
+hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts, hipStream_t s);
+int state_dot_splits(int dk, int dv);
+hipError_t launch_state_dot(const float* A, const float* B, float* part, size_t bh, int dk, int dv, int parts,
                             hipStream_t s);
-hipError_t launch_gate_grad(const void* q, const void* dq, const void* k, const void* dkk, const float* c,
-                            float* dG, float* dg, size_t bh, int N, int dk, bool bf16, bool grads_f32, bool flip_dk,
-                            hipStream_t s);
+hipError_t launch_gate_rows(const void* q, const void* dq, const void* k, const void* dkk, float* dG, size_t bh,
+                            int N, int dk, bool bf16, hipStream_t s);
+hipError_t launch_gate_scan(const float* dG, const float* cpart, int nc, float* dg, size_t bh, int N, hipStream_t s);
 
 namespace {
 
@@ -54,8 +53,9 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // Which kernel runs a forward pass of score width dkp and value width dvp.
 enum PassKind { kNone = 0, kMfma = 1, kGeneric = 2 };
 
-PassKind pass_kind(const BwdShape& s, int dkp, int dvp, bool strided, bool aligned) {
-    if (s.bf16 && mfma_chunk_supported(dkp, dvp, s.chunk, true) && aligned) return kMfma;
+// rev_ok: the matrix-core kernels' reversed walk (signed 32-bit row offsets) fits.
+PassKind pass_kind(const BwdShape& s, int dkp, int dvp, bool strided, bool aligned, bool rev, bool rev_ok) {
+    if (s.bf16 && mfma_chunk_supported(dkp, dvp, s.chunk, true) && aligned && (!rev || rev_ok)) return kMfma;
     if (strided) return kNone;
     if (dkp > kGenericMaxDk) return kNone;
     if (s.gated && s.chunk > kGenericMaxGatedChunk) return kNone;
@@ -87,15 +87,16 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
         const void* const all[] = {ptrs->q, ptrs->k, ptrs->v, ptrs->dout, ptrs->dq, ptrs->dk, ptrs->dv};
         for (const void* x : all) aligned = aligned && al16(x);
     }
-    p.kind_q = pass_kind(s, p.w, s.dk, strided, aligned);     // dq: scores over d_v
-    p.kind_v = pass_kind(s, s.dk, s.dv, false, aligned);      // dv: scores over d_k
-    p.kind_k = pass_kind(s, p.w, s.dk, strided, aligned);     // dk: scores over d_v
+    const bool rev_ok = (static_cast<size_t>(s.N) + 64) * std::max(s.dk, s.dv) * 2 < (static_cast<size_t>(1) << 31);
+    p.kind_q = pass_kind(s, p.w, s.dk, strided, aligned, false, rev_ok);   // dq: scores over d_v
+    p.kind_v = pass_kind(s, s.dk, s.dv, false, aligned, true, rev_ok);     // dv: scores over d_k
+    p.kind_k = pass_kind(s, p.w, s.dk, strided, aligned, true, rev_ok);    // dk: scores over d_v
     if (p.kind_q == kNone || p.kind_v == kNone || p.kind_k == kNone) return p;
     size_t fwd = 0;
     if (s.N > 0 && bh > 0) {
-        if (p.kind_q == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
+        if (p.kind_q == kMfma || p.kind_k == kMfma)
+            fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
         if (p.kind_v == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, s.dk, s.dv, s.chunk, s.gated).workspace_bytes);
-        if (p.kind_k == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
     }
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -110,23 +111,20 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
     }
     p.off_fwd = take(fwd);
     p.fwd_bytes = fwd;
-    p.off_qr = take(tokens * s.dk * es);
-    p.off_kr = take(tokens * s.dk * es);
-    p.off_vr = take(tokens * s.dv * es);
-    p.off_dor = take(tokens * s.dv * es);
-    p.off_dvr = take(tokens * s.dv * es);
-    p.off_dkr = take(tokens * s.dk * es);
     p.off_part = take(p.parts > 1 ? tokens * s.dk * es : 0);
     p.off_s0t = take(s.has_s0 ? sbytes : 0);
-    p.off_dss = take(s.has_ds && !s.gated ? sbytes : 0);
     p.off_dst = take(s.has_ds ? sbytes : 0);
-    p.off_gr = take(s.gated ? tokens * sizeof(float) : 0);
     p.off_sfin = take(s.gated && s.has_ds ? sbytes : 0);
-    p.off_c = take(s.gated && s.has_ds ? bh * sizeof(float) : 0);
+    p.dot_splits = state_dot_splits(s.dk, s.dv);
+    p.off_c = take(s.gated && s.has_ds ? bh * p.dot_splits * sizeof(float) : 0);
     p.off_dG = take(s.gated ? tokens * sizeof(float) : 0);
     // gated bf16 on the matrix cores: dq and dk are accumulated in fp32, since the gate
-    // gradient subtracts their dot products with q and k
-    p.f32acc = s.gated && s.bf16 && p.kind_q == kMfma && p.kind_k == kMfma;
+    // gradient subtracts their dot products with q and k; the dot products are taken
+    // while the fp32 values are converted to the outputs
+    p.f32acc = s.gated && s.bf16 && p.kind_q == kMfma && p.kind_k == kMfma &&
+               convert_dot_supported(s.dk, nullptr, nullptr, nullptr, nullptr);
+    if (p.f32acc && ptrs != nullptr)
+        p.f32acc = al16(ptrs->q) && al16(ptrs->k) && al16(ptrs->dq) && al16(ptrs->dk);
     p.off_dqf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
     p.off_dkf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
     p.off_partf = take(p.f32acc && p.parts > 1 ? tokens * s.dk * sizeof(float) : 0);
@@ -140,12 +138,12 @@ namespace {
 // One forward pass on the kernel the plan chose.
 hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
                         const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
-                        int ldqk, int ldv, void* ws, size_t ws_bytes, hipStream_t st, bool out_f32 = false) {
+                        int ldqk, void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32) {
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
                 ws_bytes};
     a.ldqk = ldqk;
-    a.ldv = ldv;
     a.out_f32 = out_f32;
+    a.reverse = rev;
     if (kind == kMfma) return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H, s.N, dkp, dvp, s.chunk, s.gated), st);
     return launch_generic_chunk(a, st);
 }
@@ -162,20 +160,15 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     }
     char* ws = static_cast<char*>(workspace);
     void* fws = ws + p.off_fwd;
-    void *qr = ws + p.off_qr, *kr = ws + p.off_kr, *vr = ws + p.off_vr, *dor = ws + p.off_dor;
-    void *dvr = ws + p.off_dvr, *dkr = ws + p.off_dkr, *part = ws + p.off_part;
+    void* part = ws + p.off_part;
     float* s0t = reinterpret_cast<float*>(ws + p.off_s0t);
-    float* dss = reinterpret_cast<float*>(ws + p.off_dss);
     float* dst = reinterpret_cast<float*>(ws + p.off_dst);
-    float* gr = reinterpret_cast<float*>(ws + p.off_gr);
     float* sfin = reinterpret_cast<float*>(ws + p.off_sfin);
-    float* cdot = reinterpret_cast<float*>(ws + p.off_c);
+    float* cpart = reinterpret_cast<float*>(ws + p.off_c);
     float* dG = reinterpret_cast<float*>(ws + p.off_dG);
     const size_t es = s.bf16 ? 2 : 4;
-    const size_t tok = static_cast<size_t>(s.N);
     const int P = p.parts, w = p.w;
     const bool has_s0 = x.state_in != nullptr, has_ds = x.dstate_out != nullptr;
-    const float* inv = s.gated ? nullptr : x.decay;   // per head: dS / gamma
     hipError_t e;
 #define RETN_TRY(call)             \
     do {                           \
@@ -183,80 +176,53 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
         if (e != hipSuccess) return e; \
     } while (0)
 
-    // states: S0^T (dq pass), dS/gamma (dv pass), (dS/gamma)^T (dk pass)
-    if (has_s0) RETN_TRY(launch_state_transpose(x.state_in, s0t, bh, s.dk, s.dv, P, nullptr, s.H, st));
-    if (has_ds) {
-        RETN_TRY(launch_state_transpose(x.dstate_out, dst, bh, s.dk, s.dv, P, inv, s.H, st));
-        if (!s.gated) RETN_TRY(launch_state_scale(x.dstate_out, dss, bh, sper, x.decay, s.H, s.N, 1, st));
-    }
-    const float* dv_in = has_ds ? (s.gated ? x.dstate_out : dss) : nullptr;
-    const size_t spart = bh * static_cast<size_t>(w) * s.dk;   // floats per part block
+    // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass)
+    if (has_s0) RETN_TRY(launch_state_transpose(x.state_in, s0t, bh, s.dk, s.dv, P, st));
+    if (has_ds) RETN_TRY(launch_state_transpose(x.dstate_out, dst, bh, s.dk, s.dv, P, st));
+    const size_t spart = bh * static_cast<size_t>(w) * s.dk;   // floats per slice block
 
     const bool f32 = p.f32acc;
-    void* dqf = ws + p.off_dqf;
-    void* dkf = ws + p.off_dkf;
+    float* dqf = reinterpret_cast<float*>(ws + p.off_dqf);
+    float* dkf = reinterpret_cast<float*>(ws + p.off_dkf);
     void* partf = ws + p.off_partf;
 
     // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS)
-    void* dq_acc = f32 ? dqf : x.dq;
-    void* dq_part = f32 ? partf : part;
+    void* dq_acc = f32 ? static_cast<void*>(dqf) : x.dq;
+    void* slice_out = f32 ? partf : part;
     for (int pi = 0; pi < P; ++pi) {
         const char* dop = static_cast<const char*>(x.dout) + static_cast<size_t>(pi) * w * es;
         const char* vp = static_cast<const char*>(x.v) + static_cast<size_t>(pi) * w * es;
-        void* out = pi == 0 ? dq_acc : dq_part;
-        RETN_TRY(forward_pass(s, p.kind_q, dop, vp, x.k, x.decay, out, has_s0 ? s0t + pi * spart : nullptr,
-                              s.gated && has_ds ? sfin + pi * spart : nullptr, w, s.dk, P > 1 ? s.dv : 0,
-                              0, fws, p.fwd_bytes, st, f32));
-        if (pi > 0) RETN_TRY(launch_rows_combine(dq_acc, dq_part, dq_acc, bh, s.N, s.dk, s.bf16, false, st, f32, f32));
+        RETN_TRY(forward_pass(s, p.kind_q, dop, vp, x.k, x.decay, pi == 0 ? dq_acc : slice_out,
+                              has_s0 ? s0t + pi * spart : nullptr, s.gated && has_ds ? sfin + pi * spart : nullptr, w,
+                              s.dk, P > 1 ? s.dv : 0, fws, p.fwd_bytes, st, false, f32));
+        if (pi > 0) RETN_TRY(launch_rows_combine(dq_acc, slice_out, dq_acc, bh, s.N, s.dk, s.bf16, st, f32, f32));
     }
-    if (f32) RETN_TRY(launch_rows_combine(dqf, nullptr, x.dq, bh, s.N, s.dk, s.bf16, false, st, true, false));
+    // (fp32 dq: the output, and q . dq for the gate gradient)
+    if (f32) RETN_TRY(launch_convert_dot(dqf, nullptr, x.q, x.dq, dG, bh, s.N, s.dk, 1.f, false, st));
 
-    // ---- time-reversed inputs and the gate of the adjoint recurrence
-    RETN_TRY(launch_rows_combine(x.q, nullptr, qr, bh, s.N, s.dk, s.bf16, true, st));
-    RETN_TRY(launch_rows_combine(x.k, nullptr, kr, bh, s.N, s.dk, s.bf16, true, st));
-    RETN_TRY(launch_rows_combine(x.v, nullptr, vr, bh, s.N, s.dv, s.bf16, true, st));
-    RETN_TRY(launch_rows_combine(x.dout, nullptr, dor, bh, s.N, s.dv, s.bf16, true, st));
-    const float* dec_r = x.decay;
-    if (s.gated) {
-        RETN_TRY(launch_reverse_gate(x.decay, gr, bh, s.N, st));
-        dec_r = gr;
-    }
+    // ---- dv = reversed forward(k, q, dO) from dS; it ends with dS0 = lam_0 U_0
+    RETN_TRY(forward_pass(s, p.kind_v, x.k, x.q, x.dout, x.decay, x.dv, x.dstate_out, x.dstate_in, s.dk, s.dv, 0,
+                          fws, p.fwd_bytes, st, true, false));
 
-    // ---- dv = reversed forward(k, q, dO) from dS (/gamma); it ends with U_0
-    RETN_TRY(forward_pass(s, p.kind_v, kr, qr, dor, dec_r, dvr, dv_in, x.dstate_in, s.dk, s.dv, 0, 0, fws,
-                          p.fwd_bytes, st));
-    RETN_TRY(launch_rows_combine(dvr, nullptr, x.dv, bh, s.N, s.dv, s.bf16, true, st));
-    if (x.dstate_in != nullptr)   // dS0 = lam_0 U_0
-        RETN_TRY(launch_state_scale(x.dstate_in, x.dstate_in, bh, sper, x.decay, s.H, s.N, s.gated ? 2 : 0, st));
-
-    // ---- dk = reversed forward(v, dO, q) from (dS (/gamma))^T
-    void* dk_acc = f32 ? dkf : dkr;
-    void* dk_part = f32 ? partf : part;
+    // ---- dk = reversed forward(v, dO, q) from dS^T
+    void* dk_acc = f32 ? static_cast<void*>(dkf) : x.dk;
     for (int pi = 0; pi < P; ++pi) {
-        const char* vp = static_cast<const char*>(vr) + static_cast<size_t>(pi) * w * es;
-        const char* dop = static_cast<const char*>(dor) + static_cast<size_t>(pi) * w * es;
-        void* out = pi == 0 ? dk_acc : dk_part;
-        RETN_TRY(forward_pass(s, p.kind_k, vp, dop, qr, dec_r, out, has_ds ? dst + pi * spart : nullptr, nullptr,
-                              w, s.dk, P > 1 ? s.dv : 0, 0, fws, p.fwd_bytes, st, f32));
-        // (the last slice is added by the final reversal, except when dk stays in fp32)
-        if (pi > 0 && (f32 || pi + 1 < P))
-            RETN_TRY(launch_rows_combine(dk_acc, dk_part, dk_acc, bh, s.N, s.dk, s.bf16, false, st, f32, f32));
+        const char* vp = static_cast<const char*>(x.v) + static_cast<size_t>(pi) * w * es;
+        const char* dop = static_cast<const char*>(x.dout) + static_cast<size_t>(pi) * w * es;
+        RETN_TRY(forward_pass(s, p.kind_k, vp, dop, x.q, x.decay, pi == 0 ? dk_acc : slice_out,
+                              has_ds ? dst + pi * spart : nullptr, nullptr, w, s.dk, P > 1 ? s.dv : 0, fws,
+                              p.fwd_bytes, st, true, f32));
+        if (pi > 0) RETN_TRY(launch_rows_combine(dk_acc, slice_out, dk_acc, bh, s.N, s.dk, s.bf16, st, f32, f32));
     }
-    if (f32) RETN_TRY(launch_rows_combine(dkf, nullptr, x.dk, bh, s.N, s.dk, s.bf16, true, st, true, false));
-    else RETN_TRY(launch_rows_combine(dkr, P > 1 ? part : nullptr, x.dk, bh, s.N, s.dk, s.bf16, true, st));
+    if (f32) RETN_TRY(launch_convert_dot(dkf, nullptr, x.k, x.dk, dG, bh, s.N, s.dk, -1.f, true, st));
 
-    // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N>
+    // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>
     if (s.gated) {
-        if (has_ds) RETN_TRY(launch_state_dot(x.dstate_out, sfin, cdot, bh, s.dk, s.dv, P, st));
-        if (f32)   // fp32 dq, and dk still time-reversed
-            RETN_TRY(launch_gate_grad(x.q, dqf, x.k, dkf, has_ds ? cdot : nullptr, dG, x.dg, bh, s.N, s.dk, s.bf16,
-                                      true, true, st));
-        else
-            RETN_TRY(launch_gate_grad(x.q, x.dq, x.k, x.dk, has_ds ? cdot : nullptr, dG, x.dg, bh, s.N, s.dk, s.bf16,
-                                      false, false, st));
+        if (!f32) RETN_TRY(launch_gate_rows(x.q, x.dq, x.k, x.dk, dG, bh, s.N, s.dk, s.bf16, st));
+        if (has_ds) RETN_TRY(launch_state_dot(dst, sfin, cpart, bh, s.dk, s.dv, P, st));
+        RETN_TRY(launch_gate_scan(dG, has_ds ? cpart : nullptr, has_ds ? p.dot_splits : 0, x.dg, bh, s.N, st));
     }
 #undef RETN_TRY
-    (void)tok;
     return hipSuccess;
 }
 

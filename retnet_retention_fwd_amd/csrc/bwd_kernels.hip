@@ -1,6 +1,6 @@
-// Bandwidth kernels around the backward pass's forward passes: time reversal and sums of
-// token rows, transposed and scaled state copies, the shifted reversed gate, and the
-// gate gradient (row dot products, then a reversed cumulative sum per (b,h)).
+// Bandwidth kernels around the backward pass's forward passes: sums and conversions of
+// token rows (with the gate gradient's row dot products folded in), transposed state
+// copies, and the gate gradient's reversed cumulative sum per (b,h).
 //
 // The backward itself is the chain rule applied to the recurrence S_n = lam_n S_{n-1} +
 // k_n^T v_n, o_n = q_n S_n ("RetNet retention mechanism" tutorial, section 递归推理); the
@@ -15,57 +15,118 @@ namespace retn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kScanThreads = 1024;
 
 unsigned grid_for(size_t work, size_t per_block) {
     const size_t g = (work + per_block - 1) / per_block;
     return static_cast<unsigned>(std::min<size_t>(std::max<size_t>(g, 1), 1u << 20));
 }
 
-// out[bh, n, :] = a[bh, s(n), :] (+ b[bh, s(n), :]) with s(n) = N-1-n when flipping,
-// converted from Tin to Tout.  Each thread moves V adjacent elements of one row (V
-// divides the row width).
-template <typename Tin, typename Tout, int V>
-__global__ __launch_bounds__(kThreads) void rows_combine_kernel(const Tin* __restrict__ a, const Tin* __restrict__ b,
-                                                              Tout* __restrict__ out, size_t rows_total, int N, int w,
-                                                              int flip) {
-    const int units = w / V;
-    const size_t total = rows_total * units;
-    for (size_t e = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; e < total;
-         e += static_cast<size_t>(gridDim.x) * kThreads) {
-        const size_t row = e / units;
-        const int u = static_cast<int>(e - row * units);
-        const size_t bh = row / N;
-        const int n = static_cast<int>(row - bh * N);
-        const size_t src = (bh * N + (flip ? N - 1 - n : n)) * static_cast<size_t>(w) + static_cast<size_t>(u) * V;
-        const size_t dst = row * static_cast<size_t>(w) + static_cast<size_t>(u) * V;
-        float x[V];
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Eight adjacent elements as fp32 (16-byte aligned addresses).
+template <typename T> struct vec8;
+template <> struct vec8<float> {
+    __device__ __forceinline__ static void load(const float* p, float (&x)[8]) {
+        const f32v4 a = *reinterpret_cast<const f32v4*>(p), b = *reinterpret_cast<const f32v4*>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    __device__ __forceinline__ static void store(float* p, const float (&x)[8]) {
+        *reinterpret_cast<f32v4*>(p) = f32v4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32v4*>(p + 4) = f32v4{x[4], x[5], x[6], x[7]};
+    }
+};
+template <> struct vec8<bf16_t> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float (&x)[8]) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int i = 0; i < V; ++i) x[i] = io<Tin>::load(a + src + i);
-        if (b != nullptr) {
-#pragma unroll
-            for (int i = 0; i < V; ++i) x[i] += io<Tin>::load(b + src + i);
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, const float (&x)[8]) {
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < V; ++i) io<Tout>::store(out + dst + i, x[i]);
+        for (int i = 0; i < 4; ++i)
+            w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+        *reinterpret_cast<uint4*>(p) = uint4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+// out[e] = a[e] (+ b[e]) over n elements, converted from Tin to Tout; VEC: eight per
+// thread (n a multiple of 8, pointers 16-byte aligned).  out may alias a or b.
+template <typename Tin, typename Tout, bool VEC>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const Tin* a, const Tin* b, Tout* out, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    if constexpr (VEC) {
+        for (size_t e = (blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x) * 8; e < n; e += stride * 8) {
+            float x[8];
+            vec8<Tin>::load(a + e, x);
+            if (b != nullptr) {
+                float y[8];
+                vec8<Tin>::load(b + e, y);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] += y[i];
+            }
+            vec8<Tout>::store(out + e, x);
+        }
+    } else {
+        for (size_t e = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; e < n; e += stride) {
+            float x = io<Tin>::load(a + e);
+            if (b != nullptr) x += io<Tin>::load(b + e);
+            io<Tout>::store(out + e, x);
+        }
     }
 }
 
-// dst[p][bh][r][c] = src[bh][c][p*w + r] * f(bh): the transposed state, split into
-// `parts` row blocks of w = dv/parts rows, each block contiguous over (b,h).
-// f = 1/gamma[h] when inv is set and gamma given, else 1.  32x32 tiles through LDS.
+// Gate gradient rows, folded into the conversion of an fp32 gradient g (+ g2) to bf16:
+// out[row] = g[row] (+ g2[row]); dG[row] = (dG[row] if accumulate) + sign * (x[row] .
+// the fp32 sum).  A row of w elements (w/8 a power of two, w <= 512) is spread over w/8
+// adjacent lanes, eight elements each; the lanes of a row share its loop trips.
+__global__ __launch_bounds__(kThreads) void convert_dot_kernel(const float* __restrict__ g, const float* __restrict__ g2,
+                                                             const bf16_t* __restrict__ x, bf16_t* __restrict__ out,
+                                                             float* __restrict__ dG, size_t rows, int w, float sign,
+                                                             int accumulate) {
+    const int lpr = w / 8;                                // lanes per row
+    const int rows_per_block = kThreads / lpr;
+    const int sub = threadIdx.x % lpr;
+    for (size_t row = blockIdx.x * static_cast<size_t>(rows_per_block) + threadIdx.x / lpr; row < rows;
+         row += static_cast<size_t>(gridDim.x) * rows_per_block) {
+        const size_t e = row * w + static_cast<size_t>(sub) * 8;
+        float v[8], xv[8];
+        vec8<float>::load(g + e, v);
+        if (g2 != nullptr) {
+            float y[8];
+            vec8<float>::load(g2 + e, y);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += y[i];
+        }
+        vec8<bf16_t>::load(x + e, xv);
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d += xv[i] * v[i];
+        vec8<bf16_t>::store(out + e, v);
+        for (int off = lpr / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
+        if (sub == 0) dG[row] = (accumulate ? dG[row] : 0.f) + sign * d;
+    }
+}
+
+// dst[p][bh][r][c] = src[bh][c][p*w + r]: the transposed state, split into `parts` row
+// blocks of w = dv/parts rows, each block contiguous over (b,h).  32x32 tiles through LDS.
 __global__ __launch_bounds__(kThreads) void state_transpose_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                                 int dk, int dv, int parts, size_t bh_total,
-                                                                 const float* __restrict__ gamma, int H) {
+                                                                 int dk, int dv, int parts, size_t bh_total) {
     __shared__ float tile[32][33];
     const int tiles_j = (dv + 31) / 32;
     const int tj = blockIdx.x % tiles_j, tc = blockIdx.x / tiles_j;
     const int w = dv / parts;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
     for (size_t bh = blockIdx.y; bh < bh_total; bh += gridDim.y) {   // block-uniform loop
-        const float f = gamma != nullptr ? 1.f / gamma[bh % H] : 1.f;
         for (int y = ty; y < 32; y += 8) {
             const int c = tc * 32 + y, j = tj * 32 + tx;
-            if (c < dk && j < dv) tile[y][tx] = src[(bh * dk + c) * dv + j] * f;
+            if (c < dk && j < dv) tile[y][tx] = src[(bh * dk + c) * dv + j];
         }
         __syncthreads();
         for (int y = ty; y < 32; y += 8) {
@@ -79,111 +140,94 @@ __global__ __launch_bounds__(kThreads) void state_transpose_kernel(const float* 
     }
 }
 
-// dst[bh] = src[bh] * f(bh), f = gamma[h] (mode 0), 1/gamma[h] (mode 1) or exp(g[bh, 0])
-// (mode 2).  In place allowed.
-__global__ __launch_bounds__(kThreads) void state_scale_kernel(const float* __restrict__ src, float* dst,
-                                                             size_t per_bh, size_t bh_total,
-                                                             const float* __restrict__ decay, int H, int N,
-                                                             int mode) {
-    const size_t total = per_bh * bh_total;
-    for (size_t e = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; e < total;
-         e += static_cast<size_t>(gridDim.x) * kThreads) {
-        const size_t bh = e / per_bh;
-        const float f = mode == 0 ? decay[bh % H] : mode == 1 ? 1.f / decay[bh % H] : expf(decay[bh * N]);
-        dst[e] = src[e] * f;
-    }
-}
-
-// gr[bh][0] = 0, gr[bh][m] = g[bh][N - m] for m >= 1: the gate of the time-reversed
-// adjoint recurrence (U_n = q_n^T dO_n + exp(g_{n+1}) U_{n+1}).
-__global__ __launch_bounds__(kThreads) void reverse_gate_kernel(const float* __restrict__ g, float* __restrict__ gr,
-                                                              size_t bh_total, int N) {
-    const size_t total = bh_total * N;
-    for (size_t e = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; e < total;
-         e += static_cast<size_t>(gridDim.x) * kThreads) {
-        const size_t bh = e / N;
-        const int m = static_cast<int>(e - bh * N);
-        gr[e] = m == 0 ? 0.f : g[bh * N + (N - m)];
-    }
-}
-
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
 
-// c[bh] = <dS[bh], S_N[bh]>, S_N given transposed in part blocks (as state_transpose).
-__global__ __launch_bounds__(kThreads) void state_dot_kernel(const float* __restrict__ dS,
-                                                           const float* __restrict__ sfin_t, float* __restrict__ c,
-                                                           int dk, int dv, int parts, size_t bh_total) {
-    __shared__ float part_sums[kThreads / 64];
-    const size_t bh = blockIdx.x;
+// Partial sums of <A[bh], B[bh]> for two states in the part-block layout of
+// state_transpose (the same layout on both sides): block (bh, s) sums its share of the
+// dk*dv products into part[bh * splits + s].
+__global__ __launch_bounds__(kThreads) void state_dot_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                           float* __restrict__ part, int dk, int dv, int parts,
+                                                           size_t bh_total, int splits) {
+    __shared__ float sums[kThreads / 64];
+    const size_t bh = blockIdx.x / splits;
+    const int sp = blockIdx.x % splits;
     const int w = dv / parts;
+    const int per_block = w * dk;                 // contiguous floats of one part block
+    const int total = dk * dv;
+    const int share = (total + splits - 1) / splits;
+    const int e0 = sp * share, e1 = min(total, e0 + share);
     float acc = 0.f;
-    for (int e = threadIdx.x; e < dk * dv; e += kThreads) {
-        const int i = e / dv, j = e - i * dv;
-        const int p = j / w, r = j - p * w;
-        acc += dS[bh * dk * dv + e] * sfin_t[((static_cast<size_t>(p) * bh_total + bh) * w + r) * dk + i];
+    for (int e = e0 + static_cast<int>(threadIdx.x); e < e1; e += kThreads) {
+        const int p = e / per_block, r = e - p * per_block;
+        const size_t i = (static_cast<size_t>(p) * bh_total + bh) * per_block + r;
+        acc += A[i] * B[i];
     }
     acc = wave_sum(acc);
-    if ((threadIdx.x & 63) == 0) part_sums[threadIdx.x >> 6] = acc;
+    if ((threadIdx.x & 63) == 0) sums[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         float t = 0.f;
-        for (int i = 0; i < kThreads / 64; ++i) t += part_sums[i];
-        c[bh] = t;
+        for (int i = 0; i < kThreads / 64; ++i) t += sums[i];
+        part[blockIdx.x] = t;
     }
 }
 
-// dG[bh][n] = q_n . dq_n - k_n . dk_n: one wave per token, lanes over the row.  q, k
-// are Tx; dq, dk are Tg; dk may be stored time-reversed (row N-1-n).
-template <typename Tx, typename Tg>
-__global__ __launch_bounds__(kThreads) void gate_rows_kernel(const Tx* __restrict__ q, const Tg* __restrict__ dq,
-                                                           const Tx* __restrict__ k, const Tg* __restrict__ dkk,
-                                                           float* __restrict__ dG, size_t rows_total, int N, int dk,
-                                                           int flip_dk) {
+// dG[bh][n] = q_n . dq_n - k_n . dk_n: one wave per token, lanes over the row (the
+// gradients in the I/O type; the matrix-core path folds this into convert_dot_kernel).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gate_rows_kernel(const T* __restrict__ q, const T* __restrict__ dq,
+                                                           const T* __restrict__ k, const T* __restrict__ dkk,
+                                                           float* __restrict__ dG, size_t rows_total, int dk) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (size_t row = blockIdx.x * static_cast<size_t>(kThreads / 64) + wave; row < rows_total;
          row += static_cast<size_t>(gridDim.x) * (kThreads / 64)) {
         const size_t base = row * dk;
-        const size_t bh = row / N;
-        const int n = static_cast<int>(row - bh * N);
-        const size_t kbase = flip_dk ? (bh * N + (N - 1 - n)) * dk : base;
         float acc = 0.f;
         for (int i = lane; i < dk; i += 64)
-            acc += io<Tx>::load(q + base + i) * io<Tg>::load(dq + base + i) -
-                   io<Tx>::load(k + base + i) * io<Tg>::load(dkk + kbase + i);
+            acc += io<T>::load(q + base + i) * io<T>::load(dq + base + i) -
+                   io<T>::load(k + base + i) * io<T>::load(dkk + base + i);
         acc = wave_sum(acc);
         if (lane == 0) dG[row] = acc;
     }
 }
 
-// dg[bh][n] = sum_{p >= n} dG[bh][p] + c[bh] (c = 0 when absent): one workgroup per
-// (b,h); each thread sums a contiguous run of tokens, the run totals are scanned in
-// LDS, then every thread writes its run.
-__global__ __launch_bounds__(kThreads) void gate_scan_kernel(const float* __restrict__ dG, const float* __restrict__ c,
-                                                           float* __restrict__ dg, int N) {
-    __shared__ float tot[kThreads];
+// dg[bh][n] = sum_{p >= n} dG[bh][p] + c[bh], c the sum of the `nc` partial dot products
+// of (b,h) (0 when nc = 0).  One workgroup per (b,h): each thread sums a contiguous run
+// of tokens; suffix sums of the run totals (within each wave by shuffles, then over the
+// waves after it) give every run its starting value.
+__global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __restrict__ dG,
+                                                               const float* __restrict__ cpart, int nc,
+                                                               float* __restrict__ dg, int N) {
+    __shared__ float wsum[kScanThreads / 64];
+    __shared__ float cval;
     const size_t bh = blockIdx.x;
     const float* src = dG + bh * N;
     float* dst = dg + bh * N;
-    const int per = (N + kThreads - 1) / kThreads;
-    const int n0 = threadIdx.x * per, n1 = min(N, n0 + per);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (N + kScanThreads - 1) / kScanThreads;
+    const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
     float s = 0.f;
     for (int n = n0; n < n1; ++n) s += src[n];
-    tot[threadIdx.x] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {   // exclusive suffix sums of the run totals
-        float run = c != nullptr ? c[bh] : 0.f;
-        for (int t = kThreads - 1; t >= 0; --t) {
-            const float x = tot[t];
-            tot[t] = run;
-            run += x;
-        }
+    float incl = s;   // sum over lanes lane..63 of this wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += y;
+    }
+    if (lane == 0) wsum[wave] = incl;
+    if (tid == 0) {
+        float c = 0.f;
+        for (int i = 0; i < nc; ++i) c += cpart[bh * nc + i];
+        cval = c;
     }
     __syncthreads();
-    float run = tot[threadIdx.x];
+    float run = cval;
+    for (int w2 = kScanThreads / 64 - 1; w2 > wave; --w2) run += wsum[w2];
+    run += incl - s;   // the lanes after this one
     for (int n = n1 - 1; n >= n0; --n) {
         run += src[n];
         dst[n] = run;
@@ -191,87 +235,88 @@ __global__ __launch_bounds__(kThreads) void gate_scan_kernel(const float* __rest
 }
 
 template <typename Tin, typename Tout>
-void combine_typed(const void* a, const void* b, void* out, size_t rows, int N, int w, bool flip, hipStream_t s) {
+void combine_typed(const void* a, const void* b, void* out, size_t n, hipStream_t s) {
     const Tin *pa = static_cast<const Tin*>(a), *pb = static_cast<const Tin*>(b);
     Tout* po = static_cast<Tout*>(out);
-    if (w % 4 == 0)
-        hipLaunchKernelGGL((rows_combine_kernel<Tin, Tout, 4>), dim3(grid_for(rows * (w / 4), kThreads)),
-                           dim3(kThreads), 0, s, pa, pb, po, rows, N, w, flip ? 1 : 0);
+    const bool vec = n % 8 == 0 && aligned16(a) && (b == nullptr || aligned16(b)) && aligned16(out);
+    if (vec)
+        hipLaunchKernelGGL((combine_kernel<Tin, Tout, true>), dim3(grid_for(n / 8, kThreads)), dim3(kThreads), 0, s,
+                           pa, pb, po, n);
     else
-        hipLaunchKernelGGL((rows_combine_kernel<Tin, Tout, 1>), dim3(grid_for(rows * w, kThreads)), dim3(kThreads), 0,
-                           s, pa, pb, po, rows, N, w, flip ? 1 : 0);
+        hipLaunchKernelGGL((combine_kernel<Tin, Tout, false>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, pa,
+                           pb, po, n);
 }
 
 }  // namespace
 
 // in_f32 / out_f32: element types of (a, b) and of out (else the I/O type: bf16 or fp32).
 hipError_t launch_rows_combine(const void* a, const void* b, void* out, size_t bh, int N, int w, bool bf16,
-                               bool flip, hipStream_t s, bool in_f32, bool out_f32) {
-    const size_t rows = bh * static_cast<size_t>(N);
-    if (rows == 0 || w == 0) return hipSuccess;
+                               hipStream_t s, bool in_f32, bool out_f32) {
+    const size_t n = bh * static_cast<size_t>(N) * w;
+    if (n == 0) return hipSuccess;
     const bool fin = in_f32 || !bf16, fout = out_f32 || !bf16;
-    if (fin && fout) combine_typed<float, float>(a, b, out, rows, N, w, flip, s);
-    else if (fin) combine_typed<float, bf16_t>(a, b, out, rows, N, w, flip, s);
-    else if (fout) combine_typed<bf16_t, float>(a, b, out, rows, N, w, flip, s);
-    else combine_typed<bf16_t, bf16_t>(a, b, out, rows, N, w, flip, s);
+    if (fin && fout) combine_typed<float, float>(a, b, out, n, s);
+    else if (fin) combine_typed<float, bf16_t>(a, b, out, n, s);
+    else if (fout) combine_typed<bf16_t, float>(a, b, out, n, s);
+    else combine_typed<bf16_t, bf16_t>(a, b, out, n, s);
     return hipGetLastError();
 }
 
-hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts,
-                                  const float* inv_gamma, int H, hipStream_t s) {
+bool convert_dot_supported(int w, const void* g, const void* g2, const void* x, const void* out) {
+    if (w % 8 != 0 || w > 512 || ((w / 8) & (w / 8 - 1)) != 0) return false;
+    return aligned16(g) && (g2 == nullptr || aligned16(g2)) && aligned16(x) && aligned16(out);
+}
+
+hipError_t launch_convert_dot(const float* g, const float* g2, const void* x, void* out, float* dG, size_t bh, int N,
+                              int w, float sign, bool accumulate, hipStream_t s) {
+    const size_t rows = bh * static_cast<size_t>(N);
+    if (rows == 0) return hipSuccess;
+    const int rows_per_block = kThreads / (w / 8);
+    hipLaunchKernelGGL(convert_dot_kernel, dim3(grid_for(rows, rows_per_block)), dim3(kThreads), 0, s, g, g2,
+                       static_cast<const bf16_t*>(x), static_cast<bf16_t*>(out), dG, rows, w, sign,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts, hipStream_t s) {
     if (bh == 0) return hipSuccess;
     const unsigned tiles = static_cast<unsigned>(((dk + 31) / 32) * ((dv + 31) / 32));
     const unsigned ys = static_cast<unsigned>(std::min<size_t>(bh, 65535));
-    hipLaunchKernelGGL(state_transpose_kernel, dim3(tiles, ys), dim3(kThreads), 0, s, src, dst, dk, dv, parts, bh,
-                       inv_gamma, H);
+    hipLaunchKernelGGL(state_transpose_kernel, dim3(tiles, ys), dim3(kThreads), 0, s, src, dst, dk, dv, parts, bh);
     return hipGetLastError();
 }
 
-hipError_t launch_state_scale(const float* src, float* dst, size_t bh, size_t per_bh, const float* decay, int H,
-                              int N, int mode, hipStream_t s) {
-    if (bh == 0 || per_bh == 0) return hipSuccess;
-    hipLaunchKernelGGL(state_scale_kernel, dim3(grid_for(bh * per_bh, kThreads)), dim3(kThreads), 0, s, src, dst,
-                       per_bh, bh, decay, H, N, mode);
-    return hipGetLastError();
-}
+int state_dot_splits(int dk, int dv) { return std::max(1, std::min(64, dk * dv / 2048)); }
 
-hipError_t launch_reverse_gate(const float* g, float* gr, size_t bh, int N, hipStream_t s) {
-    if (bh * N == 0) return hipSuccess;
-    hipLaunchKernelGGL(reverse_gate_kernel, dim3(grid_for(bh * N, kThreads)), dim3(kThreads), 0, s, g, gr, bh, N);
-    return hipGetLastError();
-}
-
-hipError_t launch_state_dot(const float* dS, const float* sfin_t, float* c, size_t bh, int dk, int dv, int parts,
+hipError_t launch_state_dot(const float* A, const float* B, float* part, size_t bh, int dk, int dv, int parts,
                             hipStream_t s) {
     if (bh == 0) return hipSuccess;
-    hipLaunchKernelGGL(state_dot_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0, s, dS, sfin_t, c, dk,
-                       dv, parts, bh);
+    const int splits = state_dot_splits(dk, dv);
+    hipLaunchKernelGGL(state_dot_kernel, dim3(static_cast<unsigned>(bh * splits)), dim3(kThreads), 0, s, A, B, part,
+                       dk, dv, parts, bh, splits);
     return hipGetLastError();
 }
 
-// grads_f32: dq and dk are fp32 (else the I/O type); flip_dk: dk stored time-reversed.
-hipError_t launch_gate_grad(const void* q, const void* dq, const void* k, const void* dkk, const float* c,
-                            float* dG, float* dg, size_t bh, int N, int dk, bool bf16, bool grads_f32, bool flip_dk,
-                            hipStream_t s) {
+hipError_t launch_gate_rows(const void* q, const void* dq, const void* k, const void* dkk, float* dG, size_t bh,
+                            int N, int dk, bool bf16, hipStream_t s) {
     const size_t rows = bh * static_cast<size_t>(N);
     if (rows == 0) return hipSuccess;
     const unsigned g1 = grid_for(rows, kThreads / 64);
-    const int fl = flip_dk ? 1 : 0;
-    if (bf16 && grads_f32)
-        hipLaunchKernelGGL((gate_rows_kernel<bf16_t, float>), dim3(g1), dim3(kThreads), 0, s,
-                           static_cast<const bf16_t*>(q), static_cast<const float*>(dq),
-                           static_cast<const bf16_t*>(k), static_cast<const float*>(dkk), dG, rows, N, dk, fl);
-    else if (bf16)
-        hipLaunchKernelGGL((gate_rows_kernel<bf16_t, bf16_t>), dim3(g1), dim3(kThreads), 0, s,
-                           static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(dq),
-                           static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(dkk), dG, rows, N, dk, fl);
+    if (bf16)
+        hipLaunchKernelGGL((gate_rows_kernel<bf16_t>), dim3(g1), dim3(kThreads), 0, s, static_cast<const bf16_t*>(q),
+                           static_cast<const bf16_t*>(dq), static_cast<const bf16_t*>(k),
+                           static_cast<const bf16_t*>(dkk), dG, rows, dk);
     else
-        hipLaunchKernelGGL((gate_rows_kernel<float, float>), dim3(g1), dim3(kThreads), 0, s,
-                           static_cast<const float*>(q), static_cast<const float*>(dq), static_cast<const float*>(k),
-                           static_cast<const float*>(dkk), dG, rows, N, dk, fl);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gate_scan_kernel, dim3(static_cast<unsigned>(bh)), dim3(kThreads), 0, s, dG, c, dg, N);
+        hipLaunchKernelGGL((gate_rows_kernel<float>), dim3(g1), dim3(kThreads), 0, s, static_cast<const float*>(q),
+                           static_cast<const float*>(dq), static_cast<const float*>(k), static_cast<const float*>(dkk),
+                           dG, rows, dk);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_scan(const float* dG, const float* cpart, int nc, float* dg, size_t bh, int N, hipStream_t s) {
+    if (bh == 0 || N == 0) return hipSuccess;
+    hipLaunchKernelGGL(gate_scan_kernel, dim3(static_cast<unsigned>(bh)), dim3(kScanThreads), 0, s, dG, cpart, nc, dg,
+                       N);
     return hipGetLastError();
 }
 

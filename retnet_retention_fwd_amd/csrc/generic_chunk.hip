@@ -12,6 +12,10 @@
 //
 // One workgroup of 256 threads owns one (b, h) and a tile of up to 64 state columns;
 // it walks the chunks in order, keeping its dk x 64 slice of S in LDS (fp32).
+// rev: the walk runs over the time-reversed sequence (the backward's adjoint
+// recurrence): walk position p is token N-1-p, with the decay of token N-p (gated:
+// g[N-p], 0 at p = 0); per head, state_in enters divided by gamma; state_out leaves
+// multiplied by the decay of token 0.
 
 #include "common.h"
 #include "launch.h"
@@ -30,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ decay,   // gamma [H] or g [B,H,N]
     T* __restrict__ o, const float* __restrict__ state_in, float* __restrict__ state_out,
-    int H, int N, int dk, int dv, int chunk) {
+    int H, int N, int dk, int dv, int chunk, int rev) {
     extern __shared__ float smem[];
     const int kpad = dk + 1;                       // padded rows: no bank conflicts on k
     float* S = smem;                               // [dk][kCols]
@@ -50,11 +54,14 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
     const size_t qk_base = static_cast<size_t>(bh) * N * dk;
     const size_t v_base = static_cast<size_t>(bh) * N * dv;
     const size_t s_base = static_cast<size_t>(bh) * dk * dv;
+    // token of walk position p
+    auto tok = [&](int p) -> size_t { return static_cast<size_t>(rev ? N - 1 - p : p); };
 
+    const float in_scale = rev && !GATED ? 1.f / decay[h] : 1.f;
     for (int e = tid; e < dk * kCols; e += kThreads) {
         const int d = e / kCols, c = e % kCols;
         float x = 0.f;
-        if (state_in != nullptr && c < ncol) x = state_in[s_base + static_cast<size_t>(d) * dv + c0 + c];
+        if (state_in != nullptr && c < ncol) x = state_in[s_base + static_cast<size_t>(d) * dv + c0 + c] * in_scale;
         S[e] = x;
     }
     const float lg = GATED ? 0.f : log2f(decay[h]);   // per-head log2(gamma)
@@ -65,11 +72,15 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
         if (GATED) {
             // chunk-local inclusive prefix sum of g (in log2 units): per-thread serial
             // runs, then a scan over the 256 run totals.
-            const float* gp = decay + static_cast<size_t>(bh) * N + cs;
+            const float* gb = decay + static_cast<size_t>(bh) * N;
             const int per = (L + kThreads - 1) / kThreads;
             const int a = tid * per, b = min(L, a + per);
             float run = 0.f;
-            for (int j = a; j < b; ++j) { run += gp[j] * kLog2e; gl[j] = run; }
+            for (int j = a; j < b; ++j) {
+                const int p = cs + j;
+                run += (rev ? (p == 0 ? 0.f : gb[N - p]) : gb[p]) * kLog2e;
+                gl[j] = run;
+            }
             red[tid] = run;
             __syncthreads();
             for (int off = 1; off < kThreads; off <<= 1) {
@@ -94,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
             const int nr = min(kQRows, L - r0);
             for (int e = tid; e < kQRows * dk; e += kThreads) {
                 const int i = e / dk, d = e % dk;
-                qb[e] = i < nr ? io<T>::load(q + qk_base + static_cast<size_t>(cs + r0 + i) * dk + d) : 0.f;
+                qb[e] = i < nr ? io<T>::load(q + qk_base + tok(cs + r0 + i) * dk + d) : 0.f;
             }
             // thread -> outputs (row i = tid/64 + 4r, column c = tid % 64)
             const int c = tid % kCols;
@@ -105,11 +116,11 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
                 __syncthreads();
                 for (int e = tid; e < kKeys * dk; e += kThreads) {
                     const int m = e / dk, d = e % dk;
-                    kb[m * kpad + d] = m < nm ? io<T>::load(k + qk_base + static_cast<size_t>(cs + m0 + m) * dk + d) : 0.f;
+                    kb[m * kpad + d] = m < nm ? io<T>::load(k + qk_base + tok(cs + m0 + m) * dk + d) : 0.f;
                 }
                 for (int e = tid; e < kKeys * kCols; e += kThreads) {
                     const int m = e / kCols, cc = e % kCols;
-                    vb[e] = (m < nm && cc < ncol) ? io<T>::load(v + v_base + static_cast<size_t>(cs + m0 + m) * dv + c0 + cc) : 0.f;
+                    vb[e] = (m < nm && cc < ncol) ? io<T>::load(v + v_base + tok(cs + m0 + m) * dv + c0 + cc) : 0.f;
                 }
                 __syncthreads();
                 // masked, decayed scores
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
                     float x = 0.f;
                     for (int d = 0; d < dk; ++d) x += qb[i * dk + d] * S[d * kCols + c];
                     const float out = acc[r] + exp2f(G(r0 + i)) * x;
-                    io<T>::store(o + v_base + static_cast<size_t>(cs + r0 + i) * dv + c0 + c, out);
+                    io<T>::store(o + v_base + tok(cs + r0 + i) * dv + c0 + c, out);
                 }
             }
             __syncthreads();
@@ -154,12 +165,12 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
             __syncthreads();
             for (int e = tid; e < kKeys * dk; e += kThreads) {
                 const int m = e / dk, d = e % dk;
-                kb[m * kpad + d] = m < nm ? io<T>::load(k + qk_base + static_cast<size_t>(cs + m0 + m) * dk + d) : 0.f;
+                kb[m * kpad + d] = m < nm ? io<T>::load(k + qk_base + tok(cs + m0 + m) * dk + d) : 0.f;
             }
             for (int e = tid; e < kKeys * kCols; e += kThreads) {
                 const int m = e / kCols, cc = e % kCols;
                 const float z = m < nm ? exp2f(Gd(L - 1, m0 + m)) : 0.f;
-                vb[e] = (m < nm && cc < ncol) ? z * io<T>::load(v + v_base + static_cast<size_t>(cs + m0 + m) * dv + c0 + cc) : 0.f;
+                vb[e] = (m < nm && cc < ncol) ? z * io<T>::load(v + v_base + tok(cs + m0 + m) * dv + c0 + cc) : 0.f;
             }
             __syncthreads();
             for (int e = tid; e < dk * kCols; e += kThreads) {
@@ -173,9 +184,10 @@ __global__ __launch_bounds__(kThreads) void generic_chunk_kernel(
     }
 
     if (state_out != nullptr) {
+        const float out_scale = !rev ? 1.f : GATED ? exp2f(decay[static_cast<size_t>(bh) * N] * kLog2e) : decay[h];
         for (int e = tid; e < dk * kCols; e += kThreads) {
             const int d = e / kCols, c = e % kCols;
-            if (c < ncol) state_out[s_base + static_cast<size_t>(d) * dv + c0 + c] = S[e];
+            if (c < ncol) state_out[s_base + static_cast<size_t>(d) * dv + c0 + c] = S[e] * out_scale;
         }
     }
 }
@@ -207,7 +219,7 @@ hipError_t launch_generic_chunk(const ChunkArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((generic_chunk_kernel<T, G>), grid, block, lds, stream,                   \
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),                   \
                        static_cast<const T*>(a.v), a.decay, static_cast<T*>(a.o), a.state_in,    \
-                       a.state_out, a.H, a.N, a.dk, a.dv, a.chunk)
+                       a.state_out, a.H, a.N, a.dk, a.dv, a.chunk, a.reverse ? 1 : 0)
     ProfScope prof(kProfGeneric, stream);
     if (a.bf16) {
         if (a.gated) { RETN_LAUNCH(bf16_t, true); } else { RETN_LAUNCH(bf16_t, false); }

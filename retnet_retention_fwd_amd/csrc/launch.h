@@ -28,6 +28,11 @@ struct ChunkArgs {
     int ldv = 0;
     // Matrix-core path, gated shapes: write o as fp32 instead of bf16.
     bool out_f32 = false;
+    // Walk the time-reversed sequence (the backward's adjoint recurrence): position m
+    // reads and writes token N-1-m and takes the decay of token N-m (gated: g[N-m], 0 at
+    // m = 0; per head: gamma, with state_in entering divided by gamma); state_out
+    // leaves multiplied by the decay of token 0.
+    bool reverse = false;
 };
 
 struct DecodeArgs {
@@ -88,8 +93,10 @@ struct BwdPlan {
     int kind_q, kind_v, kind_k;   // kernel of each pass (1 matrix-core, 2 generic)
     size_t fwd_bytes;             // workspace of the largest forward pass
     bool f32acc;                  // gated bf16: the dq and dk passes write fp32 (for dg)
-    size_t off_fwd, off_qr, off_kr, off_vr, off_dor, off_dvr, off_dkr, off_part, off_s0t, off_dss, off_dst,
-        off_gr, off_sfin, off_c, off_dG, off_dqf, off_dkf, off_partf;
+    int dot_splits;               // partial sums per (b,h) of <dS, S_N> (gated)
+    // workspace offsets: forward-pass workspace, a d_v slice's dq or dk, S0^T, dS^T,
+    // S_N^T, the partial sums, q.dq - k.dk, fp32 dq and dk and a slice of them
+    size_t off_fwd, off_part, off_s0t, off_dst, off_sfin, off_c, off_dG, off_dqf, off_dkf, off_partf;
     size_t total;                 // workspace bytes
 };
 // ptrs may be null (workspace query): matrix-core passes then assume aligned tensors.

@@ -231,38 +231,60 @@ struct Lds {
     static constexpr int kBytes = kG + kGBytes;
 };
 
+// A buffer offset past every range this file builds (ranges stay below 2^31 bytes for
+// reversed walks): loads from it return zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // Asynchronous copy of one 64-row tile (row bytes RB) of a row-major matrix with row
 // stride `sb` bytes.  Each wave issues kChunks/4 instructions of 1 KB; lane l of
 // instruction i fills LDS bytes [c*1024 + 16 l, +16) with c = wave + 4 i, i.e. row
 // (c*1024 + 16 l) / RB and the 16-byte unit whose swizzled position that is.
-template <int RB, bool VSWZ, int NW>
+// REV: the walk runs over the time-reversed sequence, so LDS row r of the block at
+// walk position t0 holds matrix row N-1-t0-r.
+template <int RB, bool VSWZ, int NW, bool REV = false>
 struct TileCopy {
     static constexpr int kChunks = kBlk * RB / 1024;
     static constexpr int kPerWave = kChunks / NW;
     static_assert(kChunks % NW == 0, "tile must split evenly over the waves");
-    uint32_t voff[kPerWave];     // byte offset of this lane's unit, relative to the block's first row
+    // byte offset of this lane's unit relative to the block's first row; REV: the
+    // offset of row N-1-r (negative, as a two's complement, when r > N-1)
+    uint32_t voff[kPerWave];
 
-    __device__ __forceinline__ void init(int sb, int wave, int lane) {
+    __device__ __forceinline__ void init(int sb, int wave, int lane, int N) {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int c = wave + i * NW;
             const int off = c * 1024 + lane * 16;
             const int r = off / RB, p = (off % RB) >> 4;
             const int u = p ^ (VSWZ ? swz_v<RB / 16>(r) : swz_qk<RB / 16>(r));
-            voff[i] = static_cast<uint32_t>(r * sb + u * 16);
+            voff[i] = static_cast<uint32_t>((REV ? N - 1 - r : r) * sb + u * 16);
+        }
+        (void)N;
+    }
+    // Offset and wave-uniform base of copy i for the block at row0 (bytes row0*sb).
+    // Forward: the base carries the block; REV: the lane offset does, and a row before
+    // the sequence start (negative offset) is sent out of range.
+    __device__ __forceinline__ uint32_t lane_off(int i, uint32_t row0_bytes) const {
+        if constexpr (REV) {
+            const int d = static_cast<int>(voff[i]) - static_cast<int>(row0_bytes);
+            return d < 0 ? kOutOfRange : static_cast<uint32_t>(d);
+        } else {
+            return voff[i];
         }
     }
+    __device__ __forceinline__ static uint32_t base_off(uint32_t row0_bytes) { return REV ? 0u : row0_bytes; }
     // Rows past the end of the tensor lie outside the buffer's range and land in LDS
     // as zeros, so every LDS row holds finite data; uses mask those rows.
     __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes,
                                           int wave) const {
         const uint32_t base = tile_lds + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
 #pragma unroll
-        for (int i = 0; i < kPerWave; ++i) buf2lds16(rsrc, voff[i], row0_bytes, base + i * NW * 1024u);
+        for (int i = 0; i < kPerWave; ++i)
+            buf2lds16(rsrc, lane_off(i, row0_bytes), base_off(row0_bytes), base + i * NW * 1024u);
     }
     // copy i of this wave alone; wbase = tile_lds + 1024 * wave
     __device__ __forceinline__ void issue_one(int i, uint32_t wbase, const u32x4_t& rsrc, uint32_t row0_bytes) const {
-        buf2lds16(rsrc, voff[i], row0_bytes, wbase + i * NW * 1024u);
+        buf2lds16(rsrc, lane_off(i, row0_bytes), base_off(row0_bytes), wbase + i * NW * 1024u);
     }
 };
 enum Mode { kFull = 0, kStateOnly = 1 };
@@ -348,10 +370,15 @@ struct KArgs {
 // ONEBLK: every chunk is a single block (chunk <= 64), so each step starts a chunk and
 // the cross term can read the old state straight from the accumulators; no bf16
 // snapshot of the state is kept, which frees registers for wider column tiles.
+// REV: the walk runs over the time-reversed sequence (the adjoint recurrence of the
+// backward pass).  Walk position m reads and writes token N-1-m; its decay is that of
+// token N-m (gated: g[N-m], and 0 at m = 0); per head, state_in enters divided by gamma
+// (so the first step adds to it undecayed) and state_out leaves multiplied by the
+// decay of token 0.
 // The LDS footprint allows one workgroup per CU, i.e. NW/4 waves per SIMD; saying so
 // lets the compiler spend registers on keeping LDS reads in flight ahead of the matrix
 // instructions instead of minimising registers for an occupancy that cannot happen.
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32>
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void chunk_kernel(
     const KArgs ka) {
     const bf16_t* __restrict__ q = ka.q;
@@ -423,10 +450,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const u32x4_t k_rs = make_rsrc(k + qk_bh + srow0, static_cast<uint32_t>((N - 1) * ldqk + dk - srow0) * 2);
     const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>((N - 1) * ldv + dv - col0) * 2);
     const uint32_t lds0 = lds_addr_of(smem);
-    TileCopy<QRB, false, NW> kcp;   // Q and K tiles (same row length and swizzle)
-    TileCopy<VRB, true, NW> vcp;
-    kcp.init(ldqk * 2, wave, lane);
-    vcp.init(ldv * 2, wave, lane);
+    TileCopy<QRB, false, NW, REV> kcp;   // Q and K tiles (same row length and swizzle)
+    TileCopy<VRB, true, NW, REV> vcp;
+    kcp.init(ldqk * 2, wave, lane, N);
+    vcp.init(ldv * 2, wave, lane, N);
 
     // State accumulator element (dt, i) of lane l holds state row srow(dt, i): tiles 2s and
     // 2s+1 together cover rows 32s..32s+31, with lane group g holding rows 32s+8g..32s+8g+7
@@ -463,6 +490,15 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 int sg0 = 0;
                 if (ka.state_in != nullptr) {
                     load(ka.state_in + s_bh, 0.f, false);
+                    if constexpr (REV && !GATED) {
+                        const float inv = 1.f / decay[h];
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) S[dt][nt][i] *= inv;
+                    }
                 } else if (seg > 0) {
                     load(ka.seg_state + static_cast<size_t>(bh) * nseg * s_stride_seg, 0.f, false);
                     sg0 = 1;
@@ -581,6 +617,11 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             vcp.issue_one(i - 2 * kNQ, dv_lds, v_rs, dv_off);
         }
     };
+    // REV: byte offset of the decay of walk position m (token N-m; none at m = 0 or
+    // past the sequence, which read as zeros)
+    auto rev_goff = [&](int m) -> uint32_t {
+        return m >= 1 && m <= N ? static_cast<uint32_t>(N - m) * 4u : kOutOfRange;
+    };
     auto issue = [&](const Step& s, int qb_, int kvb_, bool defer) {
         const int k0 = s.cs + s.kb * kBlk;
         const uint32_t wofs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
@@ -603,25 +644,40 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
         if (GATED && MODE == kStateOnly) {
             // the pre-pass walks single blocks: every wave copies the block's 64 decays
-            buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
-                     lds0 + L_::kGd + kvb_ * L_::kGdStage + wave * 256);
+            if constexpr (REV)
+                buf2lds4(g_rs, rev_goff(s.cs + lane), 0u, lds0 + L_::kGd + kvb_ * L_::kGdStage + wave * 256);
+            else
+                buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
+                         lds0 + L_::kGd + kvb_ * L_::kGdStage + wave * 256);
         } else if (GATED && s.qb == 0 && s.kb == 0) {
             // chunk start: the chunk's decays.  Two stages: wave 0 prefetches them into
             // registers (8 per lane).  Three stages: every wave copies 64 per instruction
             // into the stage's LDS slot, so that every wave issues the same loads.
             if (NST == 2) {
                 if (wave == 0) {
-                    const float* gs = g_bh + s.cs;
                     const int lim = min(C, t_end - s.cs) - 1;
+                    if constexpr (REV) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, lim)];
+                        for (int i = 0; i < 8; ++i) {
+                            const int m = s.cs + min(lane * 8 + i, lim);
+                            gpre[i] = m == 0 ? 0.f : g_bh[N - m];
+                        }
+                    } else {
+                        const float* gs = g_bh + s.cs;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) gpre[i] = gs[min(lane * 8 + i, lim)];
+                    }
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < kGLoads; ++i)
-                    buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u,
-                             static_cast<uint32_t>(s.cs + 64 * (wave + i * NW)) * 4u,
-                             lds0 + L_::kGd + kvb_ * L_::kGdStage + (wave + i * NW) * 256);
+                for (int i = 0; i < kGLoads; ++i) {
+                    const uint32_t dst = lds0 + L_::kGd + kvb_ * L_::kGdStage + (wave + i * NW) * 256;
+                    if constexpr (REV)
+                        buf2lds4(g_rs, rev_goff(s.cs + 64 * (wave + i * NW) + lane), 0u, dst);
+                    else
+                        buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u,
+                                 static_cast<uint32_t>(s.cs + 64 * (wave + i * NW)) * 4u, dst);
+                }
             }
         }
     };
@@ -635,18 +691,30 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     int st_last = 0;                 // stores issued by the last step: 0 none, 1 4*NT, 2 fewer
     // lane (g, l%16) stores 4 adjacent columns of row l%16 of each 16-row tile: a
     // wave-uniform base plus a 32-bit lane offset
+    // (REV: rows run backwards from token N-1-first row)
     const uint32_t st_lane = static_cast<uint32_t>(l16 * dv + 4 * g4);
+    const int st_lane_rev = 4 * g4 - l16 * dv;
     auto store_pending = [&]() {
         if (MODE != kFull || pend_q0 < 0) return;
-        out_t* const base = o + o_bh + static_cast<size_t>(pend_q0) * dv + col0 + wcol;
+        out_t* const base = REV ? o + o_bh + static_cast<size_t>(N - 1 - pend_q0) * dv + col0 + wcol
+                                : o + o_bh + static_cast<size_t>(pend_q0) * dv + col0 + wcol;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (pend_nq < kBlk && mt * 16 + l16 >= pend_nq) continue;   // rows past the end
-            out_t* const row = base + static_cast<size_t>(mt * 16) * dv;
+            if constexpr (REV) {
+                out_t* const row = base - static_cast<ptrdiff_t>(mt * 16) * dv + st_lane_rev;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                if constexpr (OF32) *reinterpret_cast<f32x4_t*>(row + st_lane + nt * 16) = X[mt][nt];
-                else *reinterpret_cast<u16x4_t*>(row + st_lane + nt * 16) = bf4(X[mt][nt]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (OF32) *reinterpret_cast<f32x4_t*>(row + nt * 16) = X[mt][nt];
+                    else *reinterpret_cast<u16x4_t*>(row + nt * 16) = bf4(X[mt][nt]);
+                }
+            } else {
+                out_t* const row = base + static_cast<size_t>(mt * 16) * dv;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (OF32) *reinterpret_cast<f32x4_t*>(row + st_lane + nt * 16) = X[mt][nt];
+                    else *reinterpret_cast<u16x4_t*>(row + st_lane + nt * 16) = bf4(X[mt][nt]);
+                }
             }
         }
         pend_q0 = -1;
@@ -690,12 +758,22 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
     };
     auto stage_emit = [&]() {
-        out_t* const base = o + o_bh + static_cast<size_t>(xs_q0) * dv + col0;
+        if constexpr (REV) {
+            out_t* const base = o + o_bh + static_cast<size_t>(N - 1 - xs_q0) * dv + col0;
 #pragma unroll
-        for (int r = 0; r < kXRounds; ++r) {
-            const int e = r * NW * 64 + tid;
-            const int row = e / kXU, u = e % kXU;
-            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * (16 / kXE))) = xv[r];
+            for (int r = 0; r < kXRounds; ++r) {
+                const int e = r * NW * 64 + tid;
+                const int row = e / kXU, u = e % kXU;
+                *reinterpret_cast<u16x8_t*>(base + (u * (16 / kXE) - row * dv)) = xv[r];
+            }
+        } else {
+            out_t* const base = o + o_bh + static_cast<size_t>(xs_q0) * dv + col0;
+#pragma unroll
+            for (int r = 0; r < kXRounds; ++r) {
+                const int e = r * NW * 64 + tid;
+                const int row = e / kXU, u = e % kXU;
+                *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * (16 / kXE))) = xv[r];
+            }
         }
         xs_q0 = -1;
     };
@@ -1155,7 +1233,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     if (dst != nullptr) {
         // the tile goes out through LDS as well, in whole rows of 16-byte stores
         float* const st = reinterpret_cast<float*>(smem);
-        const float r = exp2_fast(lk2);
+        // REV: the final state leaves multiplied by the decay of token 0
+        float lout = lk2;
+        if constexpr (REV && MODE == kFull) lout += GATED ? g_bh[0] * kLog2e : lg;
+        const float r = exp2_fast(lout);
         wait_vmcnt<0>();
         lds_barrier();   // every wave is done with the tile buffers
         if (!SPLITK || khalf == 0) {
@@ -1182,6 +1263,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
 // Exclusive scan of segment states, in place:  buf[seg] <- state entering seg.
 //   S = state_in (or 0); for seg: T = buf[seg]; buf[seg] = S; S = 2^(l2[seg]) S + T.
+// in_gamma (reversed per-head walks): state_in enters divided by gamma[h].
 // The last segment's local state is never computed (nor read).  One thread per state
 // element of one (b,h); blocks_per_bh blocks per (b,h).  The local states of 8
 // segments are loaded before any of them is replaced, so a batch's loads are in flight
@@ -1189,14 +1271,16 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ buf,
                                                            const float* __restrict__ seg_log2,
                                                            const float* __restrict__ state_in,
+                                                           const float* __restrict__ in_gamma, int H,
                                                            int nseg, size_t per_bh, int blocks_per_bh) {
     constexpr int kBatch = 8;
     const size_t bh = blockIdx.x / blocks_per_bh;
     const int xb = blockIdx.x % blocks_per_bh;
     const float* const l2 = seg_log2 + bh * nseg;
+    const float in_scale = in_gamma != nullptr ? 1.f / in_gamma[bh % H] : 1.f;
     for (size_t e = xb * static_cast<size_t>(blockDim.x) + threadIdx.x; e < per_bh;
          e += static_cast<size_t>(blocks_per_bh) * blockDim.x) {
-        float s = state_in != nullptr ? state_in[bh * per_bh + e] : 0.f;
+        float s = state_in != nullptr ? state_in[bh * per_bh + e] * in_scale : 0.f;
         for (int sg0 = 0; sg0 < nseg; sg0 += kBatch) {
             float t[kBatch], f[kBatch];
 #pragma unroll
@@ -1216,24 +1300,25 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
     }
 }
 
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32 = false>
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
     const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>::L::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        (void)hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
     ProfScope prof(MODE == kFull ? kProfMain : kProfPre, stream);
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32>), dim3(ka.total_groups), dim3(NW * 64),
-                       lds, stream, ka);
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV>), dim3(ka.total_groups),
+                       dim3(NW * 64), lds, stream, ka);
     return hipGetLastError();
 }
 
 // Segment-state pre-pass: state-row tile DKT (<= 128) and column tile DVT, one wave
 // per 16 columns.
-template <bool GATED>
+template <bool GATED, bool REV>
 hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     ka.ndkt = ka.dk / p.pre_dkt;
     ka.ndvt = ka.dv / p.pre_dvt;
@@ -1243,7 +1328,8 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     ka.C = kBlk;
     ka.total_groups = bh * (ka.nseg - 1) * ka.ndkt * ka.ndvt;
 #define RETN_PRE(DKT, DVT)                                                                  \
-    if (p.pre_dkt == DKT && p.pre_dvt == DVT) return launch_kernel<DKT, DVT, DVT / 16, GATED, kStateOnly, true>(ka, stream);
+    if (p.pre_dkt == DKT && p.pre_dvt == DVT)                                               \
+        return launch_kernel<DKT, DVT, DVT / 16, GATED, kStateOnly, true, false, REV>(ka, stream);
     RETN_PRE(64, 64)
     RETN_PRE(64, 128)
     RETN_PRE(128, 64)
@@ -1252,7 +1338,7 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int DK, int DVT, int NW, bool GATED, bool ONEBLK, bool OF32 = false>
+template <int DK, int DVT, int NW, bool GATED, bool ONEBLK, bool OF32, bool REV>
 hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     KArgs ka{};
     ka.q = static_cast<const bf16_t*>(a.q);
@@ -1279,13 +1365,14 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         ka.seg_log2 = ka.seg_state + static_cast<size_t>(bh) * p.nseg * per_bh;
         KArgs pre = ka;
         pre.total_groups = bh;
-        hipError_t e = launch_pre<GATED>(pre, p, stream);
+        hipError_t e = launch_pre<GATED, REV>(pre, p, stream);
         if (e != hipSuccess) return e;
         if (!p.fuse_scan) {
             const int xblocks = static_cast<int>(std::min<size_t>((per_bh + 255) / 256, 256));
             ProfScope prof(kProfScan, stream);
             hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
-                               stream, ka.seg_state, ka.seg_log2, a.state_in, p.nseg, per_bh, xblocks);
+                               stream, ka.seg_state, ka.seg_log2, a.state_in, REV && !GATED ? a.decay : nullptr,
+                               a.H, p.nseg, per_bh, xblocks);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1293,7 +1380,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
     ka.ndkt = 1;
     ka.ndvt = a.dv / DVT;
     ka.total_groups = bh * p.nseg * ka.ndvt;
-    return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK, OF32>(ka, stream);
+    return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK, OF32, REV>(ka, stream);
 }
 
 // State columns per workgroup and waves per workgroup for a head shape.
@@ -1341,23 +1428,27 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     return p;
 }
 
-hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+namespace {
+
+template <int DK, int DVT, int NW, bool REV>
+hipError_t launch_variant(const ChunkArgs& a, const MfmaPlan& p, bool one, hipStream_t stream) {
+    if (a.gated && a.out_f32)
+        return one ? launch_shape<DK, DVT, NW, true, true, true, REV>(a, p, stream)
+                   : launch_shape<DK, DVT, NW, true, false, true, REV>(a, p, stream);
+    if (a.gated)
+        return one ? launch_shape<DK, DVT, NW, true, true, false, REV>(a, p, stream)
+                   : launch_shape<DK, DVT, NW, true, false, false, REV>(a, p, stream);
+    return one ? launch_shape<DK, DVT, NW, false, true, false, REV>(a, p, stream)
+               : launch_shape<DK, DVT, NW, false, false, false, REV>(a, p, stream);
+}
+
+template <bool REV>
+hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     // the kernel handles any chunk in [1, 512], including chunks that are not a
     // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant
     const bool one = a.chunk <= kBlk;
-    // fp32 outputs: gated shapes only (the gated backward's gate gradient needs them)
-    if (a.out_f32 && !a.gated) return hipErrorInvalidValue;
-#define RETN_SHAPE(DK, DVT, NW)                                                            \
-    if (a.dk == DK && p.dvt == DVT && p.nw == NW) {                                       \
-        if (a.gated && a.out_f32)                                                         \
-            return one ? launch_shape<DK, DVT, NW, true, true, true>(a, p, stream)        \
-                       : launch_shape<DK, DVT, NW, true, false, true>(a, p, stream);      \
-        if (a.gated)                                                                      \
-            return one ? launch_shape<DK, DVT, NW, true, true>(a, p, stream)              \
-                       : launch_shape<DK, DVT, NW, true, false>(a, p, stream);            \
-        return one ? launch_shape<DK, DVT, NW, false, true>(a, p, stream)                 \
-                   : launch_shape<DK, DVT, NW, false, false>(a, p, stream);               \
-    }
+#define RETN_SHAPE(DK, DVT, NW) \
+    if (a.dk == DK && p.dvt == DVT && p.nw == NW) return launch_variant<DK, DVT, NW, REV>(a, p, one, stream);
     RETN_SHAPE(64, 64, 4)
     RETN_SHAPE(64, 128, 8)
     RETN_SHAPE(128, 64, 4)
@@ -1365,9 +1456,23 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t 
     RETN_SHAPE(256, 64, 4)
 #undef RETN_SHAPE
     // the gated form's decay array does not fit beside double-buffered 256 x 128 tiles
-    if (a.dk == 256 && p.dvt == 128 && p.nw == 8 && !a.gated && one)
-        return launch_shape<256, 128, 8, false, true>(a, p, stream);
+    if (a.dk == 256 && p.dvt == 128 && p.nw == 8 && !a.gated && !a.out_f32 && one)
+        return launch_shape<256, 128, 8, false, true, false, REV>(a, p, stream);
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    // fp32 outputs: gated shapes only (the gated backward's gate gradient needs them)
+    if (a.out_f32 && !a.gated) return hipErrorInvalidValue;
+    // reversed walks address rows with signed 32-bit byte offsets
+    if (a.reverse) {
+        const size_t ld = static_cast<size_t>(std::max({a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.dv}));
+        if ((static_cast<size_t>(a.N) + kBlk) * ld * 2 >= (static_cast<size_t>(1) << 31)) return hipErrorInvalidValue;
+        return launch_dir<true>(a, p, stream);
+    }
+    return launch_dir<false>(a, p, stream);
 }
 
 }  // namespace retn

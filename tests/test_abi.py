@@ -132,12 +132,13 @@ def test_backward_validation(L, gated):
     assert c(gsi=FAKE + 256 * MB) == ERR_ALIAS               # grad_state_in over grad_o
     # fp32 with d_v above the score width of the kernels
     assert c(dv=512) == ERR_UNSUPPORTED
-    # bf16 needs workspace for the reversed copies
+    # an initial state needs workspace (its transposed copy)
     need = L.retention_bwd_workspace_bytes(1, 2, 64, 16, 16, 16, 1, int(gated))
     assert need > 0
-    assert c(dt=1) == ERR_WORKSPACE
-    assert c(dt=1, ws=FAKE + 600 * MB, wsb=16) == ERR_WORKSPACE
-    assert c(dt=1, ws=FAKE + 600 * MB + 4, wsb=need) == ERR_WORKSPACE   # 16-byte alignment
+    si = FAKE + 700 * MB
+    assert c(dt=1, si=si) == ERR_WORKSPACE
+    assert c(dt=1, si=si, ws=FAKE + 600 * MB, wsb=16) == ERR_WORKSPACE
+    assert c(dt=1, si=si, ws=FAKE + 600 * MB + 4, wsb=need) == ERR_WORKSPACE   # 16-byte alignment
     assert c(B=0) == OK                                                   # nothing to do
 
 
