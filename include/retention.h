@@ -115,6 +115,32 @@ retn_status gated_retention_chunkwise_fwd(const void* q, const void* k, const vo
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * Parallel-form retention forward, the short-sequence training path (tutorial, section
+ * 并行训练: O = (Q K^T (.) D) V with D[n,m] = gamma^(n-m) for n >= m, else 0; pwwt.cn
+ * guide, section 三种计算路径与增量状态, names it as the first of the three paths).  No
+ * state in or out and no workspace.  The result is the chunkwise forward's with a zero
+ * initial state.  bf16 with dk in {64, 128, 256} and dv a multiple of 64 (<= 1024) runs
+ * every 64-token query block of a (b,h) in its own workgroup; other shapes and fp32 take
+ * the generic kernel.  Arguments as retention_chunkwise_fwd.
+ */
+retn_status retention_parallel_fwd(const void* q, const void* k, const void* v,
+                                   const float* gamma, void* o,
+                                   int B, int H, int N, int dk, int dv,
+                                   retn_dtype dtype, void* stream);
+
+/*
+ * Gated parallel form: D[n,m] = exp(G_n - G_m) for n >= m with G the inclusive cumulative
+ * sum of g (pwwt.cn guide, section 三种计算路径与增量状态, its parallel path).  The
+ * matrix-core kernel keeps G of the whole sequence in LDS, so it takes N <= 512; longer
+ * bf16 sequences and fp32 take the generic kernel (N <= 1024 is not required there).
+ * Arguments as gated_retention_chunkwise_fwd without state and workspace.
+ */
+retn_status gated_retention_parallel_fwd(const void* q, const void* k, const void* v,
+                                         const float* g, void* o,
+                                         int B, int H, int N, int dk, int dv,
+                                         retn_dtype dtype, void* stream);
+
+/*
  * One recurrent decode step (tutorial, section 递归推理):
  *     S <- gamma[h] S + k^T v   (fp32, in place),   o = q S   (with the updated S)
  *   q, k   [B,H,dk]  v, o [B,H,dv]  element type `dtype`

@@ -1,4 +1,4 @@
-"""MI355X-native retention operator: chunkwise forward and backward, decode step, gated variants.
+"""MI355X-native retention operator: chunkwise and parallel forward, backward, decode step, gated variants.
 
 The operator runs in libretention_fwd.so (hand-written HIP kernels for gfx950) behind
 the C ABI in include/retention.h; this package is its Python binding.  Importing the
@@ -10,12 +10,14 @@ from ._lib import (  # noqa: F401
     gated_retention_chunkwise_bwd,
     gated_retention_chunkwise_fwd,
     gated_retention_decode_step,
+    gated_retention_parallel_fwd,
     lib,
     profile_enable,
     profile_read,
     retention_chunkwise_bwd,
     retention_chunkwise_fwd,
     retention_decode_step,
+    retention_parallel_fwd,
     workspace_bytes,
 )
 
@@ -27,6 +29,8 @@ __all__ = [
     "gated_retention_chunkwise_fwd",
     "retention_decode_step",
     "gated_retention_decode_step",
+    "retention_parallel_fwd",
+    "gated_retention_parallel_fwd",
     "workspace_bytes",
     "RetentionError",
     "lib",

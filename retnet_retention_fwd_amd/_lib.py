@@ -35,6 +35,8 @@ EXPORTED = (
     "retention_chunkwise_bwd",
     "gated_retention_chunkwise_bwd",
     "retention_bwd_workspace_bytes",
+    "retention_parallel_fwd",
+    "gated_retention_parallel_fwd",
 )
 
 # Kernel kinds reported by retention_profile_read.
@@ -87,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.gated_retention_chunkwise_bwd.restype = ctypes.c_int
     L.retention_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
     L.retention_bwd_workspace_bytes.restype = _sz
+    for name in ("retention_parallel_fwd", "gated_retention_parallel_fwd"):
+        f = getattr(L, name)
+        f.argtypes = [_vp] * 5 + [_i] * 6 + [_vp]
+        f.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -203,6 +209,44 @@ def gated_retention_chunkwise_fwd(q, k, v, g, chunk, state_in=None, return_state
     """Gated chunkwise retention forward with per-token log-decays g[B,H,N] (fp32, <= 0)."""
     return _chunk_call("gated_retention_chunkwise_fwd", q, k, v, g, chunk, state_in, return_state, out,
                        state_out, stream, workspace, True)
+
+
+def _parallel_call(fn_name, q, k, v, decay, out, stream, gated):
+    torch = _torch()
+    L = lib()
+    _require(q, "q")
+    dev = q.device
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(decay, "g" if gated else "gamma", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"expected q,k [B,H,N,dk] and v [B,H,N,dv]; got {tuple(q.shape)} "
+                         f"{tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    exp_decay = (B, H, N) if gated else (H,)
+    if tuple(decay.shape) != exp_decay:
+        raise ValueError(f"decay must have shape {exp_decay}, got {tuple(decay.shape)}")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", q.dtype, dev)
+        if tuple(out.shape) != (B, H, N, dv):
+            raise ValueError("out must be [B,H,N,dv]")
+    st = getattr(L, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(out), B, H, N, dk, dv, _dtype_code(q),
+                             _stream(stream))
+    _check(st, fn_name)
+    return out
+
+
+def retention_parallel_fwd(q, k, v, gamma, out=None, stream=None):
+    """Parallel-form retention forward O = (Q K^T (.) D) V (no state); shapes as the chunkwise form."""
+    return _parallel_call("retention_parallel_fwd", q, k, v, gamma, out, stream, False)
+
+
+def gated_retention_parallel_fwd(q, k, v, g, out=None, stream=None):
+    """Gated parallel-form forward with per-token log-decays g[B,H,N] (fp32, <= 0)."""
+    return _parallel_call("gated_retention_parallel_fwd", q, k, v, g, out, stream, True)
 
 
 def bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:

@@ -16,6 +16,7 @@ namespace {
 constexpr int kMaxDk = 256;           // dk limit (state slice in LDS / registers)
 constexpr int kMaxDv = 1024;          // dv limit
 constexpr int kGenericMaxGatedChunk = 1024;  // chunk-local cumsum kept in LDS
+constexpr int kParallelGenericChunk = 64;    // chunk of the generic kernel for the parallel form
 
 struct Range {
     uintptr_t lo, hi;   // [lo, hi)
@@ -112,6 +113,23 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
     retn::ChunkArgs a{q, k, v, decay, o, state_in, state_out, B, H, N, dk, dv, eff_chunk,
                       dt == RETN_BF16, gated, workspace, workspace_bytes};
     const hipError_t e = mfma ? retn::launch_mfma_chunk(a, plan, s) : retn::launch_generic_chunk(a, s);
+    return e == hipSuccess ? RETN_OK : RETN_ERR_HIP;
+}
+
+// Parallel form: the matrix-core kernel over whole-sequence query blocks, else the
+// generic kernel, which evaluates the same function chunk by chunk.
+retn_status parallel_common(const void* q, const void* k, const void* v, const float* decay, void* o, int B, int H,
+                            int N, int dk, int dv, retn_dtype dt, void* stream, bool gated) {
+    retn_status st = validate_chunk(q, k, v, decay, o, nullptr, nullptr, B, H, N, dk, dv, 1, dt, gated);
+    if (st != RETN_OK) return st;
+    const size_t bh = static_cast<size_t>(B) * H;
+    if (bh == 0 || N == 0) return RETN_OK;
+    const bool mfma = retn::mfma_parallel_supported(dk, dv, N, gated, dt == RETN_BF16) && aligned16(q) &&
+                      aligned16(k) && aligned16(v) && aligned16(o);
+    const int chunk = mfma ? N : std::min(N, kParallelGenericChunk);
+    retn::ChunkArgs a{q, k, v, decay, o, nullptr, nullptr, B, H, N, dk, dv, chunk, dt == RETN_BF16, gated, nullptr, 0};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = mfma ? retn::launch_mfma_parallel(a, s) : retn::launch_generic_chunk(a, s);
     return e == hipSuccess ? RETN_OK : RETN_ERR_HIP;
 }
 
@@ -214,6 +232,16 @@ retn_status gated_retention_decode_step(const void* q, const void* k, const void
                                         const float* g, float* state, void* o, int B, int H,
                                         int dk, int dv, retn_dtype dtype, void* stream) {
     return decode_common(q, k, v, g, state, o, B, H, dk, dv, dtype, stream, true);
+}
+
+retn_status retention_parallel_fwd(const void* q, const void* k, const void* v, const float* gamma, void* o,
+                                   int B, int H, int N, int dk, int dv, retn_dtype dtype, void* stream) {
+    return parallel_common(q, k, v, gamma, o, B, H, N, dk, dv, dtype, stream, false);
+}
+
+retn_status gated_retention_parallel_fwd(const void* q, const void* k, const void* v, const float* g, void* o,
+                                         int B, int H, int N, int dk, int dv, retn_dtype dtype, void* stream) {
+    return parallel_common(q, k, v, g, o, B, H, N, dk, dv, dtype, stream, true);
 }
 
 size_t retention_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, retn_dtype dtype,

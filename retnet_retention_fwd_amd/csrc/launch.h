@@ -67,6 +67,10 @@ struct MfmaPlan {
 };
 MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated);
 hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream_t stream);
+// Parallel form on the matrix cores (no state): O = (Q K^T (.) D) V with the query blocks
+// of a (b,h) in parallel workgroups.
+bool mfma_parallel_supported(int dk, int dv, int N, bool gated, bool bf16);
+hipError_t launch_mfma_parallel(const ChunkArgs& a, hipStream_t stream);
 
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

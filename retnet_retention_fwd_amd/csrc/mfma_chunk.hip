@@ -378,7 +378,11 @@ struct KArgs {
 // The LDS footprint allows one workgroup per CU, i.e. NW/4 waves per SIMD; saying so
 // lets the compiler spend registers on keeping LDS reads in flight ahead of the matrix
 // instructions instead of minimising registers for an occupancy that cannot happen.
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV>
+// PAR (parallel form, MODE = kFull, no state): the whole sequence is one chunk and each
+// workgroup owns one query block, so O = (Q K^T (.) D) V with no cross term and no state;
+// the query blocks of a (b,h) run in parallel.  nseg then holds the number of query
+// blocks.
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV, bool PAR>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void chunk_kernel(
     const KArgs ka) {
     const bf16_t* __restrict__ q = ka.q;
@@ -418,7 +422,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int nseg_grid = MODE == kFull ? nseg : nseg - 1;   // the last segment's state is not needed
     const int dvt = wid % ndvt;
     const int dkt = (wid / ndvt) % ndkt;
-    const int seg = (wid / (ndvt * ndkt)) % nseg_grid;
+    // PAR: seg is the query block, the longest ones of a (b,h) first
+    const int seg = PAR ? nseg - 1 - (wid / (ndvt * ndkt)) % nseg : (wid / (ndvt * ndkt)) % nseg_grid;
     const int bh = wid / (ndvt * ndkt * nseg_grid);
     const int h = bh % H;
 
@@ -431,8 +436,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // transpose-read source coordinates of this lane within its 16-lane group
     const int trj = l16 >> 2, trq = l16 & 3;
 
-    const int t_begin = seg * seg_tokens;
-    const int t_end = min(N, t_begin + seg_tokens);
+    const int t_begin = PAR ? 0 : seg * seg_tokens;
+    const int t_end = PAR ? N : min(N, t_begin + seg_tokens);
     const float lg = GATED ? 0.f : log2f(decay[h]);
 
     // q, k rows have dk elements; this workgroup's K tile covers dims dkt*DK .. +DK
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) S[dt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (MODE == kFull) {
+        if (MODE == kFull && !PAR) {
             if (nseg == 1 || ka.fuse_scan) {
                 // entry state of segment seg: S <- 2^(l2 of segment s) S + local state of s.
                 // The first source is loaded straight into the accumulators (all loads in
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
             else
                 buf2lds4(g_rs, static_cast<uint32_t>(lane) * 4u, static_cast<uint32_t>(s.cs) * 4u,
                          lds0 + L_::kGd + kvb_ * L_::kGdStage + wave * 256);
-        } else if (GATED && s.qb == 0 && s.kb == 0) {
+        } else if (GATED && (PAR ? s.kb == 0 : s.qb == 0 && s.kb == 0)) {
             // chunk start: the chunk's decays.  Two stages: wave 0 prefetches them into
             // registers (8 per lane).  Three stages: every wave copies 64 per instruction
             // into the stage's LDS slot, so that every wave issues the same loads.
@@ -796,7 +801,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     uint32_t qof = 0, ldof = 0;
     auto issue_step = [&](const Step& s, int b, bool defer) {
         const bool needq = MODE == kFull && s.kb == 0;
-        const bool needg = GATED && MODE == kFull && NST == 3 && s.qb == 0 && s.kb == 0;
+        const bool needg = GATED && MODE == kFull && NST == 3 && (PAR ? s.kb == 0 : s.qb == 0 && s.kb == 0);
         if (needq) qlast = qlast + 1 == PL::QS ? 0 : qlast + 1;
         issue(s, qlast, b, defer);
         qof = (qof & ~(3u << (2 * b))) | (static_cast<uint32_t>(qlast) << (2 * b));
@@ -807,7 +812,16 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // the asynchronous copies, so a load it still tracked inside the loop would make it
     // wait there for them.  The full pass issues its first copies before the drain, so
     // that the two latencies overlap.
-    Step cur{t_begin, 0, 0};
+    // the walk: PAR visits key blocks 0..seg of query block seg only
+    auto advance = [&](Step& s) -> bool {
+        if constexpr (PAR) {
+            if (s.kb < s.qb) { ++s.kb; return true; }
+            return false;
+        } else {
+            return next_step<MODE>(s, t_end, C);
+        }
+    };
+    Step cur{t_begin, PAR ? seg : 0, 0};
     if (MODE == kFull) issue_step(cur, 0, false);
     __builtin_amdgcn_s_waitcnt(0);
     if (MODE != kFull) issue_step(cur, 0, false);
@@ -816,7 +830,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     bool more = true;
     int inflight = 0;
     for (int i = 0; i < NST - 2 && more; ++i) {
-        more = next_step<MODE>(ahead, t_end, C);
+        more = advance(ahead);
         if (more) issue_step(ahead, ++inflight, false);
     }
 
@@ -852,7 +866,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         const int L = min(C, t_end - cur.cs);
         const int qb = ONEBLK ? 0 : cur.qb, kb = ONEBLK ? 0 : cur.kb;
         const bool diag = kb == qb;
-        if (qb == 0 && kb == 0) {
+        if (PAR ? kb == 0 : qb == 0 && kb == 0) {
             // start of a chunk: decays, bf16 snapshot of the old state, S <- 2^(G_{L-1}) S
             if (GATED && MODE == kStateOnly) {
                 if (wave == 0) {
@@ -890,7 +904,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 lds_barrier();
             }
             const float l2chunk = l2x(L - 1);
-            if (MODE == kFull && !ONEBLK) {
+            if (MODE == kFull && !ONEBLK && !PAR) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -902,18 +916,18 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
 
         Step nxt = cur;
-        const bool has_next = next_step<MODE>(nxt, t_end, C);
+        const bool has_next = advance(nxt);
         // With three stages the output stores must precede the loads (see the wait
         // above); with two, the loads go first so that they start earlier.
         if (NST == 3) store_pending();
         if (more) {
-            more = next_step<MODE>(ahead, t_end, C);
+            more = advance(ahead);
             if (more) {
                 ++inflight;
                 int b = kvbuf + inflight;
                 if (b >= NST) b -= NST;
                 // deferred to the cross term when this step has one
-                issue_step(ahead, b, kb == 0);
+                issue_step(ahead, b, kb == 0 && !PAR);
             }
         }
         if (NST != 3) store_pending();
@@ -929,11 +943,13 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
         const uint32_t vbase = lds0 + L_::kV + kvbuf * L_::kVTile;
         if (MODE == kFull) {
             if (kb == 0) {
-                // cross-chunk term X = diag(2^G) (Q S_prev), rows of block qb
+                // cross-chunk term X = diag(2^G) (Q S_prev), rows of block qb (PAR: none)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) X[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            if (kb == 0 && !PAR) {
                 uint32_t cq[KL];
 #pragma unroll
                 for (int kl = 0; kl < KL; ++kl) cq[kl] = opaque(pq[kl] + qbase);
@@ -1047,7 +1063,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 for (int nt = 0; nt < NT; ++nt) S[dt][nt] *= r;
             lk2 = 0.f;
         }
-        if (diag) {
+        if (diag && !PAR) {
             // S += K^T (V (.) zeta) over the keys of block qb; slots are keys
             // 32ks + 8g .. 32ks + 8g + 7, gathered by transpose reads of K and V
 #pragma unroll
@@ -1225,7 +1241,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     // ---- results
     float* dst = nullptr;
     if (MODE == kFull) {
-        if (seg == nseg - 1 && ka.state_out != nullptr) dst = ka.state_out + s_bh;
+        if (!PAR && seg == nseg - 1 && ka.state_out != nullptr) dst = ka.state_out + s_bh;
     } else {
         dst = ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
         if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
@@ -1300,18 +1316,18 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
     }
 }
 
-template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV>
+template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV, bool PAR = false>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
     const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>::L::kBytes;
     static bool attr_done = false;   // benign race: the attribute call is idempotent
     if (!attr_done) {
         (void)hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV>),
+            reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV, PAR>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_done = true;
     }
     ProfScope prof(MODE == kFull ? kProfMain : kProfPre, stream);
-    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV>), dim3(ka.total_groups),
+    hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV, PAR>), dim3(ka.total_groups),
                        dim3(NW * 64), lds, stream, ka);
     return hipGetLastError();
 }
@@ -1462,6 +1478,64 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
 }
 
 }  // namespace
+
+namespace {
+
+// Parallel form: one workgroup per (b,h), query block and column tile; no state, no
+// workspace.  Chunk-length-one-block variants are not used (the query blocks differ).
+template <int DK, int DVT, int NW, bool GATED>
+hipError_t launch_parallel_shape(const ChunkArgs& a, hipStream_t stream) {
+    KArgs ka{};
+    ka.q = static_cast<const bf16_t*>(a.q);
+    ka.k = static_cast<const bf16_t*>(a.k);
+    ka.v = static_cast<const bf16_t*>(a.v);
+    ka.decay = a.decay;
+    ka.o = a.o;
+    ka.H = a.H;
+    ka.N = a.N;
+    ka.dk = a.dk;
+    ka.dv = a.dv;
+    ka.ldqk = a.dk;
+    ka.ldv = a.dv;
+    ka.C = a.N;
+    ka.seg_tokens = a.N;
+    ka.nseg = (a.N + kBlk - 1) / kBlk;   // query blocks
+    ka.ndkt = 1;
+    ka.ndvt = a.dv / DVT;
+    const size_t groups = static_cast<size_t>(a.B) * a.H * ka.nseg * ka.ndvt;
+    if (groups > static_cast<size_t>(INT32_MAX)) return hipErrorInvalidValue;
+    ka.total_groups = static_cast<int>(groups);
+    return launch_kernel<DK, DVT, NW, GATED, kFull, false, false, false, true>(ka, stream);
+}
+
+}  // namespace
+
+bool mfma_parallel_supported(int dk, int dv, int N, bool gated, bool bf16) {
+    if (!bf16 || N < 1) return false;
+    if (dk != 64 && dk != 128 && dk != 256) return false;
+    if (dv % 64 != 0 || dv > 1024) return false;
+    // the gated form keeps the sequence's cumulative decays in LDS
+    if (gated && N > kMaxChunk) return false;
+    // rows and the causal block count stay in 32-bit arithmetic
+    return static_cast<size_t>(N) * std::max(dk, dv) * 2 < (static_cast<size_t>(1) << 31);
+}
+
+hipError_t launch_mfma_parallel(const ChunkArgs& a, hipStream_t stream) {
+    if (!mfma_parallel_supported(a.dk, a.dv, a.N, a.gated, a.bf16)) return hipErrorInvalidValue;
+    int dvt, nw;
+    pick_tile(a.dk, a.dv, kBlk + 1, a.gated, dvt, nw);   // the tiles of multi-block chunks
+#define RETN_PSHAPE(DK, DVT, NW)                                                                \
+    if (a.dk == DK && dvt == DVT && nw == NW)                                                   \
+        return a.gated ? launch_parallel_shape<DK, DVT, NW, true>(a, stream)                    \
+                       : launch_parallel_shape<DK, DVT, NW, false>(a, stream);
+    RETN_PSHAPE(64, 64, 4)
+    RETN_PSHAPE(64, 128, 8)
+    RETN_PSHAPE(128, 64, 4)
+    RETN_PSHAPE(128, 128, 8)
+    RETN_PSHAPE(256, 64, 4)
+#undef RETN_PSHAPE
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     // fp32 outputs: gated shapes only (the gated backward's gate gradient needs them)

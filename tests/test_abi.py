@@ -152,6 +152,23 @@ def test_backward_workspace_query(L):
     assert L.retention_bwd_workspace_bytes(1, 1, 0, 16, 16, 16, 1, 1) == 0     # no tokens
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_parallel_validation(L, gated):
+    f = L.gated_retention_parallel_fwd if gated else L.retention_parallel_fwd
+
+    def c(q=FAKE, k=FAKE + 64 * MB, v=FAKE + 128 * MB, d=FAKE + 192 * MB, o=FAKE + 256 * MB, B=1, H=2, N=64,
+          dk=16, dv=16, dt=1):
+        return f(q, k, v, d, o, B, H, N, dk, dv, dt, None)
+
+    assert c(dt=4) == ERR_DTYPE
+    assert c(N=-1) == ERR_SHAPE
+    assert c(dk=512) == ERR_UNSUPPORTED
+    assert c(d=None) == ERR_NULL
+    assert c(o=None) == ERR_NULL
+    assert c(o=FAKE + 64 * MB) == ERR_ALIAS      # o over k
+    assert c(B=0) == OK and c(N=0) == OK          # nothing to do
+
+
 def test_profile_read_validation(L):
     assert L.retention_profile_read(None, None, -1, None) == ERR_SHAPE
     assert L.retention_profile_read(None, None, 2, None) == ERR_NULL
