@@ -14,9 +14,12 @@ over from the previous step.
 
 Secondary lines (same JSON object, "secondary"): the recurrent decode step (batch
 128, H=32, d=128, 1024 consecutive steps, GB/s of the fp32 state stream), the
-long-sequence workload at chunk 128/256/512, the gated workload, and the backward
-of the train and gated workloads (with an initial state and a final-state gradient;
-GB/s counts Q, K, V, dO read and dQ, dK, dV written once).
+long-sequence workload at chunk 128/256/512, the gated workload, the backward of the
+train and gated workloads (with an initial state and a final-state gradient; GB/s
+counts Q, K, V, dO read and dQ, dK, dV written once), the parallel form on short
+sequences (with the chunkwise form on the same inputs beside it), and the gated
+retention layer around the operator (B=4 N=2048 D=1024 H=8 d=128; TFLOP/s of its six
+projections over the layer's time).
 
 "roofline" describes the dominant kernel of the headline step, the matrix-core
 chunkwise pass (a step also runs the segment-state pre-pass): algorithmic bytes (Q, K,
@@ -179,6 +182,51 @@ def run_bwd_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps, w
     }
 
 
+def run_parallel_workload(torch, R, B, H, N, dk, dv, steps, warmup, seed):
+    """Parallel form on a short sequence, per-head decays; the chunkwise form (chunk 64)
+    on the same inputs is timed beside it."""
+    data = chunk_inputs(torch, B, H, N, dk, dv, False, 2, seed)
+    gm = torch.tensor([1.0 - 2.0 ** (-5.0 - i) for i in range(H)], device="cuda", dtype=torch.float32)
+    outs = [torch.empty(B, H, N, dv, device="cuda", dtype=torch.bfloat16) for _ in range(2)]
+
+    def par(i):
+        q, k, v, _, _ = data[i % 2]
+        R.retention_parallel_fwd(q, k, v, gm, out=outs[i % 2])
+
+    def chk(i):
+        q, k, v, _, _ = data[i % 2]
+        R.retention_chunkwise_fwd(q, k, v, gm, 64, out=outs[i % 2])
+
+    tp, _ = time_steps(par, steps, warmup, torch)
+    tc, _ = time_steps(chk, steps, warmup, torch)
+    nb = alg_bytes(B, H, N, dk, dv)
+    return {"workload": "parallel form", "B": B, "H": H, "N": N, "dk": dk, "dv": dv,
+            "us_per_step": tp / steps * 1e6, "tokens_per_s": B * N / (tp / steps),
+            "alg_GBps": nb / (tp / steps) / 1e9, "chunkwise_c64_us": tc / steps * 1e6}
+
+
+def run_msr_workload(torch, R, B, N, D, H, dk, dv, steps, warmup, seed):
+    """Gated retention layer (projections, rotation, decays, retention, norm and gate,
+    output projection) on bf16 activations and random weights."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(B, N, D, device="cuda", generator=g).to(torch.bfloat16)
+    s = D ** -0.5
+    shapes = ((H * dk, D), (H * dk, D), (H * dv, D), (H * dv, D), (H, D), (D, H * dv))
+    w = [(torch.randn(*sh, device="cuda", generator=g) * s).to(torch.bfloat16) for sh in shapes]
+    ws = torch.empty(R.msr_workspace_bytes(B, N, D, H, dk, dv, 64), dtype=torch.uint8, device="cuda")
+    y = torch.empty(B, N, D, dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        R.gated_msr_fwd(x, *w, H, dk, dv, chunk=64, out=y, workspace=ws)
+
+    t, _ = time_steps(step, steps, warmup, torch)
+    per = t / steps
+    fl = 2 * B * N * D * (2 * H * dk + 2 * H * dv + H) + 2 * B * N * H * dv * D
+    return {"workload": "gated retention layer", "B": B, "N": N, "D": D, "H": H, "dk": dk, "dv": dv, "chunk": 64,
+            "us_per_step": per * 1e6, "tokens_per_s": B * N / per, "projection_TFLOPs": fl / per / 1e12}
+
+
 def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4):
     """Recurrent decode: batch 128, H=32, d=128; S0 ~ N(0, 0.1^2) fp32; fresh bf16
     q,k,v per step (pre-generated on the GPU); gamma_h = 1 - 2^(-5 - 7h/31)."""
@@ -302,6 +350,9 @@ def main():
                                                             False, 20, 3, seed=6)
         secondary["gated_bf16_backward"] = run_bwd_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
                                                             True, 20, 3, seed=7)
+        secondary["parallel_bf16_N256"] = run_parallel_workload(torch, R, 2, 16, 256, 128, 128, 50, 5, seed=8)
+        secondary["parallel_bf16_N512"] = run_parallel_workload(torch, R, 16, 8, 512, 128, 128, 50, 5, seed=9)
+        secondary["msr_layer_bf16"] = run_msr_workload(torch, R, 4, 2048, 1024, 8, 128, 128, 30, 5, seed=10)
 
     main_us = head["kernels"]["chunk_main"]["avg_us"]
     nb = alg_bytes(4, 8, 2048, 256, 512)

@@ -206,6 +206,35 @@ retn_status gated_retention_chunkwise_bwd(const void* q, const void* k, const vo
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * Gated multi-scale retention layer forward (YOCO's gated RetNet mixer: pwwt.cn guide,
+ * section GateRetention 模块的内部结构, with the k scaling of section 三种计算路径与增量状态):
+ *     q, k, v, g, gt = x Wq^T, x Wk^T, x Wv^T, x Wg^T, x Wgt^T     (no biases)
+ *     q, k <- rotation of adjacent pairs (2i, 2i+1) of token n by n * rope_base^(-2i/dk)
+ *     k <- k / sqrt(dk);   decay = logsigmoid(gt) / 16   [B,H,N]
+ *     o = gated_retention_chunkwise_fwd(q, k, v, decay)   (zero initial state)
+ *     y = (silu(g) * RMSNorm_eps(o per head, over dv)) Wo^T
+ *   x        [B,N,D] bf16;   y [B,N,D] bf16, must not overlap any input
+ *   wq, wk   [H*dk, D];  wv, wg [H*dv, D];  wgt [H, D];  wo [D, H*dv]   (bf16,
+ *            [out_features, in_features], contiguous, 16-byte aligned)
+ *   chunk    chunk size of the retention call;  rope_base > 1;  norm_eps >= 0
+ *   workspace  16-byte aligned scratch of at least gated_msr_workspace_bytes(...) bytes
+ * Supported: dk in {64, 128, 256}, dv a multiple of 64 (<= 1024), D a multiple of 64,
+ * chunk <= 512; else RETN_ERR_UNSUPPORTED.  The projections run on a
+ * bf16 matrix-core GEMM with fp32 accumulation; q, k, v, g enter the operator in bf16, the
+ * retention output stays fp32 through the normalisation.
+ */
+retn_status gated_msr_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                          const void* wg, const void* wgt, const void* wo, void* y,
+                          int B, int N, int D, int H, int dk, int dv, int chunk,
+                          float rope_base, float norm_eps, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace gated_msr_fwd needs for these sizes; 0 for unsupported sizes.
+ */
+size_t gated_msr_workspace_bytes(int B, int N, int D, int H, int dk, int dv, int chunk);
+
+/*
  * Bytes of workspace the backward entry points need for these sizes (sized for an
  * initial state and a final-state gradient being given); 0 for invalid or unsupported
  * sizes, which the entry point then reports.

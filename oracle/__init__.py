@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the retention operator -- test infrastructure only.
+"""fp64 CPU oracle of the retention operator and its gated layer -- test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may
 import this package.  It shares no code with the HIP library and imports nothing from
@@ -7,4 +7,8 @@ rational arithmetic, closed forms, textbook special cases and hand-worked fixtur
 (``tests/golden/``); no function here is "parity unpinned".
 """
 from .retention_oracle import *  # noqa: F401,F403
-from .retention_oracle import __all__  # noqa: F401
+from .retention_oracle import __all__ as _ops_all
+from .msr_oracle import *  # noqa: F401,F403
+from .msr_oracle import __all__ as _msr_all
+
+__all__ = list(_ops_all) + list(_msr_all)

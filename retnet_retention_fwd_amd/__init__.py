@@ -1,4 +1,5 @@
-"""MI355X-native retention operator: chunkwise and parallel forward, backward, decode step, gated variants.
+"""MI355X-native retention operator: chunkwise and parallel forward, backward, decode step, gated
+variants, and the gated retention layer around it.
 
 The operator runs in libretention_fwd.so (hand-written HIP kernels for gfx950) behind
 the C ABI in include/retention.h; this package is its Python binding.  Importing the
@@ -7,11 +8,13 @@ package does not load the library; the first call does, and raises if it is miss
 from ._lib import (  # noqa: F401
     RetentionError,
     bwd_workspace_bytes,
+    gated_msr_fwd,
     gated_retention_chunkwise_bwd,
     gated_retention_chunkwise_fwd,
     gated_retention_decode_step,
     gated_retention_parallel_fwd,
     lib,
+    msr_workspace_bytes,
     profile_enable,
     profile_read,
     retention_chunkwise_bwd,
@@ -32,6 +35,8 @@ __all__ = [
     "retention_parallel_fwd",
     "gated_retention_parallel_fwd",
     "workspace_bytes",
+    "gated_msr_fwd",
+    "msr_workspace_bytes",
     "RetentionError",
     "lib",
     "profile_enable",

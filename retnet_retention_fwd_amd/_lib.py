@@ -37,6 +37,8 @@ EXPORTED = (
     "retention_bwd_workspace_bytes",
     "retention_parallel_fwd",
     "gated_retention_parallel_fwd",
+    "gated_msr_fwd",
+    "gated_msr_workspace_bytes",
 )
 
 # Kernel kinds reported by retention_profile_read.
@@ -93,6 +95,10 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [_vp] * 5 + [_i] * 6 + [_vp]
         f.restype = ctypes.c_int
+    L.gated_msr_fwd.argtypes = [_vp] * 8 + [_i] * 7 + [ctypes.c_float, ctypes.c_float, _vp, _sz, _vp]
+    L.gated_msr_fwd.restype = ctypes.c_int
+    L.gated_msr_workspace_bytes.argtypes = [_i] * 7
+    L.gated_msr_workspace_bytes.restype = _sz
     _lib = L
     return L
 
@@ -247,6 +253,47 @@ def retention_parallel_fwd(q, k, v, gamma, out=None, stream=None):
 def gated_retention_parallel_fwd(q, k, v, g, out=None, stream=None):
     """Gated parallel-form forward with per-token log-decays g[B,H,N] (fp32, <= 0)."""
     return _parallel_call("gated_retention_parallel_fwd", q, k, v, g, out, stream, True)
+
+
+def msr_workspace_bytes(B, N, D, H, dk, dv, chunk) -> int:
+    return int(lib().gated_msr_workspace_bytes(B, N, D, H, dk, dv, chunk))
+
+
+def gated_msr_fwd(x, wq, wk, wv, wg, wgt, wo, H, dk, dv, chunk=64, rope_base=10000.0, norm_eps=1e-5, out=None,
+                  workspace=None, stream=None):
+    """Gated multi-scale retention layer on x [B,N,D] (bf16): projections (weights [out, in],
+    bf16), interleaved rotary rotation of q and k, k / sqrt(dk), decay logsigmoid(gt)/16,
+    gated chunkwise retention, per-head RMSNorm, silu gate, output projection.  Returns y
+    [B,N,D] bf16."""
+    torch = _torch()
+    L = lib()
+    _require(x, "x", torch.bfloat16)
+    dev = x.device
+    if x.dim() != 3:
+        raise ValueError("x must be [B,N,D]")
+    B, N, D = x.shape
+    shapes = {"wq": (H * dk, D), "wk": (H * dk, D), "wv": (H * dv, D), "wg": (H * dv, D), "wgt": (H, D),
+              "wo": (D, H * dv)}
+    ws_ = {"wq": wq, "wk": wk, "wv": wv, "wg": wg, "wgt": wgt, "wo": wo}
+    for name, t in ws_.items():
+        _require(t, name, torch.bfloat16, dev)
+        if tuple(t.shape) != shapes[name]:
+            raise ValueError(f"{name} must be {shapes[name]}, got {tuple(t.shape)}")
+    if out is None:
+        out = torch.empty((B, N, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _require(out, "out", torch.bfloat16, dev)
+        if tuple(out.shape) != (B, N, D):
+            raise ValueError("out must be [B,N,D]")
+    need = msr_workspace_bytes(B, N, D, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = L.gated_msr_fwd(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wg), _ptr(wgt), _ptr(wo), _ptr(out), B, N, D,
+                         H, dk, dv, int(chunk), float(rope_base), float(norm_eps), _ptr(workspace), ws_bytes,
+                         _stream(stream))
+    _check(st, "gated_msr_fwd")
+    return out
 
 
 def bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:

@@ -19,7 +19,7 @@ LIB_NAME = "libretention_fwd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["api.cpp", "profile.cpp", "backward.cpp", "generic_chunk.hip", "decode.hip", "mfma_chunk.hip",
-           "bwd_kernels.hip"]
+           "bwd_kernels.hip", "msr.hip"]
 
 # Packed-fp32 instructions are disabled for all device code (the compiler would
 # otherwise form v_pk_* fp32 ops from ordinary float code).

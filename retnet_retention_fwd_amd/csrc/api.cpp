@@ -244,6 +244,42 @@ retn_status gated_retention_parallel_fwd(const void* q, const void* k, const voi
     return parallel_common(q, k, v, g, o, B, H, N, dk, dv, dtype, stream, true);
 }
 
+retn_status gated_msr_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wg,
+                          const void* wgt, const void* wo, void* y, int B, int N, int D, int H, int dk, int dv,
+                          int chunk, float rope_base, float norm_eps, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (B < 0 || N < 0 || D < 1 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return RETN_ERR_SHAPE;
+    if (!(rope_base > 1.f) || !(norm_eps >= 0.f)) return RETN_ERR_SHAPE;
+    const size_t T = static_cast<size_t>(B) * N;
+    if (T > static_cast<size_t>(INT32_MAX)) return RETN_ERR_SHAPE;
+    const retn::MsrShape sh{B, N, D, H, dk, dv, chunk, rope_base, norm_eps};
+    const retn::MsrPlan plan = retn::msr_plan(sh);
+    if (!plan.ok) return RETN_ERR_UNSUPPORTED;
+    if (T == 0) return RETN_OK;
+    if (x == nullptr || wq == nullptr || wk == nullptr || wv == nullptr || wg == nullptr || wgt == nullptr ||
+        wo == nullptr || y == nullptr)
+        return RETN_ERR_NULL;
+    const size_t hk = static_cast<size_t>(H) * dk, hv = static_cast<size_t>(H) * dv;
+    const Range ry = span(y, T * D * 2);
+    const Range in[] = {span(x, T * D * 2), span(wq, hk * D * 2), span(wk, hk * D * 2), span(wv, hv * D * 2),
+                        span(wg, hv * D * 2), span(wgt, static_cast<size_t>(H) * D * 2), span(wo, hv * D * 2)};
+    for (const Range& r : in)
+        if (overlaps(ry, r)) return RETN_ERR_ALIAS;
+    const void* const all[] = {x, wq, wk, wv, wg, wgt, wo, y};
+    for (const void* p : all)
+        if (!aligned16(p)) return RETN_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < plan.total || !aligned16(workspace)) return RETN_ERR_WORKSPACE;
+    const retn::MsrPtrs ptrs{x, wq, wk, wv, wg, wgt, wo, y};
+    const hipError_t e = retn::run_msr(sh, ptrs, plan, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RETN_OK : RETN_ERR_HIP;
+}
+
+size_t gated_msr_workspace_bytes(int B, int N, int D, int H, int dk, int dv, int chunk) {
+    if (B < 0 || N < 0 || D < 1 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return 0;
+    const retn::MsrPlan plan = retn::msr_plan(retn::MsrShape{B, N, D, H, dk, dv, chunk, 10000.f, 0.f});
+    return plan.ok ? plan.total : 0;
+}
+
 size_t retention_workspace_bytes(int B, int H, int N, int dk, int dv, int chunk, retn_dtype dtype,
                                  int gated) {
     if (!valid_dtype(dtype) || B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1 || chunk < 1 ||

@@ -107,6 +107,33 @@ struct BwdPlan {
 BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs);
 hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, void* workspace, hipStream_t st);
 
+// Matrix-core GEMM C = A W^T (bf16 A [M,K], W [N,K], contiguous; fp32 accumulation;
+// bf16 or fp32 C [M,N]); K % 64 == 0 and N % 8 == 0 (msr.hip).
+bool gemm_tn_supported(int N, int K);
+hipError_t launch_gemm_tn(const void* a, const void* w, void* c, int M, int N, int K, bool out_f32,
+                          hipStream_t stream);
+
+// Gated multi-scale retention layer (msr.hip).
+struct MsrShape {
+    int B, N, D, H, dk, dv, chunk;
+    float rope_base, norm_eps;
+};
+struct MsrPtrs {
+    const void *x, *wq, *wk, *wv, *wg, *wgt, *wo;
+    void* y;
+};
+struct MsrPlan {
+    bool ok;
+    int chunk;
+    MfmaPlan ret;   // the retention call's plan
+    // workspace: cos/sin table, q, k, v, gate projection, log decays, retention output,
+    // gated product, the retention call's workspace
+    size_t off_rot, off_q, off_k, off_v, off_gp, off_g, off_o, off_z, off_ret;
+    size_t total;   // workspace bytes
+};
+MsrPlan msr_plan(const MsrShape& s);
+hipError_t run_msr(const MsrShape& s, const MsrPtrs& x, const MsrPlan& p, void* workspace, hipStream_t st);
+
 // Optional per-kernel timing (HIP events around each launch, see profile.cpp).
 enum ProfKind { kProfMain = 0, kProfPre = 1, kProfScan = 2, kProfGeneric = 3, kProfDecode = 4, kProfCopy = 5,
                 kProfKinds = 6 };

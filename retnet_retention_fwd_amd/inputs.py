@@ -176,3 +176,17 @@ def backward_grads(seed, B, H, N, dk, dv, dtype="bf16", state=False):
     if state:
         out["grad_state_out"] = to_dtype(rng.standard_normal((B, H, dk, dv)) * 0.1, "f32")
     return out
+
+
+def msr_case(seed, B, N, D, H, dk, dv):
+    """Gated retention layer: x ~ N(0,1) [B,N,D], then the weights Wq, Wk [H*dk, D],
+    Wv, Wg [H*dv, D], Wgt [H, D] and Wo [D, H*dv] ~ N(0, 1/D) (random init of the
+    [out, in] layout), all drawn in that order from one generator and rounded to bf16.
+    Returns dict name -> (torch CPU tensor, float64)."""
+    rng = np.random.default_rng(seed)
+    s = 1.0 / np.sqrt(D)
+    out = {"x": to_dtype(rng.standard_normal((B, N, D)), "bf16")}
+    for name, shape in (("wq", (H * dk, D)), ("wk", (H * dk, D)), ("wv", (H * dv, D)), ("wg", (H * dv, D)),
+                        ("wgt", (H, D)), ("wo", (D, H * dv))):
+        out[name] = to_dtype(rng.standard_normal(shape) * s, "bf16")
+    return out

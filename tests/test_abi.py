@@ -169,6 +169,27 @@ def test_parallel_validation(L, gated):
     assert c(B=0) == OK and c(N=0) == OK          # nothing to do
 
 
+def test_msr_validation(L):
+    def c(x=FAKE, y=FAKE + 700 * MB, B=1, N=64, D=128, H=8, dk=64, dv=64, C=64, base=10000.0, eps=1e-5, ws=None,
+          wsb=0):
+        w = [FAKE + (64 + 32 * i) * MB for i in range(6)]
+        return L.gated_msr_fwd(x, *w, y, B, N, D, H, dk, dv, C, base, eps, ws, wsb, None)
+
+    assert c(D=0) == ERR_SHAPE
+    assert c(base=1.0) == ERR_SHAPE
+    assert c(eps=-1.0) == ERR_SHAPE
+    assert c(dk=48) == ERR_UNSUPPORTED          # head size off the matrix-core shapes
+    assert c(D=100) == ERR_UNSUPPORTED          # reduction not a multiple of 64
+    assert c(x=None) == ERR_NULL
+    assert c(y=FAKE + 64 * MB) == ERR_ALIAS     # y over wq
+    need = L.gated_msr_workspace_bytes(1, 64, 128, 8, 64, 64, 64)
+    assert need > 0
+    assert c() == ERR_WORKSPACE
+    assert c(ws=FAKE + 900 * MB, wsb=need - 1) == ERR_WORKSPACE
+    assert c(B=0) == OK and c(N=0) == OK
+    assert L.gated_msr_workspace_bytes(1, 64, 100, 8, 64, 64, 64) == 0
+
+
 def test_profile_read_validation(L):
     assert L.retention_profile_read(None, None, -1, None) == ERR_SHAPE
     assert L.retention_profile_read(None, None, 2, None) == ERR_NULL
