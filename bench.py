@@ -302,6 +302,34 @@ def traffic_per_launch():
     return t.get("hbm_bytes_per_launch")
 
 
+SECONDARY_NAMES = ("decode_bf16", "long_bf16_C512", "long_bf16_C256", "long_bf16_C128", "gated_bf16",
+                   "train_bf16_backward", "gated_bf16_backward", "parallel_bf16_N256", "parallel_bf16_N512",
+                   "msr_layer_bf16")
+
+
+def secondary_line(torch, R, name):
+    h = [1.0 - 2.0 ** (-5.0 - i) for i in range(8)]
+    g3 = [1.0 - 2.0 ** (-5.0 - i * 7.0 / 15.0) for i in range(16)]
+    if name == "decode_bf16":
+        return run_decode(torch, R)
+    if name.startswith("long_bf16_C"):
+        return run_chunk_workload(torch, R, "long_bf16", 1, 16, 16384, 128, 128, int(name[11:]), g3, False, 50, 5,
+                                  seed=3)
+    if name == "gated_bf16":
+        return run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None, True, 50, 5, seed=5)
+    if name == "train_bf16_backward":
+        return run_bwd_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h, False, 20, 3, seed=6)
+    if name == "gated_bf16_backward":
+        return run_bwd_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None, True, 20, 3, seed=7)
+    if name == "parallel_bf16_N256":
+        return run_parallel_workload(torch, R, 2, 16, 256, 128, 128, 50, 5, seed=8)
+    if name == "parallel_bf16_N512":
+        return run_parallel_workload(torch, R, 16, 8, 512, 128, 128, 50, 5, seed=9)
+    if name == "msr_layer_bf16":
+        return run_msr_workload(torch, R, 4, 2048, 1024, 8, 128, 128, 30, 5, seed=10)
+    raise ValueError(name)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +339,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip decode/long/gated lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    ap.add_argument("--only", choices=SECONDARY_NAMES,
+                    help="run only this secondary line and print it (for profiling one workload)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -333,26 +363,18 @@ def main():
         print(json.dumps({"calib_copy_bytes": n * 4}))
         return
 
+    if args.only:
+        print(json.dumps({args.only: secondary_line(torch, R, args.only)}))
+        return
+
     h = [1.0 - 2.0 ** (-5.0 - i) for i in range(8)]
     head = run_chunk_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h, False,
                               args.steps, args.warmup, seed=2, kernel_times=True)
 
     secondary = {}
     if not args.no_secondary:
-        secondary["decode_bf16"] = run_decode(torch, R)
-        g3 = [1.0 - 2.0 ** (-5.0 - i * 7.0 / 15.0) for i in range(16)]
-        for C in (512, 256, 128):
-            secondary[f"long_bf16_C{C}"] = run_chunk_workload(torch, R, "long_bf16", 1, 16, 16384, 128, 128, C, g3,
-                                                              False, 50, 5, seed=3)
-        secondary["gated_bf16"] = run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
-                                                     True, 50, 5, seed=5)
-        secondary["train_bf16_backward"] = run_bwd_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h,
-                                                            False, 20, 3, seed=6)
-        secondary["gated_bf16_backward"] = run_bwd_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None,
-                                                            True, 20, 3, seed=7)
-        secondary["parallel_bf16_N256"] = run_parallel_workload(torch, R, 2, 16, 256, 128, 128, 50, 5, seed=8)
-        secondary["parallel_bf16_N512"] = run_parallel_workload(torch, R, 16, 8, 512, 128, 128, 50, 5, seed=9)
-        secondary["msr_layer_bf16"] = run_msr_workload(torch, R, 4, 2048, 1024, 8, 128, 128, 30, 5, seed=10)
+        for name in SECONDARY_NAMES:
+            secondary[name] = secondary_line(torch, R, name)
 
     main_us = head["kernels"]["chunk_main"]["avg_us"]
     nb = alg_bytes(4, 8, 2048, 256, 512)

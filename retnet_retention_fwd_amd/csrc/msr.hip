@@ -42,12 +42,19 @@ struct GemmArgs {
     int seq, hd;
     const float2* rot;   // (cos, sin) of pair i of token n at rot[n * hd/2 + i]
     float scale;
+    // kRowGate: columns from n1 on come from w2 (rows [N - n1, K], same stride) and leave
+    // as logsigmoid(C) * scale in fp32 at c2[B, N - n1, seq]
+    const bf16_t* w2;
+    float* c2;
+    int n1;
 };
 
 // Epilogues: kRow stores C[M,N] row-major (bf16, or fp32 with OUTF32); kHeads stores bf16
 // at [B, heads, seq, hd] (the operator's layout); kRope also turns each adjacent column
-// pair (2i, 2i+1) of a head by the token's angle and multiplies by scale.
-enum Epi { kRow = 0, kHeads = 1, kRope = 2 };
+// pair (2i, 2i+1) of a head by the token's angle and multiplies by scale; kRowGate is
+// kRow for the columns before n1 (a multiple of the tile width) and the log-domain gate
+// for the rest.
+enum Epi { kRow = 0, kHeads = 1, kRope = 2, kRowGate = 3 };
 
 // C = A W^T with fp32 accumulation.  Requires K % 64 == 0 and N % 8 == 0; rows past M
 // or N read as zeros and are not stored.
@@ -65,10 +72,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_tn_kernel(const GemmArgs g) {
     const int m0 = (wid / tiles_n) * kGM, n0 = (wid % tiles_n) * kGN;
     const int wm = wave >> 1, wn = wave & 1;     // this wave's 64 x 64 quadrant
     const int rows_a = min(kGM, g.M - m0), rows_w = min(kGN, g.N - n0);
+    const bool second = EPI == kRowGate && n0 >= g.n1;   // a gate tile (wave-uniform)
+    const bf16_t* const wsrc = second ? g.w2 + static_cast<size_t>(n0 - g.n1) * g.ldw : g.w + static_cast<size_t>(n0) * g.ldw;
     const u32x4_t a_rs = make_rsrc(g.a + static_cast<size_t>(m0) * g.lda,
                                    static_cast<uint32_t>((rows_a - 1) * g.lda + g.K) * 2);
-    const u32x4_t w_rs = make_rsrc(g.w + static_cast<size_t>(n0) * g.ldw,
-                                   static_cast<uint32_t>((rows_w - 1) * g.ldw + g.K) * 2);
+    const u32x4_t w_rs = make_rsrc(wsrc, static_cast<uint32_t>((rows_w - 1) * g.ldw + g.K) * 2);
     // copy i of this wave fills LDS bytes [c*1024 + 16 lane, +16), c = wave + 4 i: row
     // c*8 + lane/8 and the unit whose swizzled position is lane%8
     uint32_t aoff[4], woff[4];
@@ -135,13 +143,26 @@ __global__ __launch_bounds__(kGThreads) void gemm_tn_kernel(const GemmArgs g) {
     for (int mi = 0; mi < 4; ++mi) {
         const int m = m0 + wm * 64 + mi * 16 + l16;
         if (m >= g.M) continue;
-        const int bb = EPI == kRow ? 0 : m / g.seq, tok = EPI == kRow ? 0 : m % g.seq;
+        const int bb = EPI == kRow ? 0 : m / g.seq, tok = EPI == kRow ? 0 : m % g.seq;   // (kRowGate: gate tiles)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             const int n = n0 + wn * 64 + ni * 16 + 4 * g4;
             if (n >= g.N) continue;
             f32x4_t x = acc[mi][ni];
-            if constexpr (EPI == kRow) {
+            if constexpr (EPI == kRowGate) {
+                if (second) {
+                    const int heads = g.N - g.n1;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (n + r >= g.N) break;
+                        const float y = x[r];
+                        g.c2[(static_cast<size_t>(bb) * heads + (n - g.n1 + r)) * g.seq + tok] =
+                            (fminf(y, 0.f) - log1pf(expf(-fabsf(y)))) * g.scale;
+                    }
+                } else {
+                    *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(g.c) + static_cast<size_t>(m) * g.ldc + n) = bf4(x);
+                }
+            } else if constexpr (EPI == kRow) {
                 if constexpr (OUTF32)
                     *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.c) + static_cast<size_t>(m) * g.ldc + n) = x;
                 else
@@ -304,6 +325,27 @@ hipError_t launch_gemm_tn(const void* a, const void* w, void* c, int M, int N, i
     return out_f32 ? gemm_launch<kRow, true>(g, stream) : gemm_launch<kRow, false>(g, stream);
 }
 
+namespace {
+
+// Decays for shapes whose gate projection width is not a whole number of column tiles.
+hipError_t launch_decay(const MsrPtrs& x, float* g, size_t T, const MsrShape& s, hipStream_t st) {
+    // a few workgroups per CU, each looping over tokens (the weights are staged once each)
+    const size_t wbytes = static_cast<size_t>(s.H) * s.D * 2;
+    const unsigned tblocks = static_cast<unsigned>(std::min<size_t>((T + 3) / 4, 1024));
+    static bool decay_attr = false;   // benign race: the attribute call is idempotent
+    if (!decay_attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&msr_decay_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kDecayLds);
+        decay_attr = true;
+    }
+    hipLaunchKernelGGL(msr_decay_kernel, dim3(tblocks), dim3(256), wbytes <= kDecayLds ? wbytes : 0, st,
+                       static_cast<const bf16_t*>(x.x), static_cast<const bf16_t*>(x.wgt), g, T, s.N, s.D, s.H,
+                       1.f / 16.f);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 MsrPlan msr_plan(const MsrShape& s) {
     MsrPlan p{};
     const size_t T = static_cast<size_t>(s.B) * s.N;
@@ -366,20 +408,20 @@ hipError_t run_msr(const MsrShape& s, const MsrPtrs& x, const MsrPlan& p, void* 
     gv.seq = s.N;
     gv.hd = s.dv;
     RETN_TRY((gemm_launch<kHeads, false>(gv, st)));
-    RETN_TRY((gemm_launch<kRow, false>(gemm_args(x.x, x.wg, gp, M, s.H * s.dv, s.D), st)));
-    // a few workgroups per CU, each looping over tokens (the weights are staged once each)
-    const size_t wbytes = static_cast<size_t>(s.H) * s.D * 2;
-    const unsigned tblocks = static_cast<unsigned>(std::min<size_t>((T + 3) / 4, 1024));
-    static bool decay_attr = false;   // benign race: the attribute call is idempotent
-    if (!decay_attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&msr_decay_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kDecayLds);
-        decay_attr = true;
+    if ((s.H * s.dv) % kGN == 0) {
+        // the gate projection and the decay logits in one launch: one more column tile
+        GemmArgs gg = gemm_args(x.x, x.wg, gp, M, s.H * s.dv + s.H, s.D);
+        gg.ldc = s.H * s.dv;
+        gg.n1 = s.H * s.dv;
+        gg.w2 = static_cast<const bf16_t*>(x.wgt);
+        gg.c2 = g;
+        gg.seq = s.N;
+        gg.scale = 1.f / 16.f;
+        RETN_TRY((gemm_launch<kRowGate, false>(gg, st)));
+    } else {
+        RETN_TRY((gemm_launch<kRow, false>(gemm_args(x.x, x.wg, gp, M, s.H * s.dv, s.D), st)));
+        RETN_TRY(launch_decay(x, g, T, s, st));
     }
-    hipLaunchKernelGGL(msr_decay_kernel, dim3(tblocks), dim3(256), wbytes <= kDecayLds ? wbytes : 0, st,
-                       static_cast<const bf16_t*>(x.x), static_cast<const bf16_t*>(x.wgt), g, T, s.N, s.D, s.H,
-                       1.f / 16.f);
-    RETN_TRY(hipGetLastError());
     ChunkArgs a{q, k, v, g, o, nullptr, nullptr, s.B, s.H, s.N, s.dk, s.dv, p.chunk, true, true,
                 ws + p.off_ret, p.ret.workspace_bytes};
     a.out_f32 = true;
