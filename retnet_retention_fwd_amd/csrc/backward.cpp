@@ -18,7 +18,7 @@
 //     log-decay enters only through the cumulative sums G.
 // When d_v exceeds the widest score width of the kernels (256), the dq and dk passes
 // (whose scores run over d_v) are split into column slices of d_v, read in place with a
-// row stride, and their outputs summed.
+// row stride, run as extra chains of one launch, and their outputs summed.
 
 #include "launch.h"
 
@@ -95,7 +95,7 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
     size_t fwd = 0;
     if (s.N > 0 && bh > 0) {
         if (p.kind_q == kMfma || p.kind_k == kMfma)
-            fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
+            fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H * p.parts, s.N, p.w, s.dk, s.chunk, s.gated).workspace_bytes);
         if (p.kind_v == kMfma) fwd = std::max(fwd, mfma_chunk_plan(s.B, s.H, s.N, s.dk, s.dv, s.chunk, s.gated).workspace_bytes);
     }
     size_t off = 0;
@@ -111,7 +111,6 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
     }
     p.off_fwd = take(fwd);
     p.fwd_bytes = fwd;
-    p.off_part = take(p.parts > 1 ? tokens * s.dk * es : 0);
     p.off_s0t = take(s.has_s0 ? sbytes : 0);
     p.off_dst = take(s.has_ds ? sbytes : 0);
     p.off_sfin = take(s.gated && s.has_ds ? sbytes : 0);
@@ -125,9 +124,8 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
                convert_dot_supported(s.dk, nullptr, nullptr, nullptr, nullptr);
     if (p.f32acc && ptrs != nullptr)
         p.f32acc = al16(ptrs->q) && al16(ptrs->k) && al16(ptrs->dq) && al16(ptrs->dk);
-    p.off_dqf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
-    p.off_dkf = take(p.f32acc ? tokens * s.dk * sizeof(float) : 0);
-    p.off_partf = take(p.f32acc && p.parts > 1 ? tokens * s.dk * sizeof(float) : 0);
+    // the slices of a dq or dk pass (one slice of fp32 when unsplit for the gate gradient)
+    p.off_sl = take(p.parts > 1 || p.f32acc ? p.parts * tokens * s.dk * (p.f32acc ? sizeof(float) : es) : 0);
     p.total = off;
     p.ok = true;
     return p;
@@ -138,14 +136,34 @@ namespace {
 // One forward pass on the kernel the plan chose.
 hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
                         const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
-                        int ldqk, void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32) {
+                        void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32) {
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
                 ws_bytes};
-    a.ldqk = ldqk;
     a.out_f32 = out_f32;
     a.reverse = rev;
     if (kind == kMfma) return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H, s.N, dkp, dvp, s.chunk, s.gated), st);
     return launch_generic_chunk(a, st);
+}
+
+// A pass whose scores run over d_v, split into P column slices of width w run as extra
+// chains of one matrix-core launch; slice p's output goes to o + p * tokens * dk.
+hipError_t sliced_pass(const BwdShape& s, const BwdPlan& p, int kind, const void* q, const void* k, const void* v,
+                       const float* decay, void* o, const float* state_in, float* state_out, void* ws, hipStream_t st,
+                       bool rev, bool out_f32) {
+    if (p.parts == 1)
+        return forward_pass(s, kind, q, k, v, decay, o, state_in, state_out, p.w, s.dk, ws, p.fwd_bytes, st, rev,
+                            out_f32);
+    const size_t tokens = static_cast<size_t>(s.B) * s.H * s.N;
+    ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, p.w, s.dk, s.chunk, s.bf16, s.gated, ws,
+                p.fwd_bytes};
+    a.ldqk = s.dv;
+    a.out_f32 = out_f32;
+    a.reverse = rev;
+    a.slices = p.parts;
+    a.slice_qk = p.w;
+    a.slice_o = tokens * s.dk;
+    a.slice_state = static_cast<size_t>(s.B) * s.H * p.w * s.dk;
+    return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H * p.parts, s.N, p.w, s.dk, s.chunk, s.gated), st);
 }
 
 }  // namespace
@@ -160,61 +178,63 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     }
     char* ws = static_cast<char*>(workspace);
     void* fws = ws + p.off_fwd;
-    void* part = ws + p.off_part;
     float* s0t = reinterpret_cast<float*>(ws + p.off_s0t);
     float* dst = reinterpret_cast<float*>(ws + p.off_dst);
     float* sfin = reinterpret_cast<float*>(ws + p.off_sfin);
     float* cpart = reinterpret_cast<float*>(ws + p.off_c);
     float* dG = reinterpret_cast<float*>(ws + p.off_dG);
-    const size_t es = s.bf16 ? 2 : 4;
-    const int P = p.parts, w = p.w;
+    char* sl = ws + p.off_sl;
+    const size_t tokens = bh * s.N;
+    const int P = p.parts;
     const bool has_s0 = x.state_in != nullptr, has_ds = x.dstate_out != nullptr;
+    const bool f32 = p.f32acc;
+    // where a dq or dk pass writes: straight to the output when unsplit and not kept in fp32
+    const bool direct = P == 1 && !f32;
+    const size_t slice_bytes = tokens * s.dk * (f32 ? sizeof(float) : (s.bf16 ? 2 : 4));
     hipError_t e;
 #define RETN_TRY(call)             \
     do {                           \
         e = (call);                \
         if (e != hipSuccess) return e; \
     } while (0)
+    // the slices of a pass summed into its output (fp32 slices: with the gate gradient's
+    // row dot products against xdot, added to dG with the given sign)
+    auto finish = [&](void* out, const void* xdot, float sign, bool accumulate) -> hipError_t {
+        if (direct) return hipSuccess;
+        hipError_t r;
+        if (f32) {
+            for (int pi = 2; pi < P; ++pi)
+                if ((r = launch_rows_combine(sl, sl + pi * slice_bytes, sl, bh, s.N, s.dk, s.bf16, st, true, true)) !=
+                    hipSuccess)
+                    return r;
+            return launch_convert_dot(reinterpret_cast<const float*>(sl),
+                                      P > 1 ? reinterpret_cast<const float*>(sl + slice_bytes) : nullptr, xdot, out, dG,
+                                      bh, s.N, s.dk, sign, accumulate, st);
+        }
+        if ((r = launch_rows_combine(sl, sl + slice_bytes, out, bh, s.N, s.dk, s.bf16, st)) != hipSuccess) return r;
+        for (int pi = 2; pi < P; ++pi)
+            if ((r = launch_rows_combine(out, sl + pi * slice_bytes, out, bh, s.N, s.dk, s.bf16, st)) != hipSuccess)
+                return r;
+        return hipSuccess;
+    };
 
     // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass)
     if (has_s0) RETN_TRY(launch_state_transpose(x.state_in, s0t, bh, s.dk, s.dv, P, st));
     if (has_ds) RETN_TRY(launch_state_transpose(x.dstate_out, dst, bh, s.dk, s.dv, P, st));
-    const size_t spart = bh * static_cast<size_t>(w) * s.dk;   // floats per slice block
-
-    const bool f32 = p.f32acc;
-    float* dqf = reinterpret_cast<float*>(ws + p.off_dqf);
-    float* dkf = reinterpret_cast<float*>(ws + p.off_dkf);
-    void* partf = ws + p.off_partf;
 
     // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS)
-    void* dq_acc = f32 ? static_cast<void*>(dqf) : x.dq;
-    void* slice_out = f32 ? partf : part;
-    for (int pi = 0; pi < P; ++pi) {
-        const char* dop = static_cast<const char*>(x.dout) + static_cast<size_t>(pi) * w * es;
-        const char* vp = static_cast<const char*>(x.v) + static_cast<size_t>(pi) * w * es;
-        RETN_TRY(forward_pass(s, p.kind_q, dop, vp, x.k, x.decay, pi == 0 ? dq_acc : slice_out,
-                              has_s0 ? s0t + pi * spart : nullptr, s.gated && has_ds ? sfin + pi * spart : nullptr, w,
-                              s.dk, P > 1 ? s.dv : 0, fws, p.fwd_bytes, st, false, f32));
-        if (pi > 0) RETN_TRY(launch_rows_combine(dq_acc, slice_out, dq_acc, bh, s.N, s.dk, s.bf16, st, f32, f32));
-    }
-    // (fp32 dq: the output, and q . dq for the gate gradient)
-    if (f32) RETN_TRY(launch_convert_dot(dqf, nullptr, x.q, x.dq, dG, bh, s.N, s.dk, 1.f, false, st));
+    RETN_TRY(sliced_pass(s, p, p.kind_q, x.dout, x.v, x.k, x.decay, direct ? x.dq : sl, has_s0 ? s0t : nullptr,
+                         s.gated && has_ds ? sfin : nullptr, fws, st, false, f32));
+    RETN_TRY(finish(x.dq, x.q, 1.f, false));
 
-    // ---- dv = reversed forward(k, q, dO) from dS; it ends with dS0 = lam_0 U_0
-    RETN_TRY(forward_pass(s, p.kind_v, x.k, x.q, x.dout, x.decay, x.dv, x.dstate_out, x.dstate_in, s.dk, s.dv, 0,
-                          fws, p.fwd_bytes, st, true, false));
+    // ---- dv = forward(k, q, dO) walking backwards from dS; it ends with dS0 = lam_0 U_0
+    RETN_TRY(forward_pass(s, p.kind_v, x.k, x.q, x.dout, x.decay, x.dv, x.dstate_out, x.dstate_in, s.dk, s.dv, fws,
+                          p.fwd_bytes, st, true, false));
 
-    // ---- dk = reversed forward(v, dO, q) from dS^T
-    void* dk_acc = f32 ? static_cast<void*>(dkf) : x.dk;
-    for (int pi = 0; pi < P; ++pi) {
-        const char* vp = static_cast<const char*>(x.v) + static_cast<size_t>(pi) * w * es;
-        const char* dop = static_cast<const char*>(x.dout) + static_cast<size_t>(pi) * w * es;
-        RETN_TRY(forward_pass(s, p.kind_k, vp, dop, x.q, x.decay, pi == 0 ? dk_acc : slice_out,
-                              has_ds ? dst + pi * spart : nullptr, nullptr, w, s.dk, P > 1 ? s.dv : 0, fws,
-                              p.fwd_bytes, st, true, f32));
-        if (pi > 0) RETN_TRY(launch_rows_combine(dk_acc, slice_out, dk_acc, bh, s.N, s.dk, s.bf16, st, f32, f32));
-    }
-    if (f32) RETN_TRY(launch_convert_dot(dkf, nullptr, x.k, x.dk, dG, bh, s.N, s.dk, -1.f, true, st));
+    // ---- dk = forward(v, dO, q) walking backwards from dS^T
+    RETN_TRY(sliced_pass(s, p, p.kind_k, x.v, x.dout, x.q, x.decay, direct ? x.dk : sl, has_ds ? dst : nullptr,
+                         nullptr, fws, st, true, f32));
+    RETN_TRY(finish(x.dk, x.k, -1.f, true));
 
     // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>
     if (s.gated) {

@@ -33,6 +33,13 @@ struct ChunkArgs {
     // m = 0; per head: gamma, with state_in entering divided by gamma); state_out
     // leaves multiplied by the decay of token 0.
     bool reverse = false;
+    // Matrix-core path: `slices` column slices of the score operands in one launch, each
+    // an independent chain per (b,h) (plan with H * slices heads).  Slice p reads q and k
+    // from column p * slice_qk (with the row stride ldqk), writes o from element
+    // p * slice_o, and takes state_in / state_out from float p * slice_state.
+    int slices = 1;
+    int slice_qk = 0;
+    size_t slice_o = 0, slice_state = 0;
 };
 
 struct DecodeArgs {
@@ -98,9 +105,9 @@ struct BwdPlan {
     size_t fwd_bytes;             // workspace of the largest forward pass
     bool f32acc;                  // gated bf16: the dq and dk passes write fp32 (for dg)
     int dot_splits;               // partial sums per (b,h) of <dS, S_N> (gated)
-    // workspace offsets: forward-pass workspace, a d_v slice's dq or dk, S0^T, dS^T,
-    // S_N^T, the partial sums, q.dq - k.dk, fp32 dq and dk and a slice of them
-    size_t off_fwd, off_part, off_s0t, off_dst, off_sfin, off_c, off_dG, off_dqf, off_dkf, off_partf;
+    // workspace offsets: forward-pass workspace, S0^T, dS^T, S_N^T, the partial sums of
+    // <dS, S_N>, q.dq - k.dk, and the d_v slices of a dq or dk pass
+    size_t off_fwd, off_s0t, off_dst, off_sfin, off_c, off_dG, off_sl;
     size_t total;                 // workspace bytes
 };
 // ptrs may be null (workspace query): matrix-core passes then assume aligned tensors.

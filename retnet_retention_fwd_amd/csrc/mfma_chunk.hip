@@ -246,6 +246,11 @@ struct KArgs {
     int ndvt, ndkt;          // column tiles and (pre-pass) state-row tiles per (b,h)
     int total_groups;
     int fuse_scan;           // main pass: compose the entry state from the local states
+    // column slices run as extra chains: chain c is (b,h) = c / nsl and slice c % nsl,
+    // whose q/k rows start sl_qk elements further, whose output starts sl_o elements
+    // further and whose state_in / state_out start sl_state floats further
+    int nsl, sl_qk;
+    size_t sl_o, sl_state;
 };
 
 // Main kernel (MODE = kFull) and segment-state pre-pass (MODE = kStateOnly).
@@ -312,7 +317,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int dkt = (wid / ndvt) % ndkt;
     // PAR: seg is the query block, the longest ones of a (b,h) first
     const int seg = PAR ? nseg - 1 - (wid / (ndvt * ndkt)) % nseg : (wid / (ndvt * ndkt)) % nseg_grid;
-    const int bh = wid / (ndvt * ndkt * nseg_grid);
+    const int ch = wid / (ndvt * ndkt * nseg_grid);    // chain: (b,h) and column slice
+    const int nsl = ka.nsl > 1 ? ka.nsl : 1;
+    const int slc = ch % nsl;
+    const int bh = ch / nsl;
     const int h = bh % H;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -330,10 +338,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
     // q, k rows have dk elements; this workgroup's K tile covers dims dkt*DK .. +DK
     const int ldqk = ka.ldqk, ldv = ka.ldv;
-    const size_t qk_bh = static_cast<size_t>(bh) * N * ldqk;
+    const size_t qk_bh = static_cast<size_t>(bh) * N * ldqk + static_cast<size_t>(slc) * ka.sl_qk;
     const size_t v_bh = static_cast<size_t>(bh) * N * ldv;
-    const size_t o_bh = static_cast<size_t>(bh) * N * dv;
-    const size_t s_bh = static_cast<size_t>(bh) * dk * dv;
+    const size_t o_bh = static_cast<size_t>(bh) * N * dv + slc * ka.sl_o;
+    const size_t s_bh = static_cast<size_t>(bh) * dk * dv + slc * ka.sl_state;
     const size_t s_stride_seg = static_cast<size_t>(dk) * dv;
     const int srow0 = dkt * DK;                          // first state row of this tile
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
@@ -393,14 +401,14 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
                                 for (int i = 0; i < 4; ++i) S[dt][nt][i] *= inv;
                     }
                 } else if (seg > 0) {
-                    load(ka.seg_state + static_cast<size_t>(bh) * nseg * s_stride_seg, 0.f, false);
+                    load(ka.seg_state + static_cast<size_t>(ch) * nseg * s_stride_seg, 0.f, false);
                     sg0 = 1;
                 }
                 for (int sg = sg0; nseg > 1 && sg < seg; ++sg)
-                    load(ka.seg_state + (static_cast<size_t>(bh) * nseg + sg) * s_stride_seg,
-                         exp2f(ka.seg_log2[static_cast<size_t>(bh) * nseg + sg]), true);
+                    load(ka.seg_state + (static_cast<size_t>(ch) * nseg + sg) * s_stride_seg,
+                         exp2f(ka.seg_log2[static_cast<size_t>(ch) * nseg + sg]), true);
             } else {
-                load(ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg, 0.f, false);
+                load(ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg, 0.f, false);
             }
         }
     }
@@ -1131,8 +1139,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
     if (MODE == kFull) {
         if (!PAR && seg == nseg - 1 && ka.state_out != nullptr) dst = ka.state_out + s_bh;
     } else {
-        dst = ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
-        if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(bh) * nseg + seg] = seg_l2;
+        dst = ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg + static_cast<size_t>(srow0) * dv;
+        if (dvt == 0 && dkt == 0 && tid == 0) ka.seg_log2[static_cast<size_t>(ch) * nseg + seg] = seg_l2;
     }
     if (dst != nullptr) {
         // the tile goes out through LDS as well, in whole rows of 16-byte stores
@@ -1167,7 +1175,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
 // Exclusive scan of segment states, in place:  buf[seg] <- state entering seg.
 //   S = state_in (or 0); for seg: T = buf[seg]; buf[seg] = S; S = 2^(l2[seg]) S + T.
-// in_gamma (reversed per-head walks): state_in enters divided by gamma[h].
+// in_gamma (reversed per-head walks): state_in enters divided by gamma[h].  Chains are
+// (b,h) and column slice as in the main kernel (nsl slices, state_in sl_state floats apart).
 // The last segment's local state is never computed (nor read).  One thread per state
 // element of one (b,h); blocks_per_bh blocks per (b,h).  The local states of 8
 // segments are loaded before any of them is replaced, so a batch's loads are in flight
@@ -1176,15 +1185,18 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
                                                            const float* __restrict__ seg_log2,
                                                            const float* __restrict__ state_in,
                                                            const float* __restrict__ in_gamma, int H,
-                                                           int nseg, size_t per_bh, int blocks_per_bh) {
+                                                           int nseg, size_t per_bh, int blocks_per_bh, int nsl,
+                                                           size_t sl_state) {
     constexpr int kBatch = 8;
-    const size_t bh = blockIdx.x / blocks_per_bh;
+    const size_t bh = blockIdx.x / blocks_per_bh;   // chain
+    const size_t hb = bh / nsl;                     // its (b,h)
     const int xb = blockIdx.x % blocks_per_bh;
     const float* const l2 = seg_log2 + bh * nseg;
-    const float in_scale = in_gamma != nullptr ? 1.f / in_gamma[bh % H] : 1.f;
+    const float in_scale = in_gamma != nullptr ? 1.f / in_gamma[hb % H] : 1.f;
+    const size_t in_off = (bh % nsl) * sl_state + hb * per_bh;
     for (size_t e = xb * static_cast<size_t>(blockDim.x) + threadIdx.x; e < per_bh;
          e += static_cast<size_t>(blocks_per_bh) * blockDim.x) {
-        float s = state_in != nullptr ? state_in[bh * per_bh + e] * in_scale : 0.f;
+        float s = state_in != nullptr ? state_in[in_off + e] * in_scale : 0.f;
         for (int sg0 = 0; sg0 < nseg; sg0 += kBatch) {
             float t[kBatch], f[kBatch];
 #pragma unroll
@@ -1262,7 +1274,11 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
     ka.seg_tokens = p.seg_chunks * a.chunk;
     ka.nseg = p.nseg;
     ka.fuse_scan = p.fuse_scan;
-    const int bh = a.B * a.H;
+    ka.nsl = a.slices > 1 ? a.slices : 1;
+    ka.sl_qk = a.slice_qk;
+    ka.sl_o = a.slice_o;
+    ka.sl_state = a.slice_state;
+    const int bh = a.B * a.H * ka.nsl;   // chains
     if (p.nseg > 1) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
         ka.seg_state = static_cast<float*>(a.workspace);
@@ -1276,7 +1292,7 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
             ProfScope prof(kProfScan, stream);
             hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<unsigned>(xblocks) * bh), dim3(256), 0,
                                stream, ka.seg_state, ka.seg_log2, a.state_in, REV && !GATED ? a.decay : nullptr,
-                               a.H, p.nseg, per_bh, xblocks);
+                               a.H, p.nseg, per_bh, xblocks, ka.nsl, ka.sl_state);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1390,6 +1406,7 @@ hipError_t launch_parallel_shape(const ChunkArgs& a, hipStream_t stream) {
     ka.nseg = (a.N + kBlk - 1) / kBlk;   // query blocks
     ka.ndkt = 1;
     ka.ndvt = a.dv / DVT;
+    ka.nsl = 1;
     const size_t groups = static_cast<size_t>(a.B) * a.H * ka.nseg * ka.ndvt;
     if (groups > static_cast<size_t>(INT32_MAX)) return hipErrorInvalidValue;
     ka.total_groups = static_cast<int>(groups);
