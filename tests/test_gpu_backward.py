@@ -79,6 +79,11 @@ CASES = [
     (1, 2, 70, 32, 48, 16, "f32", False, True, True),        # generic kernels
     (1, 2, 66, 32, 48, 16, "f32", True, True, True),
     (2, 1, 1, 64, 64, 64, "bf16", True, True, True),         # one token
+    # few chains and long sequences: 32 segments, so the reversed per-head walk composes
+    # its entry states in the separate scan (state_in divided by gamma there)
+    (1, 2, 2000, 128, 128, 64, "bf16", False, True, True),
+    # d_v slices as extra chains with 16 segments (scan with slice offsets), reversed dk pass
+    (1, 1, 1000, 256, 512, 64, "bf16", False, True, True),
 ]
 
 

@@ -55,6 +55,7 @@ CASES = [
     (1, 2, 512, 64, 192, "bf16", True),         # the longest gated sequence on the matrix cores
     (1, 2, 77, 256, 256, "bf16", True),
     (1, 2, 700, 128, 128, "bf16", True),        # longer gated: generic kernel
+    (1, 1, 1500, 64, 64, "bf16", False),        # per head: any length on the matrix cores
     (1, 2, 70, 32, 48, "f32", False),           # fp32: generic kernel
     (1, 2, 70, 32, 48, "f32", True),
 ]
