@@ -84,6 +84,8 @@ CASES = [
     (1, 2, 2000, 128, 128, 64, "bf16", False, True, True),
     # d_v slices as extra chains with 16 segments (scan with slice offsets), reversed dk pass
     (1, 1, 1000, 256, 512, 64, "bf16", False, True, True),
+    (1, 1, 90, 128, 1024, 64, "bf16", False, True, True),     # the widest d_v: four slices
+    (1, 1, 90, 128, 1024, 64, "bf16", True, True, True),
 ]
 
 

@@ -56,6 +56,7 @@ CASES = [
     (1, 2, 77, 256, 256, "bf16", True),
     (1, 2, 700, 128, 128, "bf16", True),        # longer gated: generic kernel
     (1, 1, 1500, 64, 64, "bf16", False),        # per head: any length on the matrix cores
+    (1, 1, 130, 128, 1024, "bf16", False),      # the widest d_v
     (1, 2, 70, 32, 48, "f32", False),           # fp32: generic kernel
     (1, 2, 70, 32, 48, "f32", True),
 ]

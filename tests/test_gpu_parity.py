@@ -100,6 +100,9 @@ SMALL = [
     (1, 2, 250, 256, 256, 48, "bf16", False, True),      # dk 256, 128-column tiles, short chunk
     (1, 2, 150, 256, 64, 64, "bf16", True, True),        # dk 256 gated, one block per chunk
     (1, 1, 170, 64, 192, 40, "bf16", False, False),
+    (1, 1, 200, 128, 1024, 64, "bf16", False, True),     # the widest d_v: eight column tiles
+    (1, 1, 150, 64, 1024, 64, "bf16", True, False),
+    (1, 1, 130, 256, 1024, 64, "bf16", False, True),     # the largest state, 256 x 1024
 ]
 
 
