@@ -32,13 +32,12 @@ hipError_t launch_rows_combine(const void* a, const void* b, void* out, size_t b
 bool convert_dot_supported(int w, const void* g, const void* g2, const void* x, const void* out);
 hipError_t launch_convert_dot(const float* g, const float* g2, const void* x, void* out, float* dG, size_t bh, int N,
                               int w, float sign, bool accumulate, hipStream_t s);
-hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts, hipStream_t s);
-int state_dot_splits(int dk, int dv);
-hipError_t launch_state_dot(const float* A, const float* B, float* part, size_t bh, int dk, int dv, int parts,
-                            hipStream_t s);
+hipError_t launch_state_transpose(const float* src0, float* dst0, const float* src1, float* dst1, size_t bh, int dk,
+                                  int dv, int parts, hipStream_t s);
 hipError_t launch_gate_rows(const void* q, const void* dq, const void* k, const void* dkk, float* dG, size_t bh,
                             int N, int dk, bool bf16, hipStream_t s);
-hipError_t launch_gate_scan(const float* dG, const float* cpart, int nc, float* dg, size_t bh, int N, hipStream_t s);
+hipError_t launch_gate_scan(const float* dG, const float* A, const float* B, int dk, int dv, int parts, float* dg,
+                            size_t bh, int N, hipStream_t s);
 
 namespace {
 
@@ -114,8 +113,6 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
     p.off_s0t = take(s.has_s0 ? sbytes : 0);
     p.off_dst = take(s.has_ds ? sbytes : 0);
     p.off_sfin = take(s.gated && s.has_ds ? sbytes : 0);
-    p.dot_splits = state_dot_splits(s.dk, s.dv);
-    p.off_c = take(s.gated && s.has_ds ? bh * p.dot_splits * sizeof(float) : 0);
     p.off_dG = take(s.gated ? tokens * sizeof(float) : 0);
     // gated bf16 on the matrix cores: dq and dk are accumulated in fp32, since the gate
     // gradient subtracts their dot products with q and k; the dot products are taken
@@ -181,7 +178,6 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     float* s0t = reinterpret_cast<float*>(ws + p.off_s0t);
     float* dst = reinterpret_cast<float*>(ws + p.off_dst);
     float* sfin = reinterpret_cast<float*>(ws + p.off_sfin);
-    float* cpart = reinterpret_cast<float*>(ws + p.off_c);
     float* dG = reinterpret_cast<float*>(ws + p.off_dG);
     char* sl = ws + p.off_sl;
     const size_t tokens = bh * s.N;
@@ -218,9 +214,9 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
         return hipSuccess;
     };
 
-    // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass)
-    if (has_s0) RETN_TRY(launch_state_transpose(x.state_in, s0t, bh, s.dk, s.dv, P, st));
-    if (has_ds) RETN_TRY(launch_state_transpose(x.dstate_out, dst, bh, s.dk, s.dv, P, st));
+    // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass), in one launch
+    RETN_TRY(launch_state_transpose(has_s0 ? x.state_in : nullptr, s0t, has_ds ? x.dstate_out : nullptr, dst, bh, s.dk,
+                                    s.dv, P, st));
 
     // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS)
     RETN_TRY(sliced_pass(s, p, p.kind_q, x.dout, x.v, x.k, x.decay, direct ? x.dq : sl, has_s0 ? s0t : nullptr,
@@ -239,8 +235,7 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>
     if (s.gated) {
         if (!f32) RETN_TRY(launch_gate_rows(x.q, x.dq, x.k, x.dk, dG, bh, s.N, s.dk, s.bf16, st));
-        if (has_ds) RETN_TRY(launch_state_dot(dst, sfin, cpart, bh, s.dk, s.dv, P, st));
-        RETN_TRY(launch_gate_scan(dG, has_ds ? cpart : nullptr, has_ds ? p.dot_splits : 0, x.dg, bh, s.N, st));
+        RETN_TRY(launch_gate_scan(dG, has_ds ? dst : nullptr, sfin, s.dk, s.dv, P, x.dg, bh, s.N, st));
     }
 #undef RETN_TRY
     return hipSuccess;

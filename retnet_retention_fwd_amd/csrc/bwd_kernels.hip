@@ -115,10 +115,15 @@ __global__ __launch_bounds__(kThreads) void convert_dot_kernel(const float* __re
 }
 
 // dst[p][bh][r][c] = src[bh][c][p*w + r]: the transposed state, split into `parts` row
-// blocks of w = dv/parts rows, each block contiguous over (b,h).  32x32 tiles through LDS.
-__global__ __launch_bounds__(kThreads) void state_transpose_kernel(const float* __restrict__ src, float* __restrict__ dst,
+// blocks of w = dv/parts rows, each block contiguous over (b,h).  32x32 tiles through LDS;
+// blockIdx.z picks one of two (src, dst) pairs (a null src skips its half).
+__global__ __launch_bounds__(kThreads) void state_transpose_kernel(const float* __restrict__ src0, float* __restrict__ dst0,
+                                                                 const float* __restrict__ src1, float* __restrict__ dst1,
                                                                  int dk, int dv, int parts, size_t bh_total) {
     __shared__ float tile[32][33];
+    const float* const src = blockIdx.z == 0 ? src0 : src1;
+    float* const dst = blockIdx.z == 0 ? dst0 : dst1;
+    if (src == nullptr) return;   // uniform over the workgroup
     const int tiles_j = (dv + 31) / 32;
     const int tj = blockIdx.x % tiles_j, tc = blockIdx.x / tiles_j;
     const int w = dv / parts;
@@ -146,36 +151,6 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Partial sums of <A[bh], B[bh]> for two states in the part-block layout of
-// state_transpose (the same layout on both sides): block (bh, s) sums its share of the
-// dk*dv products into part[bh * splits + s].
-__global__ __launch_bounds__(kThreads) void state_dot_kernel(const float* __restrict__ A, const float* __restrict__ B,
-                                                           float* __restrict__ part, int dk, int dv, int parts,
-                                                           size_t bh_total, int splits) {
-    __shared__ float sums[kThreads / 64];
-    const size_t bh = blockIdx.x / splits;
-    const int sp = blockIdx.x % splits;
-    const int w = dv / parts;
-    const int per_block = w * dk;                 // contiguous floats of one part block
-    const int total = dk * dv;
-    const int share = (total + splits - 1) / splits;
-    const int e0 = sp * share, e1 = min(total, e0 + share);
-    float acc = 0.f;
-    for (int e = e0 + static_cast<int>(threadIdx.x); e < e1; e += kThreads) {
-        const int p = e / per_block, r = e - p * per_block;
-        const size_t i = (static_cast<size_t>(p) * bh_total + bh) * per_block + r;
-        acc += A[i] * B[i];
-    }
-    acc = wave_sum(acc);
-    if ((threadIdx.x & 63) == 0) sums[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float t = 0.f;
-        for (int i = 0; i < kThreads / 64; ++i) t += sums[i];
-        part[blockIdx.x] = t;
-    }
-}
-
 // dG[bh][n] = q_n . dq_n - k_n . dk_n: one wave per token, lanes over the row (the
 // gradients in the I/O type; the matrix-core path folds this into convert_dot_kernel).
 template <typename T>
@@ -195,12 +170,15 @@ __global__ __launch_bounds__(kThreads) void gate_rows_kernel(const T* __restrict
     }
 }
 
-// dg[bh][n] = sum_{p >= n} dG[bh][p] + c[bh], c the sum of the `nc` partial dot products
-// of (b,h) (0 when nc = 0).  One workgroup per (b,h): each thread sums a contiguous run
-// of tokens; suffix sums of the run totals (within each wave by shuffles, then over the
-// waves after it) give every run its starting value.
+// dg[bh][n] = sum_{p >= n} dG[bh][p] + c[bh] with c[bh] = <A[bh], B[bh]> for two states in
+// the slice layout of state_transpose (0 when A is null).  One workgroup per (b,h): the
+// threads first sum the dk*dv products (contiguous within each slice block), then each
+// sums a contiguous run of tokens; suffix sums of the run totals (within each wave by
+// shuffles, then over the waves after it) give every run its starting value.
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __restrict__ dG,
-                                                               const float* __restrict__ cpart, int nc,
+                                                               const float* __restrict__ A,
+                                                               const float* __restrict__ B, int dk, int dv,
+                                                               int parts, size_t bh_total,
                                                                float* __restrict__ dg, int N) {
     __shared__ float wsum[kScanThreads / 64];
     __shared__ float cval;
@@ -208,6 +186,25 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __
     const float* src = dG + bh * N;
     float* dst = dg + bh * N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (A != nullptr) {
+        const int per_block = dv / parts * dk;
+        float acc = 0.f;
+        for (int p = 0; p < parts; ++p) {
+            const size_t base = (static_cast<size_t>(p) * bh_total + bh) * per_block;
+            for (int e = tid; e < per_block; e += kScanThreads) acc += A[base + e] * B[base + e];
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) wsum[wave] = acc;
+        __syncthreads();
+        if (tid == 0) {
+            float c = 0.f;
+            for (int i = 0; i < kScanThreads / 64; ++i) c += wsum[i];
+            cval = c;
+        }
+        __syncthreads();   // wsum is reused below
+    } else if (tid == 0) {
+        cval = 0.f;
+    }
     const int per = (N + kScanThreads - 1) / kScanThreads;
     const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
     float s = 0.f;
@@ -219,11 +216,6 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __
         if (lane + off < 64) incl += y;
     }
     if (lane == 0) wsum[wave] = incl;
-    if (tid == 0) {
-        float c = 0.f;
-        for (int i = 0; i < nc; ++i) c += cpart[bh * nc + i];
-        cval = c;
-    }
     __syncthreads();
     float run = cval;
     for (int w2 = kScanThreads / 64 - 1; w2 > wave; --w2) run += wsum[w2];
@@ -278,22 +270,14 @@ hipError_t launch_convert_dot(const float* g, const float* g2, const void* x, vo
     return hipGetLastError();
 }
 
-hipError_t launch_state_transpose(const float* src, float* dst, size_t bh, int dk, int dv, int parts, hipStream_t s) {
-    if (bh == 0) return hipSuccess;
+// Transposes src0 -> dst0 and src1 -> dst1 in one launch (either src may be null).
+hipError_t launch_state_transpose(const float* src0, float* dst0, const float* src1, float* dst1, size_t bh, int dk,
+                                  int dv, int parts, hipStream_t s) {
+    if (bh == 0 || (src0 == nullptr && src1 == nullptr)) return hipSuccess;
     const unsigned tiles = static_cast<unsigned>(((dk + 31) / 32) * ((dv + 31) / 32));
     const unsigned ys = static_cast<unsigned>(std::min<size_t>(bh, 65535));
-    hipLaunchKernelGGL(state_transpose_kernel, dim3(tiles, ys), dim3(kThreads), 0, s, src, dst, dk, dv, parts, bh);
-    return hipGetLastError();
-}
-
-int state_dot_splits(int dk, int dv) { return std::max(1, std::min(64, dk * dv / 2048)); }
-
-hipError_t launch_state_dot(const float* A, const float* B, float* part, size_t bh, int dk, int dv, int parts,
-                            hipStream_t s) {
-    if (bh == 0) return hipSuccess;
-    const int splits = state_dot_splits(dk, dv);
-    hipLaunchKernelGGL(state_dot_kernel, dim3(static_cast<unsigned>(bh * splits)), dim3(kThreads), 0, s, A, B, part,
-                       dk, dv, parts, bh, splits);
+    hipLaunchKernelGGL(state_transpose_kernel, dim3(tiles, ys, 2), dim3(kThreads), 0, s, src0, dst0, src1, dst1, dk, dv,
+                       parts, bh);
     return hipGetLastError();
 }
 
@@ -313,10 +297,12 @@ hipError_t launch_gate_rows(const void* q, const void* dq, const void* k, const 
     return hipGetLastError();
 }
 
-hipError_t launch_gate_scan(const float* dG, const float* cpart, int nc, float* dg, size_t bh, int N, hipStream_t s) {
+// A, B: the two states of <dS, S_N> in slice layout (A null: no such term).
+hipError_t launch_gate_scan(const float* dG, const float* A, const float* B, int dk, int dv, int parts, float* dg,
+                            size_t bh, int N, hipStream_t s) {
     if (bh == 0 || N == 0) return hipSuccess;
-    hipLaunchKernelGGL(gate_scan_kernel, dim3(static_cast<unsigned>(bh)), dim3(kScanThreads), 0, s, dG, cpart, nc, dg,
-                       N);
+    hipLaunchKernelGGL(gate_scan_kernel, dim3(static_cast<unsigned>(bh)), dim3(kScanThreads), 0, s, dG, A, B, dk, dv,
+                       parts, bh, dg, N);
     return hipGetLastError();
 }
 

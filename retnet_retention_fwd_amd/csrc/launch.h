@@ -104,10 +104,9 @@ struct BwdPlan {
     int kind_q, kind_v, kind_k;   // kernel of each pass (1 matrix-core, 2 generic)
     size_t fwd_bytes;             // workspace of the largest forward pass
     bool f32acc;                  // gated bf16: the dq and dk passes write fp32 (for dg)
-    int dot_splits;               // partial sums per (b,h) of <dS, S_N> (gated)
-    // workspace offsets: forward-pass workspace, S0^T, dS^T, S_N^T, the partial sums of
-    // <dS, S_N>, q.dq - k.dk, and the d_v slices of a dq or dk pass
-    size_t off_fwd, off_s0t, off_dst, off_sfin, off_c, off_dG, off_sl;
+    // workspace offsets: forward-pass workspace, S0^T, dS^T, S_N^T, q.dq - k.dk, and the
+    // d_v slices of a dq or dk pass
+    size_t off_fwd, off_s0t, off_dst, off_sfin, off_dG, off_sl;
     size_t total;                 // workspace bytes
 };
 // ptrs may be null (workspace query): matrix-core passes then assume aligned tensors.
