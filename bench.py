@@ -12,8 +12,8 @@ Throughput is tokens/s = B*N / step time, with inputs resident in HBM.  Several
 input sets are rotated so a step never finds its inputs in the 256 MB MALL left
 over from the previous step.
 
-Secondary lines (same JSON object, "secondary"): the recurrent decode step (batch
-128, H=32, d=128, 1024 consecutive steps, GB/s of the fp32 state stream), the
+Secondary lines (same JSON object, "secondary"): the recurrent decode step, per head and
+gated (batch 128, H=32, d=128, 1024 consecutive steps, GB/s of the fp32 state stream), the
 long-sequence workload at chunk 128/256/512, the gated workload, the backward of the
 train and gated workloads (with an initial state and a final-state gradient; GB/s
 counts Q, K, V, dO read and dQ, dK, dV written once), the parallel form on short
@@ -227,9 +227,10 @@ def run_msr_workload(torch, R, B, N, D, H, dk, dv, steps, warmup, seed):
             "us_per_step": per * 1e6, "tokens_per_s": B * N / per, "projection_TFLOPs": fl / per / 1e12}
 
 
-def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4):
+def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4, gated=False):
     """Recurrent decode: batch 128, H=32, d=128; S0 ~ N(0, 0.1^2) fp32; fresh bf16
-    q,k,v per step (pre-generated on the GPU); gamma_h = 1 - 2^(-5 - 7h/31)."""
+    q,k,v per step (pre-generated on the GPU); gamma_h = 1 - 2^(-5 - 7h/31), or (gated) a
+    fresh g = logsigmoid(x)/16 [B,H] fp32 per step."""
     B, H, d = 128, 32, 128
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
@@ -239,15 +240,22 @@ def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4):
     k = (torch.randn(steps_per_call, B, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
     v = (torch.randn(steps_per_call, B, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
     gm = torch.tensor([1.0 - 2.0 ** (-5.0 - h * 7.0 / 31.0) for h in range(H)], device="cuda")
+    gs = (torch.nn.functional.logsigmoid(torch.randn(steps_per_call, B, H, device="cuda", generator=g)) / 16
+          if gated else None)
     o = torch.empty(B, H, d, device="cuda", dtype=torch.bfloat16)
 
     def step(i):
-        R.retention_decode_step(q[i % steps_per_call], k[i % steps_per_call], v[i % steps_per_call], gm, S, out=o)
+        j = i % steps_per_call
+        if gated:
+            R.gated_retention_decode_step(q[j], k[j], v[j], gs[j], S, out=o)
+        else:
+            R.retention_decode_step(q[j], k[j], v[j], gm, S, out=o)
 
     t, _ = time_steps(step, steps_per_call, warm_calls * 16, torch)
     per = t / steps_per_call
-    nb = B * H * (2 * d * d * 4 + 4 * d * 2)
-    return {"workload": "decode_bf16", "batch": B, "H": H, "dk": d, "dv": d, "steps": steps_per_call,
+    nb = B * H * (2 * d * d * 4 + 4 * d * 2 + (4 if gated else 0))
+    return {"workload": "gated_decode_bf16" if gated else "decode_bf16", "batch": B, "H": H, "dk": d, "dv": d,
+            "steps": steps_per_call,
             "us_per_step": per * 1e6, "tokens_per_s": B / per,
             "hbm_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS}
 
@@ -302,7 +310,7 @@ def traffic_per_launch():
     return t.get("hbm_bytes_per_launch")
 
 
-SECONDARY_NAMES = ("decode_bf16", "long_bf16_C512", "long_bf16_C256", "long_bf16_C128", "gated_bf16",
+SECONDARY_NAMES = ("decode_bf16", "gated_decode_bf16", "long_bf16_C512", "long_bf16_C256", "long_bf16_C128", "gated_bf16",
                    "train_bf16_backward", "gated_bf16_backward", "parallel_bf16_N256", "parallel_bf16_N512",
                    "msr_layer_bf16")
 
@@ -312,6 +320,8 @@ def secondary_line(torch, R, name):
     g3 = [1.0 - 2.0 ** (-5.0 - i * 7.0 / 15.0) for i in range(16)]
     if name == "decode_bf16":
         return run_decode(torch, R)
+    if name == "gated_decode_bf16":
+        return run_decode(torch, R, seed=11, gated=True)
     if name.startswith("long_bf16_C"):
         return run_chunk_workload(torch, R, "long_bf16", 1, 16, 16384, 128, 128, int(name[11:]), g3, False, 50, 5,
                                   seed=3)
