@@ -39,8 +39,7 @@
  *   Domain     gamma in (0, 1] (gamma = 1 is undecayed linear attention); g finite
  *              and <= 0.  Values are not scanned on the device.
  *   Sizes      B, H, N >= 0 (B*H*N = 0 is a valid empty call: state_out, if given,
- *              receives state_in or zeros); dk, dv in [1, 256] for the generic
- *              kernels; chunk >= 1.  The bf16 matrix-core path is used when dk is
+ *              receives state_in or zeros); dk in [1, 256], dv in [1, 1024]; chunk >= 1.  The bf16 matrix-core path is used when dk is
  *              64, 128 or 256, dv is a multiple of 64 (<= 1024), chunk <= 512 and
  *              q, k, v, o are 16-byte aligned; every other shape in range runs on the
  *              generic kernels.
