@@ -40,9 +40,10 @@
  *              and <= 0.  Values are not scanned on the device.
  *   Sizes      B, H, N >= 0 (B*H*N = 0 is a valid empty call: state_out, if given,
  *              receives state_in or zeros); dk in [1, 256], dv in [1, 1024]; chunk >= 1.  The bf16 matrix-core path is used when dk is
- *              64, 128 or 256, dv is a multiple of 64 (<= 1024), chunk <= 512 and
- *              q, k, v, o are 16-byte aligned; every other shape in range runs on the
- *              generic kernels.
+ *              64, 128 or 256, dv is a multiple of 64 (<= 1024), chunk <= 512,
+ *              q, k, v, o are 16-byte aligned and one head's rows span less than
+ *              2^31 bytes ((N + 64) * max(dk, dv) * 2 < 2^31); every other shape in
+ *              range runs on the generic kernels.
  *              A ragged last chunk (N not a multiple of chunk) is computed exactly;
  *              there is no padding.
  */
@@ -178,8 +179,9 @@ retn_status gated_retention_decode_step(const void* q, const void* k, const void
  * Outputs must not overlap any input or each other (RETN_ERR_ALIAS).  Computed as
  * forward passes of the chunkwise kernels: grad_q is a forward pass over (grad_o, v, k),
  * grad_v and grad_k are forward passes that walk (k, q, grad_o) and (v, grad_o, q) from
- * the last token to the first, in place.  Shapes as the forward; for dv > 256 (bf16 only) dv must be a multiple
- * of 64 and the tensors 16-byte aligned, else RETN_ERR_UNSUPPORTED.
+ * the last token to the first, in place.  Shapes as the forward; for dv > 256 (bf16 only)
+ * dv must be a multiple of 64, the tensors 16-byte aligned and
+ * (N + 64) * max(dk, dv) * 2 < 2^31, else RETN_ERR_UNSUPPORTED.
  */
 retn_status retention_chunkwise_bwd(const void* q, const void* k, const void* v,
                                     const float* gamma, const float* state_in,
@@ -218,7 +220,7 @@ retn_status gated_retention_chunkwise_bwd(const void* q, const void* k, const vo
  *   chunk    chunk size of the retention call;  rope_base > 1;  norm_eps >= 0
  *   workspace  16-byte aligned scratch of at least gated_msr_workspace_bytes(...) bytes
  * Supported: dk in {64, 128, 256}, dv a multiple of 64 (<= 1024), D a multiple of 64,
- * chunk <= 512; else RETN_ERR_UNSUPPORTED.  The projections run on a
+ * chunk <= 512, (N + 64) * max(dk, dv) * 2 < 2^31; else RETN_ERR_UNSUPPORTED.  The projections run on a
  * bf16 matrix-core GEMM with fp32 accumulation; q, k, v, g enter the operator in bf16, the
  * retention output stays fp32 through the normalisation.
  */

@@ -73,13 +73,16 @@ int effective_chunk(int N, int chunk) { return N > 0 ? (chunk < N ? chunk : N) :
 // The matrix-core kernels move 16-byte units of q, k, v and store 8-byte units of o.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool use_mfma(int dk, int dv, int eff_chunk, retn_dtype dt) {
+// The matrix-core kernels address a head's rows with 32-bit byte offsets; longer
+// heads take the generic kernel, which indexes in 64 bits.
+bool use_mfma(int N, int dk, int dv, int eff_chunk, retn_dtype dt) {
+    if ((static_cast<size_t>(N) + 64) * std::max(dk, dv) * 2 >= (static_cast<size_t>(1) << 31)) return false;
     return retn::mfma_chunk_supported(dk, dv, eff_chunk, dt == RETN_BF16);
 }
 
 size_t workspace_for(int B, int H, int N, int dk, int dv, int chunk, retn_dtype dt, bool gated) {
     const int c = effective_chunk(N, chunk);
-    if (B <= 0 || H <= 0 || N <= 0 || !use_mfma(dk, dv, c, dt)) return 0;
+    if (B <= 0 || H <= 0 || N <= 0 || !use_mfma(N, dk, dv, c, dt)) return 0;
     return retn::mfma_chunk_plan(B, H, N, dk, dv, c, gated).workspace_bytes;
 }
 
@@ -91,7 +94,7 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
                                     dt, gated);
     if (st != RETN_OK) return st;
     const int eff_chunk = effective_chunk(N, chunk);
-    const bool mfma = use_mfma(dk, dv, eff_chunk, dt) && aligned16(q) && aligned16(k) && aligned16(v) &&
+    const bool mfma = use_mfma(N, dk, dv, eff_chunk, dt) && aligned16(q) && aligned16(k) && aligned16(v) &&
                       aligned16(o);
     // The generic kernel keeps a gated chunk's cumulative decays in LDS.
     if (!mfma && gated && eff_chunk > kGenericMaxGatedChunk) return RETN_ERR_UNSUPPORTED;

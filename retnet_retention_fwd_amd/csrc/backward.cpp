@@ -52,9 +52,10 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // Which kernel runs a forward pass of score width dkp and value width dvp.
 enum PassKind { kNone = 0, kMfma = 1, kGeneric = 2 };
 
-// rev_ok: the matrix-core kernels' reversed walk (signed 32-bit row offsets) fits.
-PassKind pass_kind(const BwdShape& s, int dkp, int dvp, bool strided, bool aligned, bool rev, bool rev_ok) {
-    if (s.bf16 && mfma_chunk_supported(dkp, dvp, s.chunk, true) && aligned && (!rev || rev_ok)) return kMfma;
+// rows_ok: a head's rows fit the matrix-core kernels' 32-bit byte offsets (signed for
+// the reversed walks).
+PassKind pass_kind(const BwdShape& s, int dkp, int dvp, bool strided, bool aligned, bool rows_ok) {
+    if (s.bf16 && mfma_chunk_supported(dkp, dvp, s.chunk, true) && aligned && rows_ok) return kMfma;
     if (strided) return kNone;
     if (dkp > kGenericMaxDk) return kNone;
     if (s.gated && s.chunk > kGenericMaxGatedChunk) return kNone;
@@ -86,10 +87,10 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
         const void* const all[] = {ptrs->q, ptrs->k, ptrs->v, ptrs->dout, ptrs->dq, ptrs->dk, ptrs->dv};
         for (const void* x : all) aligned = aligned && al16(x);
     }
-    const bool rev_ok = (static_cast<size_t>(s.N) + 64) * std::max(s.dk, s.dv) * 2 < (static_cast<size_t>(1) << 31);
-    p.kind_q = pass_kind(s, p.w, s.dk, strided, aligned, false, rev_ok);   // dq: scores over d_v
-    p.kind_v = pass_kind(s, s.dk, s.dv, false, aligned, true, rev_ok);     // dv: scores over d_k
-    p.kind_k = pass_kind(s, p.w, s.dk, strided, aligned, true, rev_ok);    // dk: scores over d_v
+    const bool rows_ok = (static_cast<size_t>(s.N) + 64) * std::max(s.dk, s.dv) * 2 < (static_cast<size_t>(1) << 31);
+    p.kind_q = pass_kind(s, p.w, s.dk, strided, aligned, rows_ok);   // dq: scores over d_v
+    p.kind_v = pass_kind(s, s.dk, s.dv, false, aligned, rows_ok);    // dv: scores over d_k
+    p.kind_k = pass_kind(s, p.w, s.dk, strided, aligned, rows_ok);   // dk: scores over d_v
     if (p.kind_q == kNone || p.kind_v == kNone || p.kind_k == kNone) return p;
     size_t fwd = 0;
     if (s.N > 0 && bh > 0) {

@@ -359,7 +359,9 @@ MsrPlan msr_plan(const MsrShape& s) {
     p.chunk = s.N > 0 ? std::min(s.chunk, s.N) : 1;
     p.ok = s.B >= 0 && s.N >= 0 && s.D > 0 && s.H > 0 && gemm_tn_supported(s.H * s.dk, s.D) &&
            gemm_tn_supported(s.H * s.dv, s.D) && gemm_tn_supported(s.D, s.H * s.dv) &&
-           mfma_chunk_supported(s.dk, s.dv, p.chunk, true) && s.dk % 4 == 0;
+           mfma_chunk_supported(s.dk, s.dv, p.chunk, true) && s.dk % 4 == 0 &&
+           // the retention step addresses a head's rows with 32-bit byte offsets
+           (static_cast<size_t>(s.N) + 64) * std::max(s.dk, s.dv) * 2 < (static_cast<size_t>(1) << 31);
     if (!p.ok || T == 0) return p;
     p.off_rot = take(static_cast<size_t>(s.N) * (s.dk / 2) * 8);
     p.off_q = take(qk * 2);

@@ -107,6 +107,22 @@ def test_workspace_query(L):
     assert L.retention_workspace_bytes(-1, 2, 64, 16, 16, 16, 0, 0) == 0
 
 
+def test_long_heads_leave_the_matrix_core_path(L):
+    # The matrix-core kernels address one head's rows with 32-bit byte offsets: a head
+    # whose rows span 2^31 bytes or more runs on the generic kernel (no workspace), its
+    # backward with d_v > 256 and the gated layer are reported unsupported.
+    n_fit = (1 << 30) // 1024 - 64 - 1          # (N + 64) * 1024 * 2 < 2^31
+    n_over = n_fit + 1
+    assert L.retention_workspace_bytes(1, 1, n_fit, 256, 1024, 64, 1, 0) > 0
+    assert L.retention_workspace_bytes(1, 1, n_over, 256, 1024, 64, 1, 0) == 0
+    assert L.retention_workspace_bytes(1, 1, n_over, 256, 1024, 64, 1, 1) == 0
+    assert L.retention_bwd_workspace_bytes(1, 1, n_fit, 256, 1024, 64, 1, 0) > 0
+    assert L.retention_bwd_workspace_bytes(1, 1, n_over, 256, 1024, 64, 1, 0) == 0
+    n_fit = (1 << 30) // 128 - 64 - 1
+    assert L.gated_msr_workspace_bytes(1, n_fit, 128, 1, 128, 128, 64) > 0
+    assert L.gated_msr_workspace_bytes(1, n_fit + 1, 128, 1, 128, 128, 64) == 0
+
+
 def bwd(L, gated=False, q=FAKE, k=FAKE + 64 * MB, v=FAKE + 128 * MB, d=FAKE + 192 * MB, si=None,
         go=FAKE + 256 * MB, gso=None, gq=FAKE + 320 * MB, gk=FAKE + 384 * MB, gv=FAKE + 448 * MB,
         gg=FAKE + 512 * MB, gsi=None, B=1, H=2, N=64, dk=16, dv=16, C=16, dt=0, ws=None, wsb=0):
