@@ -145,6 +145,52 @@ __global__ __launch_bounds__(kThreads) void state_transpose_kernel(const float* 
     }
 }
 
+// The same transpose in 64x64 tiles moved as 16-byte vectors (dk and dv multiples of 4,
+// so that every vector stays inside one row and is aligned): thread t loads 4-float
+// pieces of rows t/16 + 16i and stores 4-float pieces of output rows t/16 + 16i.  The
+// LDS tile has a row stride of 65 floats, so both the row writes and the column reads
+// of a wave fall in 64 distinct banks.
+__global__ __launch_bounds__(kThreads) void state_transpose4_kernel(const float* __restrict__ src0,
+                                                                  float* __restrict__ dst0,
+                                                                  const float* __restrict__ src1,
+                                                                  float* __restrict__ dst1, int dk, int dv, int parts,
+                                                                  size_t bh_total) {
+    __shared__ float tile[64 * 65];
+    const float* const src = blockIdx.z == 0 ? src0 : src1;
+    float* const dst = blockIdx.z == 0 ? dst0 : dst1;
+    if (src == nullptr) return;   // uniform over the workgroup
+    const int tiles_j = (dv + 63) / 64;
+    const int tj = blockIdx.x % tiles_j, tc = blockIdx.x / tiles_j;
+    const int w = dv / parts;
+    const int u = threadIdx.x & 15, y0 = threadIdx.x >> 4;   // 16 x 16
+    for (size_t bh = blockIdx.y; bh < bh_total; bh += gridDim.y) {   // block-uniform loop
+        const float* const sb = src + bh * dk * dv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int y = y0 + 16 * i, c = tc * 64 + y, j = tj * 64 + 4 * u;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < dk && j < dv) x = *reinterpret_cast<const float4*>(sb + static_cast<size_t>(c) * dv + j);
+            float* const t = tile + y * 65 + 4 * u;
+            t[0] = x.x;
+            t[1] = x.y;
+            t[2] = x.z;
+            t[3] = x.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int y = y0 + 16 * i, j = tj * 64 + y, c = tc * 64 + 4 * u;
+            if (c < dk && j < dv) {
+                const float* const t = tile + (4 * u) * 65 + y;
+                const float4 x = make_float4(t[0], t[65], t[130], t[195]);
+                const int p = j / w, r = j - p * w;
+                *reinterpret_cast<float4*>(dst + ((static_cast<size_t>(p) * bh_total + bh) * w + r) * dk + c) = x;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -274,8 +320,16 @@ hipError_t launch_convert_dot(const float* g, const float* g2, const void* x, vo
 hipError_t launch_state_transpose(const float* src0, float* dst0, const float* src1, float* dst1, size_t bh, int dk,
                                   int dv, int parts, hipStream_t s) {
     if (bh == 0 || (src0 == nullptr && src1 == nullptr)) return hipSuccess;
-    const unsigned tiles = static_cast<unsigned>(((dk + 31) / 32) * ((dv + 31) / 32));
     const unsigned ys = static_cast<unsigned>(std::min<size_t>(bh, 65535));
+    const bool vec = dk % 4 == 0 && dv % 4 == 0 && (src0 == nullptr || (aligned16(src0) && aligned16(dst0))) &&
+                     (src1 == nullptr || (aligned16(src1) && aligned16(dst1)));
+    if (vec) {
+        const unsigned tiles4 = static_cast<unsigned>(((dk + 63) / 64) * ((dv + 63) / 64));
+        hipLaunchKernelGGL(state_transpose4_kernel, dim3(tiles4, ys, 2), dim3(kThreads), 0, s, src0, dst0, src1, dst1,
+                           dk, dv, parts, bh);
+        return hipGetLastError();
+    }
+    const unsigned tiles = static_cast<unsigned>(((dk + 31) / 32) * ((dv + 31) / 32));
     hipLaunchKernelGGL(state_transpose_kernel, dim3(tiles, ys, 2), dim3(kThreads), 0, s, src0, dst0, src1, dst1, dk, dv,
                        parts, bh);
     return hipGetLastError();

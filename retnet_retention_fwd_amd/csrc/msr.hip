@@ -33,6 +33,26 @@ constexpr int kGTile = kGM * kGK * 2;            // bytes of one operand tile (1
 // bank cycle) cover distinct banks.
 __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
+// Epilogues: kRow stores C[M,N] row-major (bf16, or fp32 with OUTF32); kHeads stores bf16
+// at [B, heads, seq, hd] (the operator's layout); kRope also turns each adjacent column
+// pair (2i, 2i+1) of a head by the token's angle and multiplies by scale; kGateLog stores
+// logsigmoid(C) * scale in fp32 at [B, columns, seq] (the operator's decay layout).
+// kGroups: the columns are the concatenation of up to kMaxGroups projections of the same
+// A, each with its own weight, output and epilogue (one launch for all of them).
+enum Epi { kRow = 0, kHeads = 1, kRope = 2, kGateLog = 3, kGroups = 4 };
+constexpr int kMaxGroups = 5;
+
+// One projection of a fused launch: columns [previous group's end, end) of the launch.
+// Every group but the last spans a whole number of column tiles.
+struct GemmGroup {
+    const bf16_t* w;   // [columns, K] weight rows, stride ldw
+    void* c;           // output (layout of `kind`; kRow rows have `columns` elements)
+    int end;           // exclusive end column within the launch
+    int kind;          // kRow, kHeads, kRope or kGateLog
+    int hd;            // head width (kHeads, kRope)
+    float scale;       // kRope, kGateLog
+};
+
 struct GemmArgs {
     const bf16_t* a;   // [M, K], row stride lda
     const bf16_t* w;   // [N, K], row stride ldw
@@ -42,22 +62,12 @@ struct GemmArgs {
     int seq, hd;
     const float2* rot;   // (cos, sin) of pair i of token n at rot[n * hd/2 + i]
     float scale;
-    // kRowGate: columns from n1 on come from w2 (rows [N - n1, K], same stride) and leave
-    // as logsigmoid(C) * scale in fp32 at c2[B, N - n1, seq]
-    const bf16_t* w2;
-    float* c2;
-    int n1;
+    int ngroups;         // kGroups: the projections (N = grp[ngroups - 1].end)
+    GemmGroup grp[kMaxGroups];
 };
 
-// Epilogues: kRow stores C[M,N] row-major (bf16, or fp32 with OUTF32); kHeads stores bf16
-// at [B, heads, seq, hd] (the operator's layout); kRope also turns each adjacent column
-// pair (2i, 2i+1) of a head by the token's angle and multiplies by scale; kRowGate is
-// kRow for the columns before n1 (a multiple of the tile width) and the log-domain gate
-// for the rest.
-enum Epi { kRow = 0, kHeads = 1, kRope = 2, kRowGate = 3 };
-
-// C = A W^T with fp32 accumulation.  Requires K % 64 == 0 and N % 8 == 0; rows past M
-// or N read as zeros and are not stored.
+// C = A W^T with fp32 accumulation.  Requires K % 64 == 0 and N % 8 == 0 (kGroups: every
+// group's width); rows past M or N read as zeros and are not stored.
 template <int EPI, bool OUTF32>
 __global__ __launch_bounds__(kGThreads) void gemm_tn_kernel(const GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kGTile];
@@ -71,9 +81,29 @@ __global__ __launch_bounds__(kGThreads) void gemm_tn_kernel(const GemmArgs g) {
     if (total % 8 == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
     const int m0 = (wid / tiles_n) * kGM, n0 = (wid % tiles_n) * kGN;
     const int wm = wave >> 1, wn = wave & 1;     // this wave's 64 x 64 quadrant
-    const int rows_a = min(kGM, g.M - m0), rows_w = min(kGN, g.N - n0);
-    const bool second = EPI == kRowGate && n0 >= g.n1;   // a gate tile (wave-uniform)
-    const bf16_t* const wsrc = second ? g.w2 + static_cast<size_t>(n0 - g.n1) * g.ldw : g.w + static_cast<size_t>(n0) * g.ldw;
+    // this tile's projection (workgroup-uniform): weight rows, output and epilogue
+    const bf16_t* wbase = g.w;
+    void* cout = g.c;
+    int nstart = 0, nend = g.N, kind = EPI == kGroups ? kRow : EPI, hd = g.hd, ldc = g.ldc;
+    float scale = g.scale;
+    if constexpr (EPI == kGroups) {
+        int gi = 0;
+#pragma unroll
+        for (int i = 0; i + 1 < kMaxGroups; ++i)
+            if (i + 1 < g.ngroups && n0 >= g.grp[i].end) gi = i + 1;
+        nstart = gi > 0 ? g.grp[gi - 1].end : 0;
+        nend = g.grp[gi].end;
+        wbase = g.grp[gi].w;
+        cout = g.grp[gi].c;
+        kind = g.grp[gi].kind;
+        hd = g.grp[gi].hd;
+        scale = g.grp[gi].scale;
+        ldc = nend - nstart;
+    }
+    const int rows_a = min(kGM, g.M - m0), rows_w = min(kGN, nend - n0);
+    // columns of this wave's quadrant that exist (a narrow last group computes only those)
+    const int wcols = rows_w - wn * 64;
+    const bf16_t* const wsrc = wbase + static_cast<size_t>(n0 - nstart) * g.ldw;
     const u32x4_t a_rs = make_rsrc(g.a + static_cast<size_t>(m0) * g.lda,
                                    static_cast<uint32_t>((rows_a - 1) * g.lda + g.K) * 2);
     const u32x4_t w_rs = make_rsrc(wsrc, static_cast<uint32_t>((rows_w - 1) * g.ldw + g.K) * 2);
@@ -122,63 +152,79 @@ __global__ __launch_bounds__(kGThreads) void gemm_tn_kernel(const GemmArgs g) {
         lds_barrier();
         if (kt + 1 < nk) issue(kt + 1, st ^ 1);
         const uint32_t base = lds0 + st * 2 * kGTile;
+        if (wcols >= 64) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u16x8_t af[4], wf[4];
+            for (int ks = 0; ks < 2; ++ks) {
+                u16x8_t af[4], wf[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int unit = ks * 4 + g4;
-                af[t] = lds16a(base + ra[t] + ((unit ^ sa[t]) << 4));
-                wf[t] = lds16a(base + rw[t] + ((unit ^ sw[t]) << 4));
+                for (int t = 0; t < 4; ++t) {
+                    const int unit = ks * 4 + g4;
+                    af[t] = lds16a(base + ra[t] + ((unit ^ sa[t]) << 4));
+                    wf[t] = lds16a(base + rw[t] + ((unit ^ sw[t]) << 4));
+                }
+                // lane (g, l%16) of acc[mi][ni] gets C[row l%16 of A tile mi][columns
+                // 4g..4g+3 of W tile ni]
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16(wf[ni], af[mi], acc[mi][ni]);
             }
-            // lane (g, l%16) of acc[mi][ni] gets C[row l%16 of A tile mi][columns 4g..4g+3
-            // of W tile ni]
+        } else if (wcols > 0) {
+            // a narrow tile: only the 16-column slices that hold columns
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int ks = 0; ks < 2; ++ks) {
+                const int unit = ks * 4 + g4;
+                u16x8_t af[4];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16(wf[ni], af[mi], acc[mi][ni]);
+                for (int t = 0; t < 4; ++t) af[t] = lds16a(base + ra[t] + ((unit ^ sa[t]) << 4));
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    if (ni * 16 >= wcols) break;
+                    const u16x8_t wf = lds16a(base + rw[ni] + ((unit ^ sw[ni]) << 4));
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = mfma16(wf, af[mi], acc[mi][ni]);
+                }
+            }
         }
     }
+    if (wcols <= 0) return;   // after the loop: every wave took part in its barriers
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int m = m0 + wm * 64 + mi * 16 + l16;
         if (m >= g.M) continue;
-        const int bb = EPI == kRow ? 0 : m / g.seq, tok = EPI == kRow ? 0 : m % g.seq;   // (kRowGate: gate tiles)
+        const int bb = m / g.seq, tok = m % g.seq;   // head layouts
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             const int n = n0 + wn * 64 + ni * 16 + 4 * g4;
-            if (n >= g.N) continue;
+            if (n >= nend) continue;
+            const int nl = n - nstart;   // column within this projection
             f32x4_t x = acc[mi][ni];
-            if constexpr (EPI == kRowGate) {
-                if (second) {
-                    const int heads = g.N - g.n1;
+            if (kind == kGateLog) {
+                const int heads = nend - nstart;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (n + r >= g.N) break;
-                        const float y = x[r];
-                        g.c2[(static_cast<size_t>(bb) * heads + (n - g.n1 + r)) * g.seq + tok] =
-                            (fminf(y, 0.f) - log1pf(expf(-fabsf(y)))) * g.scale;
-                    }
-                } else {
-                    *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(g.c) + static_cast<size_t>(m) * g.ldc + n) = bf4(x);
+                for (int r = 0; r < 4; ++r) {
+                    if (nl + r >= heads) break;
+                    const float y = x[r];
+                    static_cast<float*>(cout)[(static_cast<size_t>(bb) * heads + (nl + r)) * g.seq + tok] =
+                        (fminf(y, 0.f) - log1pf(expf(-fabsf(y)))) * scale;
                 }
-            } else if constexpr (EPI == kRow) {
+            } else if (kind == kRow) {
                 if constexpr (OUTF32)
-                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.c) + static_cast<size_t>(m) * g.ldc + n) = x;
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(cout) + static_cast<size_t>(m) * ldc + nl) = x;
                 else
-                    *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(g.c) + static_cast<size_t>(m) * g.ldc + n) = bf4(x);
+                    *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(cout) + static_cast<size_t>(m) * ldc + nl) = bf4(x);
             } else {
-                const int head = n / g.hd, j = n % g.hd;   // the four columns stay in one head
-                if constexpr (EPI == kRope) {
-                    const float2 r0 = g.rot[static_cast<size_t>(tok) * (g.hd / 2) + j / 2];
-                    const float2 r1 = g.rot[static_cast<size_t>(tok) * (g.hd / 2) + j / 2 + 1];
+                const int head = nl / hd, j = nl % hd;   // the four columns stay in one head
+                if (kind == kRope) {
+                    const float2 r0 = g.rot[static_cast<size_t>(tok) * (hd / 2) + j / 2];
+                    const float2 r1 = g.rot[static_cast<size_t>(tok) * (hd / 2) + j / 2 + 1];
                     const f32x4_t y = {x[0] * r0.x - x[1] * r0.y, x[0] * r0.y + x[1] * r0.x,
                                        x[2] * r1.x - x[3] * r1.y, x[2] * r1.y + x[3] * r1.x};
-                    x = y * g.scale;
+                    x = y * scale;
                 }
-                const int heads = g.N / g.hd;
-                *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(g.c) +
-                                            ((static_cast<size_t>(bb) * heads + head) * g.seq + tok) * g.hd + j) = bf4(x);
+                const int heads = (nend - nstart) / hd;
+                *reinterpret_cast<u16x4_t*>(static_cast<bf16_t*>(cout) +
+                                            ((static_cast<size_t>(bb) * heads + head) * g.seq + tok) * hd + j) = bf4(x);
             }
         }
     }
@@ -396,32 +442,38 @@ hipError_t run_msr(const MsrShape& s, const MsrPtrs& x, const MsrPlan& p, void* 
     hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, st, rot, s.N,
                        s.dk / 2, log(static_cast<double>(s.rope_base)));
     RETN_TRY(hipGetLastError());
-    GemmArgs gq = gemm_args(x.x, x.wq, q, M, s.H * s.dk, s.D);
-    gq.seq = s.N;
-    gq.hd = s.dk;
-    gq.rot = rot;
-    RETN_TRY((gemm_launch<kRope, false>(gq, st)));
-    GemmArgs gk = gq;
-    gk.w = static_cast<const bf16_t*>(x.wk);
-    gk.c = k;
-    gk.scale = 1.f / sqrtf(static_cast<float>(s.dk));
-    RETN_TRY((gemm_launch<kRope, false>(gk, st)));
-    GemmArgs gv = gemm_args(x.x, x.wv, v, M, s.H * s.dv, s.D);
-    gv.seq = s.N;
-    gv.hd = s.dv;
-    RETN_TRY((gemm_launch<kHeads, false>(gv, st)));
-    if ((s.H * s.dv) % kGN == 0) {
-        // the gate projection and the decay logits in one launch: one more column tile
-        GemmArgs gg = gemm_args(x.x, x.wg, gp, M, s.H * s.dv + s.H, s.D);
-        gg.ldc = s.H * s.dv;
-        gg.n1 = s.H * s.dv;
-        gg.w2 = static_cast<const bf16_t*>(x.wgt);
-        gg.c2 = g;
-        gg.seq = s.N;
-        gg.scale = 1.f / 16.f;
-        RETN_TRY((gemm_launch<kRowGate, false>(gg, st)));
+    const int nq = s.H * s.dk, nv = s.H * s.dv;
+    const float kscale = 1.f / sqrtf(static_cast<float>(s.dk));
+    if (nq % kGN == 0 && nv % kGN == 0) {
+        // the q, k, v and gate projections and the decay logits in one launch: all five
+        // read x, and one launch has one tail instead of five (the decay group's tile
+        // computes only its H columns)
+        GemmArgs ga = gemm_args(x.x, x.wq, q, M, 2 * nq + 2 * nv + s.H, s.D);
+        ga.seq = s.N;
+        ga.rot = rot;
+        ga.ngroups = 5;
+        ga.grp[0] = GemmGroup{static_cast<const bf16_t*>(x.wq), q, nq, kRope, s.dk, 1.f};
+        ga.grp[1] = GemmGroup{static_cast<const bf16_t*>(x.wk), k, 2 * nq, kRope, s.dk, kscale};
+        ga.grp[2] = GemmGroup{static_cast<const bf16_t*>(x.wv), v, 2 * nq + nv, kHeads, s.dv, 1.f};
+        ga.grp[3] = GemmGroup{static_cast<const bf16_t*>(x.wg), gp, 2 * nq + 2 * nv, kRow, 1, 1.f};
+        ga.grp[4] = GemmGroup{static_cast<const bf16_t*>(x.wgt), g, 2 * nq + 2 * nv + s.H, kGateLog, 1, 1.f / 16.f};
+        RETN_TRY((gemm_launch<kGroups, false>(ga, st)));
     } else {
-        RETN_TRY((gemm_launch<kRow, false>(gemm_args(x.x, x.wg, gp, M, s.H * s.dv, s.D), st)));
+        GemmArgs gq = gemm_args(x.x, x.wq, q, M, nq, s.D);
+        gq.seq = s.N;
+        gq.hd = s.dk;
+        gq.rot = rot;
+        RETN_TRY((gemm_launch<kRope, false>(gq, st)));
+        GemmArgs gk = gq;
+        gk.w = static_cast<const bf16_t*>(x.wk);
+        gk.c = k;
+        gk.scale = kscale;
+        RETN_TRY((gemm_launch<kRope, false>(gk, st)));
+        GemmArgs gv = gemm_args(x.x, x.wv, v, M, nv, s.D);
+        gv.seq = s.N;
+        gv.hd = s.dv;
+        RETN_TRY((gemm_launch<kHeads, false>(gv, st)));
+        RETN_TRY((gemm_launch<kRow, false>(gemm_args(x.x, x.wg, gp, M, nv, s.D), st)));
         RETN_TRY(launch_decay(x, g, T, s, st));
     }
     ChunkArgs a{q, k, v, g, o, nullptr, nullptr, s.B, s.H, s.N, s.dk, s.dv, p.chunk, true, true,

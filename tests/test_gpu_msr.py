@@ -65,6 +65,13 @@ CASES = [
     (1, 200, 256, 8, 128, 128, 128),
     (1, 1, 64, 8, 64, 64, 64),
     (1, 90, 128, 3, 64, 64, 64),             # a head count off the multiples of 8
+    # one launch for all projections with a narrow decay group (6 and 2 columns)
+    (1, 100, 128, 6, 64, 64, 64),
+    (2, 50, 64, 2, 64, 128, 64),
+    # more projection tiles than the device holds at once: ragged rows, one and three
+    # reduction steps
+    (1, 1900, 64, 8, 128, 128, 64),
+    (1, 1900, 192, 8, 128, 128, 64),
 ]
 
 
