@@ -354,7 +354,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the operator on a single MI355X and has no "
+        print("bench.py measures one GPU: the operator runs on a single MI355X and there is no "
               "multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
