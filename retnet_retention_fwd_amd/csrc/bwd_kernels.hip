@@ -220,7 +220,12 @@ __global__ __launch_bounds__(kThreads) void gate_rows_kernel(const T* __restrict
 // the slice layout of state_transpose (0 when A is null).  One workgroup per (b,h): the
 // threads first sum the dk*dv products (contiguous within each slice block), then each
 // sums a contiguous run of tokens; suffix sums of the run totals (within each wave by
-// shuffles, then over the waves after it) give every run its starting value.
+// shuffles, then over the waves after it) give every run its starting value.  With few
+// workgroups the kernel is bound by memory latency, so every thread issues its loads
+// together: the products four 16-byte pairs at a time, and runs of up to kScanRun tokens
+// held in registers.
+constexpr int kScanRun = 16;
+
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __restrict__ dG,
                                                                const float* __restrict__ A,
                                                                const float* __restrict__ B, int dk, int dv,
@@ -234,10 +239,21 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (A != nullptr) {
         const int per_block = dv / parts * dk;
+        const bool vec = per_block % 4 == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15u) == 0;
         float acc = 0.f;
         for (int p = 0; p < parts; ++p) {
             const size_t base = (static_cast<size_t>(p) * bh_total + bh) * per_block;
-            for (int e = tid; e < per_block; e += kScanThreads) acc += A[base + e] * B[base + e];
+            if (vec) {
+                const float4* a4 = reinterpret_cast<const float4*>(A + base);
+                const float4* b4 = reinterpret_cast<const float4*>(B + base);
+#pragma unroll 4
+                for (int e = tid; e < per_block / 4; e += kScanThreads) {
+                    const float4 x = a4[e], y = b4[e];
+                    acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+                }
+            } else {
+                for (int e = tid; e < per_block; e += kScanThreads) acc += A[base + e] * B[base + e];
+            }
         }
         acc = wave_sum(acc);
         if (lane == 0) wsum[wave] = acc;
@@ -251,10 +267,19 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __
     } else if (tid == 0) {
         cval = 0.f;
     }
-    const int per = (N + kScanThreads - 1) / kScanThreads;
+    const int per = (N + kScanThreads - 1) / kScanThreads;   // uniform
     const int n0 = min(N, tid * per), n1 = min(N, n0 + per);
+    const bool regs = per <= kScanRun;
+    float val[kScanRun];
     float s = 0.f;
-    for (int n = n0; n < n1; ++n) s += src[n];
+    if (regs) {
+#pragma unroll
+        for (int i = 0; i < kScanRun; ++i) val[i] = n0 + i < n1 ? src[n0 + i] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kScanRun; ++i) s += val[i];
+    } else {
+        for (int n = n0; n < n1; ++n) s += src[n];
+    }
     float incl = s;   // sum over lanes lane..63 of this wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -266,9 +291,19 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(const float* __
     float run = cval;
     for (int w2 = kScanThreads / 64 - 1; w2 > wave; --w2) run += wsum[w2];
     run += incl - s;   // the lanes after this one
-    for (int n = n1 - 1; n >= n0; --n) {
-        run += src[n];
-        dst[n] = run;
+    if (regs) {
+#pragma unroll
+        for (int i = kScanRun - 1; i >= 0; --i) {
+            if (n0 + i < n1) {
+                run += val[i];
+                dst[n0 + i] = run;
+            }
+        }
+    } else {
+        for (int n = n1 - 1; n >= n0; --n) {
+            run += src[n];
+            dst[n] = run;
+        }
     }
 }
 

@@ -80,6 +80,7 @@ CASES = [
     (1, 2, 66, 32, 48, 16, "f32", True, True, True),
     (1, 1, 50, 96, 80, 32, "f32", False, True, True),       # state transposes: partial 64x64 tiles
     (1, 2, 45, 21, 30, 16, "f32", True, True, True),        # sizes off multiples of 4: scalar transposes
+    (1, 1, 17000, 16, 16, 64, "f32", True, False, True),    # gate scan: more than 16 tokens a thread
     (2, 1, 1, 64, 64, 64, "bf16", True, True, True),         # one token
     # few chains and long sequences: 32 segments, so the reversed per-head walk composes
     # its entry states in the separate scan (state_in divided by gamma there)
