@@ -246,11 +246,20 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ro
 // z[t, h*dv + j] = silu(gp[t, h*dv + j]) * o[b,h,n,j] / sqrt(mean_j o[b,h,n,:]^2 + eps).
 // A (token, head) row is spread over LPR = min(64, dv/8) adjacent lanes, eight elements
 // per lane and step; a wave takes 64/LPR rows (dv a multiple of 64).
+// Lanes that share one row of d_v elements, eight elements a lane per pass: the largest
+// power of two up to 64 and d_v / 8, so that a row's lanes form an aligned group that a
+// butterfly of shuffles reduces.
+__host__ __device__ inline int gate_lanes_per_row(int dv) {
+    int l = 1;
+    while (2 * l <= 64 && 2 * l <= dv / 8) l *= 2;
+    return l;
+}
+
 __global__ __launch_bounds__(256) void msr_gate_kernel(const float* __restrict__ o, const bf16_t* __restrict__ gp,
                                                      bf16_t* __restrict__ z, size_t T, int N, int H, int dv,
                                                      float eps) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = min(64, dv / 8), rpw = 64 / lpr, sub = lane % lpr;
+    const int lpr = gate_lanes_per_row(dv), rpw = 64 / lpr, sub = lane % lpr;
     const size_t rows = T * H;
     for (size_t r0 = (blockIdx.x * static_cast<size_t>(4) + wave) * rpw; r0 < rows;
          r0 += static_cast<size_t>(gridDim.x) * 4 * rpw) {
@@ -262,6 +271,31 @@ __global__ __launch_bounds__(256) void msr_gate_kernel(const float* __restrict__
         const float* orow = o + ((static_cast<size_t>(b) * H + h) * N + n) * dv;
         const size_t zrow = t * (static_cast<size_t>(H) * dv) + static_cast<size_t>(h) * dv;
         float ss = 0.f;
+        if (dv / 8 == lpr) {
+            // one 8-element unit per lane: its loads (retention output and gate) go out
+            // together, before the reduction, and the unit stays in registers
+            f32x4_t a{}, c{};
+            u16x8_t gv{};
+            if (live) {
+                a = *reinterpret_cast<const f32x4_t*>(orow + 8 * sub);
+                c = *reinterpret_cast<const f32x4_t*>(orow + 8 * sub + 4);
+                gv = *reinterpret_cast<const u16x8_t*>(gp + zrow + 8 * sub);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += a[i] * a[i] + c[i] * c[i];
+            for (int off = lpr / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            const float inv = 1.f / sqrtf(ss / dv + eps);
+            if (!live) continue;
+            f32x4_t lo, hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = bf16_to_f32(gv[i]), x1 = bf16_to_f32(gv[i + 4]);
+                lo[i] = x0 / (1.f + expf(-x0)) * a[i] * inv;
+                hi[i] = x1 / (1.f + expf(-x1)) * c[i] * inv;
+            }
+            *reinterpret_cast<u16x8_t*>(z + zrow + 8 * sub) = cat(bf4(lo), bf4(hi));
+            continue;
+        }
         for (int u = sub; live && u < dv / 8; u += lpr) {
             const f32x4_t a = *reinterpret_cast<const f32x4_t*>(orow + 8 * u);
             const f32x4_t c = *reinterpret_cast<const f32x4_t*>(orow + 8 * u + 4);
@@ -481,7 +515,7 @@ hipError_t run_msr(const MsrShape& s, const MsrPtrs& x, const MsrPlan& p, void* 
     a.out_f32 = true;
     RETN_TRY(launch_mfma_chunk(a, p.ret, st));
     const size_t rows = T * s.H;
-    const size_t rows_per_block = 4 * static_cast<size_t>(64 / std::min(64, s.dv / 8));
+    const size_t rows_per_block = 4 * static_cast<size_t>(64 / gate_lanes_per_row(s.dv));
     const unsigned blocks = static_cast<unsigned>(std::min<size_t>((rows + rows_per_block - 1) / rows_per_block, 1u << 20));
     hipLaunchKernelGGL(msr_gate_kernel, dim3(blocks), dim3(256), 0, st, o, static_cast<const bf16_t*>(gp),
                        static_cast<bf16_t*>(z), T, s.N, s.H, s.dv, s.norm_eps);

@@ -70,6 +70,10 @@ CASES = [
     (2, 50, 64, 2, 64, 128, 64),
     # more projection tiles than the device holds at once: ragged rows, one and three
     # reduction steps
+    # value widths whose rows are not a power-of-two number of 8-element units (the
+    # norm's lanes then loop over units)
+    (1, 60, 128, 2, 64, 192, 64),
+    (1, 40, 64, 1, 64, 320, 64),
     (1, 1900, 64, 8, 128, 128, 64),
     (1, 1900, 192, 8, 128, 128, 64),
 ]
