@@ -41,7 +41,7 @@
  *   Sizes      B, H, N >= 0 (B*H*N = 0 is a valid empty call: state_out, if given,
  *              receives state_in or zeros); dk in [1, 256], dv in [1, 1024]; chunk >= 1.  The bf16 matrix-core path is used when dk is
  *              64, 128 or 256, dv is a multiple of 64 (<= 1024), chunk <= 512,
- *              q, k, v, o are 16-byte aligned and one head's rows span less than
+ *              q, k, v, o (and state_out, when given) are 16-byte aligned and one head's rows span less than
  *              2^31 bytes ((N + 64) * max(dk, dv) * 2 < 2^31); every other shape in
  *              range runs on the generic kernels.
  *              A ragged last chunk (N not a multiple of chunk) is computed exactly;
@@ -89,8 +89,10 @@ typedef enum {
  *   state_out   optional [B,H,dk,dv] fp32 final state S_N (NULL = not written); may
  *               equal state_in (in-place update) but must not overlap q/k/v/o
  *   chunk       chunk size in tokens (>= 1); changes rounding only, not the result
- *   workspace   device scratch of at least retention_workspace_bytes(...) bytes
- *               (may be NULL when that is 0); contents need not be initialised
+ *   workspace   device scratch of at least retention_workspace_bytes(...) bytes,
+ *               16-byte aligned (may be NULL when that is 0; RETN_ERR_WORKSPACE when
+ *               it is needed and missing, smaller or misaligned); contents need not be
+ *               initialised
  *   stream      hipStream_t to enqueue on
  */
 retn_status retention_chunkwise_fwd(const void* q, const void* k, const void* v,

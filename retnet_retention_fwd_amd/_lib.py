@@ -150,11 +150,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context in which the wrapper allocates its outputs and workspace: the stream the
+    kernels run on, so that torch's caching allocator hands a freed block out again only
+    in that stream's order (a block allocated on another stream could be reused there
+    while the kernels still read or write it)."""
+    import contextlib
+    torch = _torch()
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:
     return int(lib().retention_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, 1 if gated else 0))
 
 
-def _chunk_call(fn_name, q, k, v, decay, chunk, state_in, return_state, out, state_out, stream,
+def _chunk_call_impl(fn_name, q, k, v, decay, chunk, state_in, return_state, out, state_out, stream,
                 workspace, gated):
     torch = _torch()
     L = lib()
@@ -199,6 +209,12 @@ def _chunk_call(fn_name, q, k, v, decay, chunk, state_in, return_state, out, sta
     return (out, state_out) if (return_state or state_out is not None) else out
 
 
+def _chunk_call(fn_name, q, k, v, decay, chunk, state_in, return_state, out, state_out, stream, workspace, gated):
+    with _on_stream(stream):
+        return _chunk_call_impl(fn_name, q, k, v, decay, chunk, state_in, return_state, out, state_out, stream,
+                                workspace, gated)
+
+
 def retention_chunkwise_fwd(q, k, v, gamma, chunk, state_in=None, return_state=False, out=None,
                             state_out=None, stream=None, workspace=None):
     """Chunkwise retention forward with per-head decays gamma[H] (fp32).
@@ -217,7 +233,7 @@ def gated_retention_chunkwise_fwd(q, k, v, g, chunk, state_in=None, return_state
                        state_out, stream, workspace, True)
 
 
-def _parallel_call(fn_name, q, k, v, decay, out, stream, gated):
+def _parallel_call_impl(fn_name, q, k, v, decay, out, stream, gated):
     torch = _torch()
     L = lib()
     _require(q, "q")
@@ -245,6 +261,11 @@ def _parallel_call(fn_name, q, k, v, decay, out, stream, gated):
     return out
 
 
+def _parallel_call(fn_name, q, k, v, decay, out, stream, gated):
+    with _on_stream(stream):
+        return _parallel_call_impl(fn_name, q, k, v, decay, out, stream, gated)
+
+
 def retention_parallel_fwd(q, k, v, gamma, out=None, stream=None):
     """Parallel-form retention forward O = (Q K^T (.) D) V (no state); shapes as the chunkwise form."""
     return _parallel_call("retention_parallel_fwd", q, k, v, gamma, out, stream, False)
@@ -265,6 +286,12 @@ def gated_msr_fwd(x, wq, wk, wv, wg, wgt, wo, H, dk, dv, chunk=64, rope_base=100
     bf16), interleaved rotary rotation of q and k, k / sqrt(dk), decay logsigmoid(gt)/16,
     gated chunkwise retention, per-head RMSNorm, silu gate, output projection.  Returns y
     [B,N,D] bf16."""
+    with _on_stream(stream):
+        return _gated_msr_fwd_impl(x, wq, wk, wv, wg, wgt, wo, H, dk, dv, chunk, rope_base, norm_eps, out, workspace,
+                                   stream)
+
+
+def _gated_msr_fwd_impl(x, wq, wk, wv, wg, wgt, wo, H, dk, dv, chunk, rope_base, norm_eps, out, workspace, stream):
     torch = _torch()
     L = lib()
     _require(x, "x", torch.bfloat16)
@@ -300,7 +327,7 @@ def bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, gated) -> int:
     return int(lib().retention_bwd_workspace_bytes(B, H, N, dk, dv, chunk, dtype_code, 1 if gated else 0))
 
 
-def _bwd_call(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
+def _bwd_call_impl(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
               workspace, gated):
     torch = _torch()
     L = lib()
@@ -349,6 +376,13 @@ def _bwd_call(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_gr
     return (gq, gk, gv, gs) if return_grad_state_in else (gq, gk, gv)
 
 
+def _bwd_call(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream, workspace,
+              gated):
+    with _on_stream(stream):
+        return _bwd_call_impl(q, k, v, decay, grad_o, chunk, state_in, grad_state_out, return_grad_state_in, stream,
+                              workspace, gated)
+
+
 def retention_chunkwise_bwd(q, k, v, gamma, grad_o, chunk, state_in=None, grad_state_out=None,
                             return_grad_state_in=False, stream=None, workspace=None):
     """Backward of retention_chunkwise_fwd for L = <grad_o, o> + <grad_state_out, state_out>.
@@ -367,7 +401,7 @@ def gated_retention_chunkwise_bwd(q, k, v, g, grad_o, chunk, state_in=None, grad
                      workspace, True)
 
 
-def _decode_call(fn_name, q, k, v, decay, state, out, stream, gated):
+def _decode_call_impl(fn_name, q, k, v, decay, state, out, stream, gated):
     torch = _torch()
     L = lib()
     _require(q, "q")
@@ -388,10 +422,17 @@ def _decode_call(fn_name, q, k, v, decay, state, out, stream, gated):
         out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     else:
         _require(out, "out", q.dtype, dev)
+        if tuple(out.shape) != (B, H, dv):
+            raise ValueError(f"out must be [B,H,dv] = {(B, H, dv)}, got {tuple(out.shape)}")
     st = getattr(L, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state), _ptr(out), B, H, dk,
                              dv, _dtype_code(q), _stream(stream))
     _check(st, fn_name)
     return out
+
+
+def _decode_call(fn_name, q, k, v, decay, state, out, stream, gated):
+    with _on_stream(stream):
+        return _decode_call_impl(fn_name, q, k, v, decay, state, out, stream, gated)
 
 
 def retention_decode_step(q, k, v, gamma, state, out=None, stream=None):

@@ -94,8 +94,9 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
                                     dt, gated);
     if (st != RETN_OK) return st;
     const int eff_chunk = effective_chunk(N, chunk);
+    // (the matrix-core kernels write state_out and the segment states in 16-byte units)
     const bool mfma = use_mfma(N, dk, dv, eff_chunk, dt) && aligned16(q) && aligned16(k) && aligned16(v) &&
-                      aligned16(o);
+                      aligned16(o) && (state_out == nullptr || aligned16(state_out));
     // The generic kernel keeps a gated chunk's cumulative decays in LDS.
     if (!mfma && gated && eff_chunk > kGenericMaxGatedChunk) return RETN_ERR_UNSUPPORTED;
     size_t need = 0;
@@ -104,7 +105,8 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
         plan = retn::mfma_chunk_plan(B, H, N, dk, dv, eff_chunk, gated);
         need = plan.workspace_bytes;
     }
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return RETN_ERR_WORKSPACE;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return RETN_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t bh = static_cast<size_t>(B) * H;

@@ -57,9 +57,9 @@ __device__ __forceinline__ u16x4_t lds_tr(const char* base, int byte_off) {
 // Reads at an absolute LDS byte address (the compiler folds constant additions into
 // the instruction's offset field).
 typedef __attribute__((address_space(3))) u16x8_t lds_u16x8_t;
-__device__ __forceinline__ u16x8_t lds16a(uint32_t addr) { return *(const lds_u16x8_t*)(addr); }
+__device__ __forceinline__ u16x8_t lds16a(uint32_t addr) { return *(const lds_u16x8_t*)(static_cast<size_t>(addr)); }
 __device__ __forceinline__ u16x4_t lds_tra(uint32_t addr) {
-    return __builtin_bit_cast(u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(addr)));
+    return __builtin_bit_cast(u16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(static_cast<size_t>(addr))));
 }
 // Hides how a value was computed, so the compiler keeps it in one register instead of
 // re-deriving it from its parts at every use.
@@ -93,27 +93,28 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // l reads rsrc + soffset + voffset and its 16 bytes land at LDS byte lds_addr + 16 l
 // (lds_addr and soffset are wave-uniform).  The instruction writes no registers; it is
 // issued from inline assembly so that the compiler does not treat it as aliasing every
-// later LDS read.  Completion is awaited explicitly (s_waitcnt vmcnt(0) followed by a
-// workgroup barrier) before the tile is read.
+// later LDS read.  The LDS address goes in through an input operand bound to m0, so the
+// compiler itself sets m0 and knows it holds that value.  Completion is awaited
+// explicitly (s_waitcnt vmcnt(0) followed by a workgroup barrier) before the tile is read.
 __device__ __forceinline__ void buf2lds16(const u32x4_t& rsrc, uint32_t voffset, uint32_t soffset,
                                           uint32_t lds_addr) {
     // the scalar operands are wave-uniform; readfirstlane pins them to SGPRs
     const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr)));
     const uint32_t soff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(soffset)));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+                 : "v"(voffset), "s"(rsrc), "s"(soff), "{m0}"(m0v)
+                 : "memory");
 }
 // Same for 4 bytes per lane: lane l's dword lands at LDS byte lds_addr + 4 l.
 __device__ __forceinline__ void buf2lds4(const u32x4_t& rsrc, uint32_t voffset, uint32_t soffset,
                                          uint32_t lds_addr) {
     const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr)));
     const uint32_t soff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(soffset)));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dword %0, %1, %2 offen lds"
                  :
-                 : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+                 : "v"(voffset), "s"(rsrc), "s"(soff), "{m0}"(m0v)
+                 : "memory");
 }
 // Wait until at most N vector memory operations of this wave are outstanding.
 template <int N>

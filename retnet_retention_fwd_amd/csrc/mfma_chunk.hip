@@ -42,6 +42,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace retn {
@@ -1220,14 +1221,14 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ b
 
 template <int DK, int DVT, int NW, bool GATED, int MODE, bool ONEBLK, bool OF32, bool REV, bool PAR = false>
 hipError_t launch_kernel(const KArgs& ka, hipStream_t stream) {
-    const size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>::L::kBytes;
-    static bool attr_done = false;   // benign race: the attribute call is idempotent
-    if (!attr_done) {
+    constexpr size_t lds = Plan<DK, DVT, GATED, MODE, NW, ONEBLK, OF32>::L::kBytes;
+    // the LDS limit is raised once per kernel instance (thread-safe one-time init)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [] {
         (void)hipFuncSetAttribute(
             reinterpret_cast<const void*>(&chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV, PAR>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        attr_done = true;
-    }
+    });
     ProfScope prof(MODE == kFull ? kProfMain : kProfPre, stream);
     hipLaunchKernelGGL((chunk_kernel<DK, DVT, NW, GATED, MODE, ONEBLK, OF32, REV, PAR>), dim3(ka.total_groups),
                        dim3(NW * 64), lds, stream, ka);

@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace retn {
 namespace {
 
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ro
 }
 
 // z[t, h*dv + j] = silu(gp[t, h*dv + j]) * o[b,h,n,j] / sqrt(mean_j o[b,h,n,:]^2 + eps).
-// A (token, head) row is spread over LPR = min(64, dv/8) adjacent lanes, eight elements
-// per lane and step; a wave takes 64/LPR rows (dv a multiple of 64).
+// A (token, head) row is spread over gate_lanes_per_row(dv) adjacent lanes, eight
+// elements per lane and pass; a wave takes 64 / that many rows.
 // Lanes that share one row of d_v elements, eight elements a lane per pass: the largest
 // power of two up to 64 and d_v / 8, so that a row's lanes form an aligned group that a
 // butterfly of shuffles reduces.
@@ -412,12 +414,11 @@ hipError_t launch_decay(const MsrPtrs& x, float* g, size_t T, const MsrShape& s,
     // a few workgroups per CU, each looping over tokens (the weights are staged once each)
     const size_t wbytes = static_cast<size_t>(s.H) * s.D * 2;
     const unsigned tblocks = static_cast<unsigned>(std::min<size_t>((T + 3) / 4, 1024));
-    static bool decay_attr = false;   // benign race: the attribute call is idempotent
-    if (!decay_attr) {
+    static std::once_flag attr_once;   // thread-safe one-time init of the LDS limit
+    std::call_once(attr_once, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&msr_decay_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kDecayLds);
-        decay_attr = true;
-    }
+    });
     hipLaunchKernelGGL(msr_decay_kernel, dim3(tblocks), dim3(256), wbytes <= kDecayLds ? wbytes : 0, st,
                        static_cast<const bf16_t*>(x.x), static_cast<const bf16_t*>(x.wgt), g, T, s.N, s.D, s.H,
                        1.f / 16.f);

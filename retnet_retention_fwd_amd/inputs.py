@@ -152,6 +152,14 @@ def make_decode(w: Workload, *, B=None, steps=None, seed=None):
     return out
 
 
+def decode_log_decays(seed, steps, B, H):
+    """Per-step log-decays of a gated decode run: g_t = logsigmoid(x_t)/16 with
+    x_t ~ N(0,1) [B,H], from a generator of its own seed, drawn step by step.  Returns
+    (torch CPU tensor [steps,B,H] fp32, float64 copy)."""
+    rng = np.random.default_rng(seed)
+    return to_dtype(logsigmoid(rng.standard_normal((steps, B, H))) / 16.0, "f32")
+
+
 def random_case(seed, B, H, N, dk, dv, dtype="bf16", gated=False, state_in=False,
                 gamma_lo=0.8):
     """Generic seeded case for tests: Q,K,V ~ N(0,1)/sqrt(dk); gamma ~ U(gamma_lo, 1)

@@ -73,6 +73,8 @@ def test_chunk_validation(L, gated):
     assert need > 0
     assert c(N=65536, dk=128, dv=128, C=64, dt=1) == ERR_WORKSPACE
     assert c(N=65536, dk=128, dv=128, C=64, dt=1, ws=FAKE + 400 * MB, wsb=need - 1) == ERR_WORKSPACE
+    # the segment states are written in 16-byte units: a misaligned workspace is refused
+    assert c(N=65536, dk=128, dv=128, C=64, dt=1, ws=FAKE + 400 * MB + 4, wsb=need) == ERR_WORKSPACE
 
 
 def test_decode_validation(L):
@@ -218,3 +220,25 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         retention_chunkwise_fwd(q, q, q, torch.ones(1), 4)
+
+
+def test_decode_wrapper_rejects_wrong_out_shape(monkeypatch):
+    """The C entry point sees only pointers, so the binding checks the shape of a
+    caller's `out`; a smaller one would let the kernel write past it."""
+    torch = pytest.importorskip("torch")
+
+    def lenient(t, name, dtype=None, device=None):   # host tensors stand in for device ones
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(name)
+
+    monkeypatch.setattr(_lib, "_require", lenient)
+    B, H, d = 2, 3, 16
+    q = torch.zeros(B, H, d, dtype=torch.bfloat16)
+    gamma = torch.full((H,), 0.9)
+    state = torch.zeros(B, H, d, d)
+    for bad in ((B, H, d // 2), (B, H - 1, d), (B * H * d,)):
+        out = torch.zeros(bad, dtype=torch.bfloat16)
+        with pytest.raises(ValueError, match="out must be"):
+            _lib.retention_decode_step(q, q, q, gamma, state, out=out)
+        with pytest.raises(ValueError, match="out must be"):
+            _lib.gated_retention_decode_step(q, q, q, torch.zeros(B, H), state, out=out)

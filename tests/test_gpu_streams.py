@@ -40,6 +40,33 @@ def test_side_stream_matches_default_stream():
     assert torch.equal(out, ref)
 
 
+def test_explicit_stream_without_workspace():
+    """stream= names a side stream and the wrapper allocates the workspace and the output
+    itself: both must belong to that stream, so that memory freed after the call is not
+    handed to the current stream's work while the side stream's kernels still use it."""
+    print("\n[case] explicit stream, wrapper-allocated workspace", flush=True)
+    x = _case()
+    ref = R().gated_retention_chunkwise_fwd(x["q"], x["k"], x["v"], x["g"], 64, state_in=x["state_in"])
+    torch.cuda.synchronize()
+    nbytes = R().workspace_bytes(1, 4, 1500, 128, 128, 64, 1, True)
+    assert nbytes > 0
+    side = torch.cuda.Stream()
+    outs = []
+    for rep in range(4):
+        side.wait_stream(torch.cuda.current_stream())
+        outs.append(R().gated_retention_chunkwise_fwd(x["q"], x["k"], x["v"], x["g"], 64, state_in=x["state_in"],
+                                                      stream=side))
+        # the current stream allocates blocks of the workspace's size and overwrites them
+        # at once, while the side stream may still be running
+        junk = [torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        junk += [torch.full(tuple(ref.shape), 7.0, dtype=ref.dtype, device="cuda")]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for rep, out in enumerate(outs):
+        assert torch.equal(out, ref), rep
+
+
 def test_graph_capture_and_replay():
     print("\n[case] graph capture", flush=True)
     x = _case()

@@ -6,7 +6,10 @@ page and mathematics fix, independent of the oracle's own code path:
   * RMSNorm has unit root-mean-square (eps = 0) and is scale invariant;
   * silu and logsigmoid against scipy's expit and numpy's logaddexp;
   * the whole layer on one and on two tokens, worked out by hand from the recurrence
-    (S = lambda S + k^T v, o = q S) with the rotation done in complex arithmetic.
+    (S = lambda S + k^T v, o = q S) with the rotation done in complex arithmetic, both in
+    full precision and with bf16 activations (every tensor handed from one operation to
+    the next rounded to bf16 where it is stored, with torch's round-to-nearest-even
+    cast), which pins the oracle's optional rounding path.
 The mutation tests plant plausible mistakes in a copy of the oracle and check that a
 pin fails for each.
 """
@@ -125,8 +128,72 @@ def pin_layer_two_tokens(mod):
     assert np.allclose(y[0, 1], w["wo"] @ np.concatenate(z), rtol=1e-12, atol=1e-12)
 
 
+def _bf16(a):
+    """Round to bfloat16 (nearest even) with torch's cast, the library routine the GPU
+    comparison also uses; returned as float64."""
+    import torch
+    return torch.tensor(np.asarray(a, dtype=np.float64)).to(torch.bfloat16).double().numpy()
+
+
+def _bf16_inputs(rng, B, N, D, H, dk, dv):
+    x = _bf16(rng.standard_normal((B, N, D)))
+    w = {n: _bf16(a) for n, a in _weights(rng, D, H, dk, dv).items()}
+    return x, w
+
+
+def pin_layer_one_token_bf16(mod):
+    """The layer with bf16 activations on one token, worked step by step: every tensor
+    the layer hands from one operation to the next is stored in bf16 (q, and k after its
+    scaling; v; the gate projection; the gated product; y), the retention output and the
+    norm stay in full precision.  d_k = 6 makes the key scale irrational, so rounding
+    before or after it differs."""
+    rng = np.random.default_rng(13)
+    B, D, H, dk, dv, eps = 2, 10, 2, 6, 4, 1e-5
+    x, w = _bf16_inputs(rng, B, 1, D, H, dk, dv)
+    y, _ = mod.gated_msr_forward(x, **w, H=H, dk=dk, dv=dv, eps=eps, act=_bf16)
+    for b in range(B):
+        xb = x[b, 0]
+        z = []
+        for h in range(H):
+            sl, sv = slice(h * dk, (h + 1) * dk), slice(h * dv, (h + 1) * dv)
+            q = _bf16(w["wq"][sl] @ xb)                    # position 0: no rotation
+            k = _bf16(w["wk"][sl] @ xb / np.sqrt(dk))
+            v = _bf16(w["wv"][sv] @ xb)
+            o = (q @ k) * v                                 # S = k^T v, o = q S
+            o = o / np.sqrt(np.mean(o ** 2) + eps)
+            gate = _bf16(w["wg"][sv] @ xb)
+            z.append(gate * expit(gate) * o)
+        want = _bf16(w["wo"] @ _bf16(np.concatenate(z)))
+        assert np.array_equal(y[b, 0], want), (y[b, 0], want)
+
+
+def pin_layer_two_tokens_bf16(mod):
+    """Two tokens with bf16 activations: token 1's q and k are rotated as position 1 in
+    full precision and then rounded; the decay and the recurrence stay in full
+    precision."""
+    rng = np.random.default_rng(14)
+    D, H, dk, dv, eps, base = 12, 2, 6, 3, 1e-5, 10.0
+    x, w = _bf16_inputs(rng, 1, 2, D, H, dk, dv)
+    y, _ = mod.gated_msr_forward(x, **w, H=H, dk=dk, dv=dv, eps=eps, rope_base=base, act=_bf16)
+    x0, x1 = x[0, 0], x[0, 1]
+    z = []
+    for h in range(H):
+        sl, sv = slice(h * dk, (h + 1) * dk), slice(h * dv, (h + 1) * dv)
+        k0 = _bf16(w["wk"][sl] @ x0 / np.sqrt(dk))
+        q1 = _bf16(_rot_complex(w["wq"][sl] @ x1, 1, base))
+        k1 = _bf16(_rot_complex(w["wk"][sl] @ x1, 1, base) / np.sqrt(dk))
+        v0, v1 = _bf16(w["wv"][sv] @ x0), _bf16(w["wv"][sv] @ x1)
+        lam1 = expit(w["wgt"][h] @ x1) ** (1.0 / 16.0)
+        o = lam1 * (q1 @ k0) * v0 + (q1 @ k1) * v1
+        o = o / np.sqrt(np.mean(o ** 2) + eps)
+        gate = _bf16(w["wg"][sv] @ x1)
+        z.append(gate * expit(gate) * o)
+    want = _bf16(w["wo"] @ _bf16(np.concatenate(z)))
+    assert np.allclose(y[0, 1], want, rtol=0, atol=0), (y[0, 1], want)
+
+
 PINS = [pin_rope_complex, pin_rope_position_zero_and_relative, pin_rms_norm, pin_activations,
-        pin_layer_one_token, pin_layer_two_tokens]
+        pin_layer_one_token, pin_layer_two_tokens, pin_layer_one_token_bf16, pin_layer_two_tokens_bf16]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -180,6 +247,21 @@ MUTANTS = {
     "silu_on_output": [("    z = r(silu(r(proj(wg))) * o)\n", "    z = r(r(proj(wg)) * silu(o))\n")],
     # sigmoid instead of silu
     "sigmoid_gate": [("    return x / (1.0 + np.exp(-x))\n", "    return 1.0 / (1.0 + np.exp(-x))\n")],
+    # bf16 activations rounded at other points than the stored tensors:
+    # q rounded before its rotation
+    "act_q_before_rotation": [("    q = r(rope_interleaved(heads(proj(wq), dk), rope_base))\n",
+                               "    q = rope_interleaved(heads(r(proj(wq)), dk), rope_base)\n")],
+    # k rounded before its scaling
+    "act_k_before_scale": [("    k = r(rope_interleaved(heads(proj(wk), dk), rope_base) / np.sqrt(dk))\n",
+                            "    k = r(rope_interleaved(heads(proj(wk), dk), rope_base)) / np.sqrt(dk)\n")],
+    # v kept in full precision
+    "act_v_unrounded": [("    v = heads(r(proj(wv)), dv)\n", "    v = heads(proj(wv), dv)\n")],
+    # the retention output rounded before the norm
+    "act_o_rounded": [("    o, _ = gated_retention_recurrent(q, k, v, g)", "    o = r(gated_retention_recurrent(q, k, v, g)[0]); _ = 0")],
+    # the gate projection kept in full precision
+    "act_gate_unrounded": [("    z = r(silu(r(proj(wg))) * o)\n", "    z = r(silu(proj(wg)) * o)\n")],
+    # the output left unrounded
+    "act_y_unrounded": [("    return r(z @ _f64(wo).T), g\n", "    return z @ _f64(wo).T, g\n")],
 }
 
 
