@@ -1,0 +1,633 @@
+// bf16 chunkwise retention forward on the gfx950 matrix cores, for chunks of exactly
+// 64 tokens (one LDS block per chunk).
+//
+// Method ("RetNet retention mechanism" tutorial, section 块级循环, with the per-row
+// cross-chunk decay; gated decays from the pwwt.cn guide, section Triton 内核与自校验测试).
+// For a chunk of L tokens with chunk-local log2 decays G (G_j = log2 of the product of
+// the decays of positions 0..j):
+//     O     = (Q K^T (.) D) V + diag(2^G) (Q S_prev),      D_jl = 2^(G_j - G_l), j >= l
+//     S_new = 2^(G_{L-1}) S_prev + K^T (V (.) zeta),        zeta_l = 2^(G_{L-1} - G_l)
+//
+// This is the general matrix-core kernel's single-block path without its general
+// machinery: every step of the walk is one whole chunk, so there is no query/key block
+// bookkeeping; the walk is unrolled by two so that every LDS address is a per-lane
+// pattern plus a compile-time offset; per-head decay factors of a full chunk are
+// computed once (a step then needs two exponentials); the gated chunk-local prefix sums
+// are formed one chunk ahead by wave 0, so no step waits on them behind a barrier.
+// Fragment layouts, swizzles and the state-row permutation are those of the general
+// kernel (mfma_chunk.hip).
+//
+// Work decomposition: a workgroup owns one (b,h), one segment of the sequence and 128
+// state columns; its eight waves own 16 columns each and hold their DK x 16 slice of S
+// in fp32 matrix-core accumulators.  A step (one chunk) runs:
+//   barrier; cross term X = diag(2^G) Q S_prev (the next chunk's K and V copies go out
+//   between its matrix instructions); this wave's score tiles, decayed, bf16, into LDS;
+//   barrier; (one Q stage: the next chunk's Q copies) state update; X += P V; X staged
+//   in LDS as bf16 and stored in whole rows after the next barrier.
+
+#include "cdna4.h"
+#include "chunk_tiles.h"
+#include "common.h"
+#include "launch.h"
+
+#include <mutex>
+#include <type_traits>
+
+namespace retn {
+
+namespace {
+
+constexpr int kC1Cols = 128;   // state columns per workgroup
+constexpr int kC1Waves = 8;    // 16 columns per wave
+
+// LDS layout: Q (one stage for d_k = 256, two otherwise), two stages of K and V, the P
+// fragments of the current chunk, the staging area of one output block, and (gated)
+// two stages of the chunk-local log2 prefix sums.
+template <int DK, bool GATED>
+struct C1Lds {
+    static constexpr int QRB = DK * 2, VRB = kC1Cols * 2;       // row bytes
+    static constexpr int QS = DK == 256 ? 1 : 2;                // Q stages
+    static constexpr int kQTile = kBlk * QRB, kKTile = kBlk * QRB, kVTile = kBlk * VRB;
+    static constexpr int kQ = 0;
+    static constexpr int kK = kQ + QS * kQTile;
+    static constexpr int kV = kK + 2 * kKTile;
+    static constexpr int kP = kV + 2 * kVTile;
+    static constexpr int kX = kP + kPBytes;
+    static constexpr int kG = kX + kBlk * kC1Cols * 2;
+    static constexpr int kBytes = kG + (GATED ? 2 * kBlk * 4 : 0);
+    static_assert(kBytes <= kLdsBytes, "LDS layout too large");
+};
+
+template <int DK, bool GATED>
+__global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk1_kernel(
+    const KArgs ka) {
+    using L_ = C1Lds<DK, GATED>;
+    constexpr int NW = kC1Waves, DVT = kC1Cols;
+    constexpr int QRB = L_::QRB, VRB = L_::VRB, QS = L_::QS;
+    constexpr int DT = DK / 16;    // 16-row tiles of the state
+    constexpr int KS = DK / 32;    // reduction steps over DK
+    constexpr int KL = KS < 4 ? KS : 4;
+    constexpr int SL = KS < 4 ? KS : 4;
+    using QCopy = TileCopy<QRB, false, NW>;
+    using VCopy = TileCopy<VRB, true, NW>;
+    constexpr int kNQ = QCopy::kPerWave, kNV = VCopy::kPerWave;
+
+    const bf16_t* __restrict__ q = ka.q;
+    const bf16_t* __restrict__ k = ka.k;
+    const bf16_t* __restrict__ v = ka.v;
+    const float* __restrict__ decay = ka.decay;
+    bf16_t* __restrict__ o = static_cast<bf16_t*>(ka.o);
+    const int H = ka.H, N = ka.N, dv = ka.dv;
+    const int nseg = ka.nseg, ndvt = ka.ndvt;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    // ---- work item (XCD-aware: each XCD takes a contiguous range of work ids, so a
+    // (b,h)'s column tiles and segments share an L2)
+    int wid = blockIdx.x;
+    if (ka.total_groups % 8 == 0) wid = (wid & 7) * (ka.total_groups >> 3) + (wid >> 3);
+    const int dvt = wid % ndvt;
+    const int seg = (wid / ndvt) % nseg;
+    const int bh = wid / (ndvt * nseg);
+    const int h = bh % H;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int trj = l16 >> 2, trq = l16 & 3;
+    const int col0 = dvt * DVT, wcol = wave * 16;
+
+    // prefix split (two segments): segment 1 first walks [0, pre_tokens) state-only
+    const bool split = ka.pre_tokens > 0;
+    const int t_begin = split ? (seg == 0 ? 0 : ka.pre_tokens) : seg * ka.seg_tokens;
+    const int t_end = split ? (seg == 0 ? min(N, ka.pre_tokens) : N) : min(N, t_begin + ka.seg_tokens);
+    const int nck = (t_end - t_begin + kBlk - 1) / kBlk;
+    const int npre = split && seg == 1 ? ka.pre_tokens / kBlk : 0;   // prefix chunks
+    const float lg = GATED ? 0.f : log2f(decay[h]);
+
+    const size_t qk_bh = static_cast<size_t>(bh) * N * DK;
+    const size_t v_bh = static_cast<size_t>(bh) * N * dv;
+    const size_t s_bh = static_cast<size_t>(bh) * DK * dv;
+    const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
+    const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
+    // ranges end with the last row's own columns; rows past N read as zeros
+    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * DK * 2);
+    const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
+    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>((N - 1) * dv + dv - col0) * 2);
+    const uint32_t lds0 = lds_addr_of(smem);
+    QCopy kcp;   // Q and K tiles (same row length and swizzle)
+    VCopy vcp;
+    kcp.init(DK * 2, wave, lane, N);
+    vcp.init(dv * 2, wave, lane, N);
+    const uint32_t wofs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+
+    // State accumulator element (dt, i) of lane (g, l%16) holds state row srow(dt, i) of
+    // column col0 + wcol + l%16 (the layout of the general kernel: conflict-free K^T
+    // transpose reads, and an 8-row B operand of Q S per 16-byte Q read).
+    auto srow = [&](int dt, int i) -> int { return 32 * (dt >> 1) + 8 * g4 + 4 * ((dt ^ g4) & 1) + i; };
+
+    // ---- incoming state: state_in, the scanned entry state, or (fuse_scan) composed here
+    f32x4_t S[DT];
+    {
+        const int cidx = col0 + wcol + l16;
+        auto load = [&](const float* src, float scale, bool add) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = src[static_cast<uint32_t>(srow(dt, i) * dv + cidx)];
+                    S[dt][i] = add ? S[dt][i] * scale + x : x;
+                }
+        };
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) S[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (nseg == 1 || split || ka.fuse_scan) {
+            int sg0 = 0;
+            if (ka.state_in != nullptr) {
+                load(ka.state_in + s_bh, 0.f, false);
+            } else if (seg > 0 && !split) {
+                load(ka.seg_state + static_cast<size_t>(bh) * nseg * s_stride_seg, 0.f, false);
+                sg0 = 1;
+            }
+            for (int sg = sg0; nseg > 1 && !split && sg < seg; ++sg)
+                load(ka.seg_state + (static_cast<size_t>(bh) * nseg + sg) * s_stride_seg,
+                     exp2f(ka.seg_log2[static_cast<size_t>(bh) * nseg + sg]), true);
+        } else {
+            load(ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg, 0.f, false);
+        }
+    }
+
+    // ---- per-lane LDS read patterns (byte offsets within a tile)
+    //   Q/K rows (row tile t, reduction step ks): pq[ks%4] + t*16*QRB + (ks/4)*256;
+    //   K^T transposed reads (state tile dt, key rows r0 and r0+4, key half kh):
+    //     pkt[pl][(dt/2)%4][dt%2] + kh*32*QRB + (dt/8)*256;
+    //   V transposed reads: pvp + (ks*32 + 16 half)*VRB (P V), pvs[pl] + kh*32*VRB (state).
+    uint32_t pq[KL], pkt[2][SL][2], pvp, pvs[2];
+    {
+        const int s = swz_qk<QRB / 16>(l16);
+#pragma unroll
+        for (int kl = 0; kl < KL; ++kl)
+            pq[kl] = static_cast<uint32_t>(l16 * QRB + 16 * (4 * (kl ^ (s >> 2)) + (g4 ^ (s & 3))));
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+            const int rb = 8 * g4 + trj + 4 * pl;
+            const int w = swz_qk<QRB / 16>(rb);
+#pragma unroll
+            for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+                    pkt[pl][sl][hb] = static_cast<uint32_t>(rb * QRB + 16 * (4 * (sl ^ (w >> 2)) + (trq ^ (w & 3))) +
+                                                            8 * (hb ^ (trq & 1)));
+            const int sv = swz_v<VRB / 16>(rb);
+            pvs[pl] = static_cast<uint32_t>(rb * VRB + 16 * (2 * (wave ^ (sv >> 1)) + (trq >> 1)) + 8 * (trq & 1));
+        }
+        const int rbp = 4 * g4 + trj;
+        const int svp = swz_v<VRB / 16>(rbp);
+        pvp = static_cast<uint32_t>(rbp * VRB + 16 * (2 * (wave ^ (svp >> 1)) + (trq >> 1)) + 8 * (trq & 1));
+    }
+
+    // ---- decays of a full chunk (per head), computed once.  Every exponent is >= 0,
+    // so no factor exceeds 1.
+    //   fxi[mt]:   gamma^(row + 1) for this lane's query row of row tile mt;
+    //   ws[s][i]:  score weights of this wave's two tiles (gamma^(query - key), 0 above
+    //              the diagonal; tiles above the diagonal are never written);
+    //   fz[i]:     gamma^(31 - key) for this lane's eight keys of the second key half
+    //              (the first half's are these times gamma^32).
+    // The two score tiles of wave w are tile_order(w) and tile_order(w + 8).
+    int tq[2], tk[2];
+#pragma unroll
+    for (int s16 = 0; s16 < 2; ++s16) {
+        const int code = tile_order(wave + s16 * NW);
+        tq[s16] = code >> 2;
+        tk[s16] = code & 3;
+    }
+    float fxi[4], ws[2][4], fz[8];
+    const float g32 = GATED ? 0.f : exp2_fast(32.f * lg);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) fxi[mt] = GATED ? 0.f : exp2_fast(static_cast<float>(mt * 16 + l16 + 1) * lg);
+#pragma unroll
+    for (int s16 = 0; s16 < 2; ++s16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dj = (tq[s16] - tk[s16]) * 16 + l16 - 4 * g4 - i;   // query - key
+            ws[s16][i] = GATED || dj < 0 ? 0.f : exp2_fast(static_cast<float>(dj) * lg);
+        }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fz[i] = GATED ? 0.f : exp2_fast(static_cast<float>(31 - 8 * g4 - i) * lg);
+
+    // The registers hold S / 2^lk2: a chunk's decay moves the uniform lk2 instead of
+    // rescaling every accumulator; contributions are multiplied by 2^-lk2 and the cross
+    // term by 2^lkx (lk2 before the chunk).  Below -64 the registers are rescaled once.
+    float lk2 = 0.f;
+    f32x4_t X[4];
+
+    // ---- gated: wave 0 forms the chunk-local inclusive prefix of g (times log2 e) for
+    // a chunk into gl[stage][0..63] (positions past the chunk end repeat the last sum)
+    float gnext = 0.f;
+    auto g_load = [&](int cs) {
+        if (GATED && wave == 0) {
+            const int lim = t_end - cs;
+            gnext = lane < lim ? g_bh[cs + lane] : 0.f;
+        }
+    };
+    auto g_scan = [&](int stage) {
+        if (GATED && wave == 0) {
+            float incl = gnext * kLog2e;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            reinterpret_cast<float*>(smem + L_::kG)[stage * kBlk + lane] = incl;
+        }
+    };
+
+    // ---- tile copies of chunk c into stage b (Q stage: b for two stages, 0 for one)
+    auto k_copy = [&](int i, int b, uint32_t row0) {
+        kcp.issue_one(i, lds0 + L_::kK + b * L_::kKTile + wofs, k_rs, row0 * QRB);
+    };
+    auto q_copy = [&](int i, int b, uint32_t row0) {
+        kcp.issue_one(i, lds0 + L_::kQ + (QS == 2 ? b : 0) * L_::kQTile + wofs, q_rs, row0 * QRB);
+    };
+    auto v_copy = [&](int i, int b, uint32_t row0) {
+        vcp.issue_one(i, lds0 + L_::kV + b * L_::kVTile + wofs, v_rs, row0 * dv * 2);
+    };
+
+    // ---- output staging: a finished block goes to LDS as bf16, row-major [64][128] with
+    // the 16-byte units of row r rotated by XOR with r; after the next barrier every lane
+    // stores 16-byte units, so each wave writes whole 256-byte rows.
+    constexpr int kXU = DVT * 2 / 16;                 // 16-byte units per staged row
+    constexpr int kXRounds = kBlk * kXU / (NW * 64);  // units per lane
+    u16x8_t xv[kXRounds];
+    int xs_row = -1;                                  // first token of the staged block
+    auto stage_write = [&]() {
+        char* const xs = smem + L_::kX;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = mt * 16 + l16;
+            const int u = wcol / 8 + (g4 >> 1);
+            *reinterpret_cast<u16x4_t*>(xs + row * (DVT * 2) + ((u ^ (row & (kXU - 1))) << 4) + (g4 & 1) * 8) =
+                bf4(X[mt]);
+        }
+    };
+    auto stage_load = [&]() {
+        const char* const xs = smem + L_::kX;
+#pragma unroll
+        for (int r = 0; r < kXRounds; ++r) {
+            const int e = r * NW * 64 + tid;
+            const int row = e / kXU, u = e % kXU;
+            xv[r] = *reinterpret_cast<const u16x8_t*>(xs + row * (DVT * 2) + ((u ^ (row & (kXU - 1))) << 4));
+        }
+    };
+    auto stage_emit = [&]() {
+        bf16_t* const base = o + v_bh + static_cast<size_t>(xs_row) * dv + col0;
+#pragma unroll
+        for (int r = 0; r < kXRounds; ++r) {
+            const int e = r * NW * 64 + tid;
+            const int row = e / kXU, u = e % kXU;
+            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = xv[r];
+        }
+        xs_row = -1;
+    };
+
+    // ---- prologue: P tiles above the diagonal are read by P V but never written, so
+    // the P area starts zeroed; chunk 0's tiles (and decays) are copied, then the
+    // incoming state's loads drain (the compiler does not count the asynchronous copies;
+    // a load it still tracked inside the walk would make it wait there for them)
+    {
+        static_assert(kPBytes == NW * 64 * 16, "one 16-byte unit of P per thread");
+        *reinterpret_cast<u16x8_t*>(smem + L_::kP + tid * 16) = u16x8_t{};
+        // the first chunk walked: the first prefix chunk (no Q), or the segment's first
+        const uint32_t r0 = static_cast<uint32_t>(npre > 0 ? 0 : t_begin);
+        if (npre == 0) {
+#pragma unroll
+            for (int i = 0; i < kNQ; ++i) q_copy(i, 0, r0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNQ; ++i) k_copy(i, 0, r0);
+#pragma unroll
+        for (int i = 0; i < kNV; ++i) v_copy(i, 0, r0);
+        g_load(static_cast<int>(r0));
+        __builtin_amdgcn_s_waitcnt(0);
+        g_scan(0);
+    }
+
+
+    // The state update over the chunk's L keys (full: L = 64), after the caller has
+    // added the chunk's decay to lk2.
+    auto state_update = [&](uint32_t kbase, uint32_t vbase, const float* gl, int L, bool full, auto hook) {
+        // rescale the registers once the state scale gets small (after the cross term,
+        // which reads them at the old scale)
+        if (lk2 < -64.f) {
+            const float r = exp2_fast(lk2);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) S[dt] *= r;
+            lk2 = 0.f;
+        }
+
+        // S += K^T (V (.) zeta) over the chunk's keys; slots are keys 32kh + 8g .. +7,
+        // gathered by transpose reads of K and V.  The Kt reads of the next G state tiles
+        // are issued before the matrix instructions on the current ones; hook(kh, group,
+        // groups) runs between the products of each group.
+        {
+            const float zs = exp2_fast(-lk2);
+            const float glast = GATED ? gl[L - 1] : 0.f;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                auto kt_frag = [&](int dt) -> u16x8_t {
+                    const int sd = dt >> 1;
+                    const uint32_t off = kbase + kh * 32 * QRB + (sd / SL) * 256;
+                    return cat(lds_tra(pkt[0][sd % SL][dt & 1] + off), lds_tra(pkt[1][sd % SL][dt & 1] + off));
+                };
+                constexpr int G = DT < 4 ? DT : (DT >= 16 ? 2 : 4);
+                u16x8_t acur[G], anext[G];
+                const u16x8_t raw = cat(lds_tra(vbase + pvs[0] + kh * 32 * VRB), lds_tra(vbase + pvs[1] + kh * 32 * VRB));
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) acur[jj] = kt_frag(jj);
+                __builtin_amdgcn_sched_barrier(0);
+                float z[8];
+                if constexpr (GATED) {
+                    const f32x4_t ga = *reinterpret_cast<const f32x4_t*>(gl + kh * 32 + 8 * g4);
+                    const f32x4_t gb = *reinterpret_cast<const f32x4_t*>(gl + kh * 32 + 8 * g4 + 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        z[i] = exp2_fast(glast - ga[i] - lk2);
+                        z[i + 4] = exp2_fast(glast - gb[i] - lk2);
+                    }
+                } else if (full) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) z[i] = fz[i] * (kh == 0 ? zs * g32 : zs);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        z[i] = exp2_fast(static_cast<float>(L - 1 - (kh * 32 + 8 * g4 + i)) * lg - lk2);
+                }
+                if (!full) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (kh * 32 + 8 * g4 + i >= L) z[i] = 0.f;
+                }
+                f32x4_t lo, hi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = bf16_to_f32(raw[i]) * z[i];
+                    hi[i] = bf16_to_f32(raw[i + 4]) * z[i + 4];
+                }
+                const u16x8_t bv = cat(bf4(lo), bf4(hi));
+#pragma unroll
+                for (int g0 = 0; g0 < DT; g0 += G) {
+                    if (g0 + G < DT) {
+#pragma unroll
+                        for (int jj = 0; jj < G; ++jj) anext[jj] = kt_frag(g0 + G + jj);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jj = 0; jj < G; ++jj) S[g0 + jj] = mfma16(acur[jj], bv, S[g0 + jj]);
+                    hook(kh, g0 / G, DT / G);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jj = 0; jj < G; ++jj) acur[jj] = anext[jj];
+                }
+            }
+        }
+    };
+
+
+    // The walk: npre state-only chunks (the first segment of a prefix split, walked by
+    // segment 1 for its entry state), then the segment's nck chunks.  Chunk c is staged
+    // in stage c % 2; the next chunk's copies go out between the products of the cross
+    // term (full steps; with one Q stage its Q copies after the P barrier) or of the
+    // state update (state-only steps).
+    const int ntot = npre + nck;
+    auto chunk_row = [&](int c) -> int { return c < npre ? c * kBlk : t_begin + (c - npre) * kBlk; };
+    constexpr int kOps = 2 * kNQ + kNV;                        // K, V, then Q copies
+    constexpr int kCrossOps = QS == 2 ? kOps : kNQ + kNV;      // those issued in the cross term
+    // Returns false past the last chunk.
+    auto step = [&](auto stage_c, int c) -> bool {
+        constexpr int ST = decltype(stage_c)::value;
+        constexpr int QB = QS == 2 ? ST : 0;
+        const bool sonly = c < npre;            // the state update alone
+        const int cs = chunk_row(c);
+        const int L = min(kBlk, t_end - cs);    // (prefix chunks are whole)
+        const bool full = L == kBlk;
+        const bool has_next = c + 1 < ntot;
+        const bool next_q = c + 1 >= npre;      // the next chunk is a full step: copy its Q
+        const uint32_t next_row = static_cast<uint32_t>(chunk_row(c + 1));
+        const uint32_t qbase = lds0 + L_::kQ + QB * L_::kQTile;
+        const uint32_t kbase = lds0 + L_::kK + ST * L_::kKTile;
+        const uint32_t vbase = lds0 + L_::kV + ST * L_::kVTile;
+        const float* const gl = reinterpret_cast<const float*>(smem + L_::kG) + ST * kBlk;
+        // copy op i of the next chunk (every index is tested by the callers' unrolled
+        // loops, so each copy's offset register is a constant)
+        auto copy_op = [&](int i) {
+            if (i < kNQ) k_copy(i, 1 - ST, next_row);
+            else if (i < kNQ + kNV) v_copy(i - kNQ, 1 - ST, next_row);
+            else if (next_q) q_copy(i - kNQ - kNV, 1 - ST, next_row);
+        };
+        // ops [lo, hi) spread over nslots slots: those of slot `slot`
+        auto copy_slice = [&](int lo, int hi, int slot, int nslots) {
+#pragma unroll
+            for (int i = 0; i < kOps; ++i)
+                if (i >= lo + slot * (hi - lo) / nslots && i < lo + (slot + 1) * (hi - lo) / nslots) copy_op(i);
+        };
+
+        // this chunk's tiles (and prefix sums) have landed and are visible to every wave
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        if (xs_row >= 0) {
+            stage_load();
+            stage_emit();
+        }
+        if (has_next) g_load(static_cast<int>(next_row));
+
+        // decays of this chunk
+        float gj[4] = {0.f, 0.f, 0.f, 0.f};   // gated: G of this lane's query rows
+        float l2chunk;
+        if constexpr (GATED) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) gj[mt] = gl[mt * 16 + l16];
+            l2chunk = gl[L - 1];
+        } else {
+            l2chunk = static_cast<float>(L) * lg;
+        }
+        const float lkx = lk2;
+        lk2 += l2chunk;
+
+        if (!sonly) {
+            // cross term X^T = S^T Q^T over the chunk's 64 query rows
+            {
+                u16x8_t qa[4], qn[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) qa[mt] = lds16a(qbase + pq[0] + mt * 16 * QRB);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            qn[mt] = lds16a(qbase + pq[(ks + 1) % KL] + mt * 16 * QRB + ((ks + 1) / KL) * 256);
+                    }
+                    const u16x4_t a0 = bf4(S[2 * ks]), a1 = bf4(S[2 * ks + 1]);
+                    const u16x8_t b = (g4 & 1) ? cat(a1, a0) : cat(a0, a1);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        X[mt] = mfma16(b, qa[mt], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : X[mt]);
+                    if (has_next) copy_slice(0, kCrossOps, ks, KS);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) qa[mt] = qn[mt];
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const float xi = GATED ? exp2_fast(gj[mt] + lkx) : fxi[mt] * exp2_fast(lkx);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) X[mt][i] *= xi;
+                }
+            }
+
+            // this wave's score tiles (K Q^T), decayed and rounded to bf16, into the P area
+#pragma unroll
+            for (int s16 = 0; s16 < 2; ++s16) {
+                const int qt = tq[s16], kt = tk[s16];
+                if (kt > qt) continue;   // above the diagonal: never written, stays zero
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                u16x8_t kf[KS], qf[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS && ks < 2; ++ks) {
+                    kf[ks] = lds16a(kbase + pq[ks % KL] + kt * 16 * QRB + (ks / KL) * 256);
+                    qf[ks] = lds16a(qbase + pq[ks % KL] + qt * 16 * QRB + (ks / KL) * 256);
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 2 < KS) {
+                        kf[ks + 2] = lds16a(kbase + pq[(ks + 2) % KL] + kt * 16 * QRB + ((ks + 2) / KL) * 256);
+                        qf[ks + 2] = lds16a(qbase + pq[(ks + 2) % KL] + qt * 16 * QRB + ((ks + 2) / KL) * 256);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc = mfma16(kf[ks], qf[ks], acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int j = qt * 16 + l16;   // query row (chunk-local)
+                float w[4];
+                if constexpr (GATED) {
+                    const f32x4_t gk = *reinterpret_cast<const f32x4_t*>(gl + kt * 16 + 4 * g4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w[i] = kt == qt && 4 * g4 + i > l16 ? 0.f : exp2_fast(gj[qt] - gk[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = ws[s16][i];
+                }
+                if (!full) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kt * 16 + 4 * g4 + i >= L || j >= L) w[i] = 0.f;
+                }
+                const u16x4_t p = bf4(f32x4_t{acc[0] * w[0], acc[1] * w[1], acc[2] * w[2], acc[3] * w[3]});
+                *reinterpret_cast<u16x4_t*>(smem + L_::kP + ((qt * 2 + (kt >> 1)) * 64 + lane) * 16 + (kt & 1) * 8) = p;
+            }
+            // every wave is past its Q reads and P is complete
+            lds_barrier();
+
+        }
+
+        // the state update; a state-only step issues all of the next chunk's copies
+        // between its products, a full step with one Q stage the Q copies
+        state_update(kbase, vbase, gl, L, full, [&](int kh, int gi, int ng) {
+            if (!has_next) return;
+            if (sonly) copy_slice(0, kOps, kh * ng + gi, 2 * ng);
+            else if (QS == 1 && kh == 0) copy_slice(kCrossOps, kOps, gi, ng);
+        });
+        if (sonly) {
+            if (has_next) g_scan(1 - ST);
+            return has_next;
+        }
+
+        // X += P V over the chunk's 64 keys (as X^T += V^T P^T); V fragments by transpose
+        // reads: slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u16x8_t bv = cat(lds_tra(vbase + pvp + ks * 32 * VRB), lds_tra(vbase + pvp + (ks * 32 + 16) * VRB));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (2 * ks > mt) continue;   // key tiles above row tile mt are zero
+                const u16x8_t a = lds16a(lds0 + L_::kP + ((mt * 2 + ks) * 64 + lane) * 16);
+                X[mt] = mfma16(bv, a, X[mt]);
+            }
+        }
+
+        // gated: wave 0 forms the next chunk's prefix sums (its decays were loaded at the
+        // top of the step; the next barrier publishes them)
+        if (has_next) g_scan(1 - ST);
+
+        // the output block: staged when more chunks follow (stored after the next
+        // barrier), else stored from registers (rows past the chunk end skipped)
+        if (full && has_next) {
+            stage_write();
+            xs_row = cs;
+        } else {
+            bf16_t* const base = o + v_bh + static_cast<size_t>(cs) * dv + col0 + wcol + 4 * g4;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int row = mt * 16 + l16;
+                if (row < L) *reinterpret_cast<u16x4_t*>(base + static_cast<uint32_t>(row * dv)) = bf4(X[mt]);
+            }
+        }
+        return has_next;
+    };
+
+    for (int c = 0;; c += 2) {
+        if (!step(std::integral_constant<int, 0>{}, c)) break;
+        if (!step(std::integral_constant<int, 1>{}, c + 1)) break;
+    }
+
+    // ---- final state (last segment only), through LDS in whole rows of 16-byte stores
+    if (seg == nseg - 1 && ka.state_out != nullptr) {
+        float* const st = reinterpret_cast<float*>(smem);
+        const float r = exp2_fast(lk2);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();   // every wave is done with the tile buffers
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[srow(dt, i) * DVT + wcol + l16] = S[dt][i] * r;
+        lds_barrier();
+        constexpr int kU = DVT / 4;                        // 16-byte units per row
+        constexpr int kRounds = DK * kU / (NW * 64);
+        static_assert(kRounds * NW * 64 == DK * kU, "state rows must split evenly");
+        float* const dst = ka.state_out + s_bh;
+#pragma unroll
+        for (int rr = 0; rr < kRounds; ++rr) {
+            const int e = rr * NW * 64 + tid;
+            const int row = e / kU, u = e % kU;
+            *reinterpret_cast<f32x4_t*>(dst + static_cast<size_t>(row) * dv + col0 + u * 4) =
+                *reinterpret_cast<const f32x4_t*>(st + row * DVT + u * 4);
+        }
+    }
+}
+
+template <int DK, bool GATED>
+hipError_t launch_c1(const KArgs& ka, hipStream_t stream) {
+    constexpr size_t lds = C1Lds<DK, GATED>::kBytes;
+    static std::once_flag attr_once;   // thread-safe one-time init of the LDS limit
+    std::call_once(attr_once, [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    });
+    ProfScope prof(kProfMain, stream);
+    hipLaunchKernelGGL((chunk1_kernel<DK, GATED>), dim3(ka.total_groups), dim3(kC1Waves * 64), lds, stream, ka);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse) {
+    return chunk == kBlk && (dk == 128 || dk == 256) && dv % kC1Cols == 0 && ldqk == dk && ldv == dv &&
+           slices <= 1 && !out_f32 && !reverse;
+}
+
+hipError_t launch_chunk1(const KArgs& ka, bool gated, hipStream_t stream) {
+    if (ka.dk == 256) return gated ? launch_c1<256, true>(ka, stream) : launch_c1<256, false>(ka, stream);
+    if (ka.dk == 128) return gated ? launch_c1<128, true>(ka, stream) : launch_c1<128, false>(ka, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace retn

@@ -70,10 +70,20 @@ struct MfmaPlan {
     int pre_dkt;      // state rows per workgroup of the segment-state pre-pass
     int pre_dvt;      // state columns per workgroup of the pre-pass
     int fuse_scan;    // 1: the main pass composes segment entry states itself
+    // > 0: two segments split at this token; the second segment's workgroups walk the
+    // first segment's tokens state-only before their own (no pre-pass, no workspace)
+    int prefix_tokens;
     size_t workspace_bytes;
 };
-MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated);
+// c64_fwd: the caller runs the forward with 64-token chunks on the single-block main
+// pass (contiguous rows, bf16 output, one slice), which can take a prefix split.
+MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool c64_fwd = false);
 hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream_t stream);
+// Main pass for chunks of exactly 64 tokens (chunk64.hip): forward, bf16 output,
+// contiguous rows, one slice, d_k 128 or 256, d_v a multiple of 128.
+struct KArgs;
+bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse);
+hipError_t launch_chunk1(const KArgs& ka, bool gated, hipStream_t stream);
 // Parallel form on the matrix cores (no state): O = (Q K^T (.) D) V with the query blocks
 // of a (b,h) in parallel workgroups.
 bool mfma_parallel_supported(int dk, int dv, int N, bool gated, bool bf16);

@@ -39,6 +39,7 @@
 // (section Triton 内核与自校验测试).
 
 #include "cdna4.h"
+#include "chunk_tiles.h"
 #include "common.h"
 #include "launch.h"
 
@@ -49,52 +50,15 @@ namespace retn {
 
 namespace {
 
-constexpr int kBlk = 64;       // tokens per LDS block
-constexpr int kMaxChunk = 512;
 constexpr int kTargetGroups = 256;
 // Up to this many segments the main pass composes its entry state from the local
 // segment states itself (segment s reads s of them); beyond, a scan kernel does it.
 // (Measured: 8 saves the scan launch on the gated workload, 7 us of 117; with 16
 // segments the longest composition costs as much as the scan.)
 constexpr int kFuseScanMax = 8;
-
-// Row swizzles: the 16-byte unit u of row r is stored at unit u ^ swz(r).  LDS serves
-// 256 bytes per clock from 64 four-byte banks: a 16-byte-per-lane read in groups of 16
-// lanes, an 8-byte (or 8-byte transpose) read in groups of 32 lanes; a group is
-// conflict free when its lanes cover distinct banks.
-//   Q and K (row = token, units over the head dimension): score and cross-term reads
-//   take one unit from 16 consecutive rows, so swz must be distinct on them; the
-//   transposed K reads of the state update take 8 bytes from rows {0..3, 8..11} (or
-//   {4..7, 12..15}) with the two 8-byte halves alternating over the lanes of a row, so
-//   rows of such a set must land in distinct 32-byte pairs (or opposite halves).
-//   With 16+ units per row, swz(r) = r with bits 1 and 2 exchanged does both; with 8
-//   units per row (two rows per bank cycle), (r >> 1) & 7.
-//   V (row = token, units over state columns): transposed reads take one 32-byte pair
-//   from rows {0..7} (P V) or {0..3, 8..11} (state update), so swz = 2 g(r) with
-//   g(r) = (r & 3) | (bit 2 ^ bit 3 of r) << 2 is distinct on both; with 8 units per
-//   row, 2 (g(r) >> 1).
-template <int UPR>
-__device__ __forceinline__ int swz_qk(int r) {
-    if (UPR >= 16) return (r & 9) | ((r & 4) >> 1) | ((r & 2) << 1);
-    return (r >> 1) & 7;
-}
-template <int UPR>
-__device__ __forceinline__ int swz_v(int r) {
-    const int g = (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
-    return UPR >= 16 ? 2 * g : 2 * (g >> 1);
-}
-
-template <int RB>   // row bytes
-__device__ __forceinline__ int qk_off(int row, int unit) {
-    return row * RB + ((unit ^ swz_qk<RB / 16>(row)) << 4);
-}
-template <int RB>
-__device__ __forceinline__ int v_off(int row, int unit) {
-    return row * RB + ((unit ^ swz_v<RB / 16>(row)) << 4);
-}
-
-constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
-constexpr int kPBytes = 4 * 2 * 64 * 16;   // P fragments [4 qt][2 key pairs][64 lanes][16 B]
+// Time of a state-only step (the state update of one 64-token chunk) relative to a full
+// step of the single-block main pass, for the prefix split of two segments.
+constexpr double kPrefixCost = 0.4;
 
 // LDS layout: QS stages of Q (full pass only), NST stages of K and V blocks and of the
 // decays the block's step loads (gated: the pre-pass copies its block's 64 decays once
@@ -122,62 +86,6 @@ struct Lds {
     static constexpr int kBytes = kG + kGBytes;
 };
 
-// A buffer offset past every range this file builds (ranges stay below 2^31 bytes for
-// reversed walks): loads from it return zeros.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-// Asynchronous copy of one 64-row tile (row bytes RB) of a row-major matrix with row
-// stride `sb` bytes.  Each wave issues kChunks/4 instructions of 1 KB; lane l of
-// instruction i fills LDS bytes [c*1024 + 16 l, +16) with c = wave + 4 i, i.e. row
-// (c*1024 + 16 l) / RB and the 16-byte unit whose swizzled position that is.
-// REV: the walk runs over the time-reversed sequence, so LDS row r of the block at
-// walk position t0 holds matrix row N-1-t0-r.
-template <int RB, bool VSWZ, int NW, bool REV = false>
-struct TileCopy {
-    static constexpr int kChunks = kBlk * RB / 1024;
-    static constexpr int kPerWave = kChunks / NW;
-    static_assert(kChunks % NW == 0, "tile must split evenly over the waves");
-    // byte offset of this lane's unit relative to the block's first row; REV: the
-    // offset of row N-1-r (negative, as a two's complement, when r > N-1)
-    uint32_t voff[kPerWave];
-
-    __device__ __forceinline__ void init(int sb, int wave, int lane, int N) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            const int c = wave + i * NW;
-            const int off = c * 1024 + lane * 16;
-            const int r = off / RB, p = (off % RB) >> 4;
-            const int u = p ^ (VSWZ ? swz_v<RB / 16>(r) : swz_qk<RB / 16>(r));
-            voff[i] = static_cast<uint32_t>((REV ? N - 1 - r : r) * sb + u * 16);
-        }
-        (void)N;
-    }
-    // Offset and wave-uniform base of copy i for the block at row0 (bytes row0*sb).
-    // Forward: the base carries the block; REV: the lane offset does, and a row before
-    // the sequence start (negative offset) is sent out of range.
-    __device__ __forceinline__ uint32_t lane_off(int i, uint32_t row0_bytes) const {
-        if constexpr (REV) {
-            const int d = static_cast<int>(voff[i]) - static_cast<int>(row0_bytes);
-            return d < 0 ? kOutOfRange : static_cast<uint32_t>(d);
-        } else {
-            return voff[i];
-        }
-    }
-    __device__ __forceinline__ static uint32_t base_off(uint32_t row0_bytes) { return REV ? 0u : row0_bytes; }
-    // Rows past the end of the tensor lie outside the buffer's range and land in LDS
-    // as zeros, so every LDS row holds finite data; uses mask those rows.
-    __device__ __forceinline__ void issue(uint32_t tile_lds, const u32x4_t& rsrc, uint32_t row0_bytes,
-                                          int wave) const {
-        const uint32_t base = tile_lds + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i)
-            buf2lds16(rsrc, lane_off(i, row0_bytes), base_off(row0_bytes), base + i * NW * 1024u);
-    }
-    // copy i of this wave alone; wbase = tile_lds + 1024 * wave
-    __device__ __forceinline__ void issue_one(int i, uint32_t wbase, const u32x4_t& rsrc, uint32_t row0_bytes) const {
-        buf2lds16(rsrc, lane_off(i, row0_bytes), base_off(row0_bytes), wbase + i * NW * 1024u);
-    }
-};
 enum Mode { kFull = 0, kStateOnly = 1 };
 // Pipeline stages: the pre-pass keeps four blocks in flight.  The full pass
 // double-buffers: a third stage (which fits for d_k <= 128) measured 4-8% slower on
@@ -206,12 +114,6 @@ struct Plan {
     using L = std::conditional_t<kQ1, L1, std::conditional_t<kQ2, L2, Lds<DK, DVT, GATED, MODE == kFull, NST, NW>>>;
 };
 
-// The 16 score tiles of a 64x64 block as qt*4+kt, causal (kt <= qt) ones first:
-// 0,4,5,8,9,10,12,13,14,15, then 1,2,3,6,7,11 (one 4-bit entry per slot).
-__device__ __forceinline__ int tile_order(int slot) {
-    return static_cast<int>((0xB76321FEDCA98540ULL >> (4 * slot)) & 15);
-}
-
 // Position in the walk over a segment: chunk start cs, query block qb, key block kb.
 struct Step {
     int cs, qb, kb;
@@ -231,30 +133,6 @@ __device__ __forceinline__ bool next_step(Step& s, int t_end, int C) {
     s.kb = 0;
     return s.cs < t_end;
 }
-
-// Kernel arguments (one struct, passed by value).
-struct KArgs {
-    const bf16_t* q;
-    const bf16_t* k;
-    const bf16_t* v;
-    const float* decay;      // gamma [H] or g [B,H,N]
-    void* o;                 // bf16, or fp32 for the fp32-output variant
-    const float* state_in;   // [B,H,dk,dv] or null (zeros)
-    float* state_out;        // [B,H,dk,dv] or null
-    float* seg_state;        // workspace [B*H][nseg][dk][dv]: local, then (scanned) entry states
-    float* seg_log2;         // workspace [B*H][nseg]: log2 of each segment's total decay
-    int H, N, dk, dv, C;
-    int ldqk, ldv;           // row strides (elements) of q and k, and of v; o is contiguous
-    int seg_tokens, nseg;    // sequence split: tokens per segment, segments per (b,h)
-    int ndvt, ndkt;          // column tiles and (pre-pass) state-row tiles per (b,h)
-    int total_groups;
-    int fuse_scan;           // main pass: compose the entry state from the local states
-    // column slices run as extra chains: chain c is (b,h) = c / nsl and slice c % nsl,
-    // whose q/k rows start sl_qk elements further, whose output starts sl_o elements
-    // further and whose state_in / state_out start sl_state floats further
-    int nsl, sl_qk;
-    size_t sl_o, sl_state;
-};
 
 // Main kernel (MODE = kFull) and segment-state pre-pass (MODE = kStateOnly).
 //   Main pass: state rows = all dk (DK == dk); a workgroup per (b,h), segment, column
@@ -1257,9 +1135,11 @@ hipError_t launch_pre(KArgs ka, const MfmaPlan& p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int DK, int DVT, int NW, bool GATED, bool ONEBLK, bool OF32, bool REV>
-hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
-    KArgs ka{};
+// Kernel arguments of the main pass, after the segment-state pre-pass and (when the
+// main pass does not compose the entry states itself) the scan have been launched.
+template <bool GATED, bool REV>
+hipError_t launch_prep(const ChunkArgs& a, const MfmaPlan& p, int dvt, hipStream_t stream, KArgs& ka) {
+    ka = KArgs{};
     ka.q = static_cast<const bf16_t*>(a.q);
     ka.k = static_cast<const bf16_t*>(a.k);
     ka.v = static_cast<const bf16_t*>(a.v);
@@ -1281,8 +1161,9 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
     ka.sl_qk = a.slice_qk;
     ka.sl_o = a.slice_o;
     ka.sl_state = a.slice_state;
+    ka.pre_tokens = p.prefix_tokens;
     const int bh = a.B * a.H * ka.nsl;   // chains
-    if (p.nseg > 1) {
+    if (p.nseg > 1 && p.prefix_tokens == 0) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
         ka.seg_state = static_cast<float*>(a.workspace);
         ka.seg_log2 = ka.seg_state + static_cast<size_t>(bh) * p.nseg * per_bh;
@@ -1301,9 +1182,33 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
         }
     }
     ka.ndkt = 1;
-    ka.ndvt = a.dv / DVT;
+    ka.ndvt = a.dv / dvt;
     ka.total_groups = bh * p.nseg * ka.ndvt;
+    return hipSuccess;
+}
+
+template <int DK, int DVT, int NW, bool GATED, bool ONEBLK, bool OF32, bool REV>
+hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    KArgs ka;
+    const hipError_t e = launch_prep<GATED, REV>(a, p, DVT, stream, ka);
+    if (e != hipSuccess) return e;
     return launch_kernel<DK, DVT, NW, GATED, kFull, ONEBLK, OF32, REV>(ka, stream);
+}
+
+// Chunks of exactly 64 tokens take the leaner single-block main pass (chunk64.hip).
+template <bool REV>
+hipError_t launch_chunk64(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    KArgs ka;
+    const hipError_t e = launch_prep<false, REV>(a, p, p.dvt, stream, ka);
+    if (e != hipSuccess) return e;
+    return launch_chunk1(ka, false, stream);
+}
+template <bool REV>
+hipError_t launch_chunk64_gated(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    KArgs ka;
+    const hipError_t e = launch_prep<true, REV>(a, p, p.dvt, stream, ka);
+    if (e != hipSuccess) return e;
+    return launch_chunk1(ka, true, stream);
 }
 
 // State columns per workgroup and waves per workgroup for a head shape.
@@ -1314,6 +1219,8 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
 // registers freed by single-block chunks.
 void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
     if (dk == 256 && !gated && dv % 128 == 0 && chunk <= kBlk) { dvt = 128; nw = 8; return; }
+    // 64-token chunks, gated: the single-block main pass fits 128 columns
+    if (dk == 256 && gated && dv % 128 == 0 && chunk == kBlk) { dvt = 128; nw = 8; return; }
     if (dk == 256) { dvt = 64; nw = 4; return; }
     if (dv % 128 == 0) { dvt = 128; nw = 8; return; }
     dvt = 64;
@@ -1329,7 +1236,7 @@ bool mfma_chunk_supported(int dk, int dv, int chunk, bool bf16) {
     return chunk >= 1 && chunk <= kMaxChunk;
 }
 
-MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated) {
+MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool c64_fwd) {
     MfmaPlan p{};
     pick_tile(dk, dv, chunk, gated, p.dvt, p.nw);
     const long bh = static_cast<long>(B) * H;
@@ -1342,6 +1249,20 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     p.pre_dkt = std::min(dk, 128);
     p.pre_dvt = dv % 128 == 0 ? 128 : 64;
     p.fuse_scan = p.nseg <= kFuseScanMax ? 1 : 0;
+    p.prefix_tokens = 0;
+    if (c64_fwd && p.nseg == 2 && chunk == kBlk && p.dvt == 128 && nchunks >= 4 &&
+        chunk1_supported(dk, dv, chunk, dk, dv, 1, false, false)) {
+        // Two segments: the second segment's workgroups compute their entry state by
+        // walking the first segment state-only, which costs about kPrefixCost of a full
+        // step per chunk; the first segment is made longer so both finish together.
+        int sp = static_cast<int>(nchunks / (2.0 - kPrefixCost) + 0.5);
+        sp = std::max(1, std::min(sp, nchunks - 1));
+        p.prefix_tokens = sp * kBlk;
+        p.seg_chunks = sp;
+        p.fuse_scan = 0;
+        p.workspace_bytes = 0;
+        return p;
+    }
     if (p.nseg > 1) {
         const size_t per_bh = static_cast<size_t>(dk) * dv;
         p.workspace_bytes = (static_cast<size_t>(bh) * p.nseg * per_bh + static_cast<size_t>(bh) * p.nseg) * sizeof(float);
@@ -1368,8 +1289,14 @@ hipError_t launch_variant(const ChunkArgs& a, const MfmaPlan& p, bool one, hipSt
 template <bool REV>
 hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     // the kernel handles any chunk in [1, 512], including chunks that are not a
-    // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant
+    // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant, and
+    // chunks of exactly one block (forward, bf16 output) the single-block main pass
     const bool one = a.chunk <= kBlk;
+    if (p.dvt == 128 && p.nw == 8 &&
+        chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
+                         a.out_f32, a.reverse))
+        return a.gated ? launch_chunk64_gated<REV>(a, p, stream) : launch_chunk64<REV>(a, p, stream);
+    if (p.prefix_tokens > 0) return hipErrorInvalidValue;   // only the single-block pass walks prefixes
 #define RETN_SHAPE(DK, DVT, NW) \
     if (a.dk == DK && p.dvt == DVT && p.nw == NW) return launch_variant<DK, DVT, NW, REV>(a, p, one, stream);
     RETN_SHAPE(64, 64, 4)

@@ -102,6 +102,9 @@ def test_workspace_query(L):
     assert L.retention_workspace_bytes(1, 2, 64, 16, 16, 16, 0, 0) == 0
     # a short sequence with enough (b,h) x column tiles runs unsplit
     assert L.retention_workspace_bytes(16, 16, 2048, 128, 128, 64, 1, 0) == 0
+    # two segments of 64-token chunks: the second walks the first state-only, no workspace
+    assert L.retention_workspace_bytes(4, 8, 2048, 256, 512, 64, 1, 0) == 0
+    assert L.retention_workspace_bytes(2, 8, 2048, 128, 1024, 64, 1, 1) == 0
     # long sequences with few heads are split; workspace holds one fp32 state per segment
     ws = L.retention_workspace_bytes(1, 16, 16384, 128, 128, 512, 1, 0)
     assert ws >= 2 * 16 * 128 * 128 * 4

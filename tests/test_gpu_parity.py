@@ -103,6 +103,10 @@ SMALL = [
     (1, 1, 200, 128, 1024, 64, "bf16", False, True),     # the widest d_v: eight column tiles
     (1, 1, 150, 64, 1024, 64, "bf16", True, False),
     (1, 1, 130, 256, 1024, 64, "bf16", False, True),     # the largest state, 256 x 1024
+    # two segments where the second walks the first state-only (prefix split)
+    (1, 16, 600, 128, 1024, 64, "bf16", False, True),
+    (2, 8, 450, 128, 1024, 64, "bf16", True, True),
+    (1, 32, 300, 256, 512, 64, "bf16", False, True),     # ragged last chunk
 ]
 
 
