@@ -183,6 +183,24 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         const int svp = swz_v<VRB / 16>(rbp);
         pvp = static_cast<uint32_t>(rbp * VRB + 16 * (2 * (wave ^ (svp >> 1)) + (trq >> 1)) + 8 * (trq & 1));
     }
+    // Absolute per-lane LDS addresses of the patterns, one register each, so that every
+    // stage, tile and reduction-step offset is an immediate of the read (below 64 KB).
+    uint32_t aq[KL], ak[KL], akt[2][SL][2], avs[2];
+#pragma unroll
+    for (int kl = 0; kl < KL; ++kl) {
+        aq[kl] = opaque(lds0 + L_::kQ + pq[kl]);
+        ak[kl] = opaque(lds0 + L_::kK + pq[kl]);
+    }
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) akt[pl][sl][hb] = opaque(lds0 + L_::kK + pkt[pl][sl][hb]);
+        avs[pl] = opaque(lds0 + L_::kV + pvs[pl]);
+    }
+    const uint32_t avp = opaque(lds0 + L_::kV + pvp);
+    const uint32_t ap = opaque(lds0 + L_::kP + static_cast<uint32_t>(lane) * 16u);
 
     // ---- decays of a full chunk (per head), computed once.  Every exponent is >= 0,
     // so no factor exceeds 1.
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
     // The state update over the chunk's L keys (full: L = 64), after the caller has
     // added the chunk's decay to lk2.
-    auto state_update = [&](uint32_t kbase, uint32_t vbase, const float* gl, int L, bool full, auto hook) {
+    auto state_update = [&](uint32_t koff, uint32_t voff, const float* gl, int L, bool full, auto hook) {
         // rescale the registers once the state scale gets small (after the cross term,
         // which reads them at the old scale)
         if (lk2 < -64.f) {
@@ -334,12 +352,12 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             for (int kh = 0; kh < 2; ++kh) {
                 auto kt_frag = [&](int dt) -> u16x8_t {
                     const int sd = dt >> 1;
-                    const uint32_t off = kbase + kh * 32 * QRB + (sd / SL) * 256;
-                    return cat(lds_tra(pkt[0][sd % SL][dt & 1] + off), lds_tra(pkt[1][sd % SL][dt & 1] + off));
+                    const uint32_t off = koff + kh * 32 * QRB + (sd / SL) * 256;
+                    return cat(lds_tra(akt[0][sd % SL][dt & 1] + off), lds_tra(akt[1][sd % SL][dt & 1] + off));
                 };
                 constexpr int G = DT < 4 ? DT : (DT >= 16 ? 2 : 4);
                 u16x8_t acur[G], anext[G];
-                const u16x8_t raw = cat(lds_tra(vbase + pvs[0] + kh * 32 * VRB), lds_tra(vbase + pvs[1] + kh * 32 * VRB));
+                const u16x8_t raw = cat(lds_tra(avs[0] + voff + kh * 32 * VRB), lds_tra(avs[1] + voff + kh * 32 * VRB));
 #pragma unroll
                 for (int jj = 0; jj < G; ++jj) acur[jj] = kt_frag(jj);
                 __builtin_amdgcn_sched_barrier(0);
@@ -411,9 +429,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         const bool has_next = c + 1 < ntot;
         const bool next_q = c + 1 >= npre;      // the next chunk is a full step: copy its Q
         const uint32_t next_row = static_cast<uint32_t>(chunk_row(c + 1));
-        const uint32_t qbase = lds0 + L_::kQ + QB * L_::kQTile;
-        const uint32_t kbase = lds0 + L_::kK + ST * L_::kKTile;
-        const uint32_t vbase = lds0 + L_::kV + ST * L_::kVTile;
+        constexpr uint32_t qoff = QB * L_::kQTile, koff = ST * L_::kKTile, voff = ST * L_::kVTile;
         const float* const gl = reinterpret_cast<const float*>(smem + L_::kG) + ST * kBlk;
         // copy op i of the next chunk (every index is tested by the callers' unrolled
         // loops, so each copy's offset register is a constant)
@@ -456,13 +472,13 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             {
                 u16x8_t qa[4], qn[4];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) qa[mt] = lds16a(qbase + pq[0] + mt * 16 * QRB);
+                for (int mt = 0; mt < 4; ++mt) qa[mt] = lds16a(aq[0] + qoff + mt * 16 * QRB);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     if (ks + 1 < KS) {
 #pragma unroll
                         for (int mt = 0; mt < 4; ++mt)
-                            qn[mt] = lds16a(qbase + pq[(ks + 1) % KL] + mt * 16 * QRB + ((ks + 1) / KL) * 256);
+                            qn[mt] = lds16a(aq[(ks + 1) % KL] + qoff + mt * 16 * QRB + ((ks + 1) / KL) * 256);
                     }
                     const u16x4_t a0 = bf4(S[2 * ks]), a1 = bf4(S[2 * ks + 1]);
                     const u16x8_t b = (g4 & 1) ? cat(a1, a0) : cat(a0, a1);
@@ -492,14 +508,14 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
                 u16x8_t kf[KS], qf[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS && ks < 2; ++ks) {
-                    kf[ks] = lds16a(kbase + pq[ks % KL] + kt * 16 * QRB + (ks / KL) * 256);
-                    qf[ks] = lds16a(qbase + pq[ks % KL] + qt * 16 * QRB + (ks / KL) * 256);
+                    kf[ks] = lds16a(ak[ks % KL] + koff + kt * 16 * QRB + (ks / KL) * 256);
+                    qf[ks] = lds16a(aq[ks % KL] + qoff + qt * 16 * QRB + (ks / KL) * 256);
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     if (ks + 2 < KS) {
-                        kf[ks + 2] = lds16a(kbase + pq[(ks + 2) % KL] + kt * 16 * QRB + ((ks + 2) / KL) * 256);
-                        qf[ks + 2] = lds16a(qbase + pq[(ks + 2) % KL] + qt * 16 * QRB + ((ks + 2) / KL) * 256);
+                        kf[ks + 2] = lds16a(ak[(ks + 2) % KL] + koff + kt * 16 * QRB + ((ks + 2) / KL) * 256);
+                        qf[ks + 2] = lds16a(aq[(ks + 2) % KL] + qoff + qt * 16 * QRB + ((ks + 2) / KL) * 256);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     acc = mfma16(kf[ks], qf[ks], acc);
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
         // the state update; a state-only step issues all of the next chunk's copies
         // between its products, a full step with one Q stage the Q copies
-        state_update(kbase, vbase, gl, L, full, [&](int kh, int gi, int ng) {
+        state_update(koff, voff, gl, L, full, [&](int kh, int gi, int ng) {
             if (!has_next) return;
             if (sonly) copy_slice(0, kOps, kh * ng + gi, 2 * ng);
             else if (QS == 1 && kh == 0) copy_slice(kCrossOps, kOps, gi, ng);
@@ -545,11 +561,11 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // reads: slots {4g..4g+3} of key tile 2ks and of key tile 2ks+1
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const u16x8_t bv = cat(lds_tra(vbase + pvp + ks * 32 * VRB), lds_tra(vbase + pvp + (ks * 32 + 16) * VRB));
+            const u16x8_t bv = cat(lds_tra(avp + voff + ks * 32 * VRB), lds_tra(avp + voff + (ks * 32 + 16) * VRB));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (2 * ks > mt) continue;   // key tiles above row tile mt are zero
-                const u16x8_t a = lds16a(lds0 + L_::kP + ((mt * 2 + ks) * 64 + lane) * 16);
+                const u16x8_t a = lds16a(ap + (mt * 2 + ks) * 1024);
                 X[mt] = mfma16(bv, a, X[mt]);
             }
         }

@@ -58,7 +58,7 @@ constexpr int kTargetGroups = 256;
 constexpr int kFuseScanMax = 8;
 // Time of a state-only step (the state update of one 64-token chunk) relative to a full
 // step of the single-block main pass, for the prefix split of two segments.
-constexpr double kPrefixCost = 0.4;
+constexpr double kPrefixCost = 0.5;
 
 // LDS layout: QS stages of Q (full pass only), NST stages of K and V blocks and of the
 // decays the block's step loads (gated: the pre-pass copies its block's 64 decays once
