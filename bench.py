@@ -2,6 +2,7 @@
 """Benchmark of the retention operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+                    [--only NAME] [--calib-copy] [--calib-mfma]
 
 Headline workload (one "step" = one chunkwise forward over one batch, i.e. every stage
 of the chunkwise hot path: tile staging, decay generation, intra-chunk scores and
@@ -21,14 +22,21 @@ sequences (with the chunkwise form on the same inputs beside it), and the gated
 retention layer around the operator (B=4 N=2048 D=1024 H=8 d=128; TFLOP/s of its six
 projections over the layer's time).
 
-"roofline" describes the dominant kernel of the headline step, the matrix-core
-chunkwise pass (a step also runs the segment-state pre-pass): algorithmic bytes (Q, K,
-V read once, O written once) per launch / its average launch time, measured with HIP
-events the library records around each of its launches on the launch stream
+"roofline" describes the dominant kernel of the headline step, the single-block
+matrix-core chunkwise pass (the headline's one launch per step): algorithmic bytes (Q,
+K, V read once, O written once) per launch / its average launch time, measured with
+HIP events the library records around each of its launches on the launch stream
 (retention_profile_enable / retention_profile_read) over a second timed run of the
 same steps, against 8 TB/s.  "traffic" is HBM bytes per launch from the committed
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the copy-kernel calibration
-factor, or null when the kernel source changed since it was taken.
+factor, and "mfma_busy_counter" the matrix-core busy fraction from the committed
+rocprofv3 counters (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs); both are
+null when the kernel source changed since they were taken.
+"timing" adds per-call HIP-event times of the headline (median, minimum, mean, p90 over
+at least 100 calls), back to back and with a 1 GiB write before each call that evicts
+the inputs from the MALL and L2; the decode lines add the per-step distribution.
+"achievable" is measured context: the library's matrix-core loop (no memory traffic)
+and a plain device copy, against the spec peaks.
 "cpu_baseline" times the fp64 oracle (recurrent form, numpy) on a bounded sample of
 the same workload on the host.
 """
@@ -50,7 +58,9 @@ METRIC = "chunkwise retention fwd tokens/s & % MFMA peak; decode-step HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_bf16_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "retnet_retention_fwd_amd", "csrc", "mfma_chunk.hip")
+# source of the headline's dominant kernel (the single-block chunkwise pass)
+KERNEL_SRC = os.path.join(ROOT, "retnet_retention_fwd_amd", "csrc", "chunk64.hip")
+HEADLINE_KERNEL = "chunk1_kernel<256, false> (single-block matrix-core chunkwise pass)"
 
 
 def kernel_hash() -> str:
@@ -85,6 +95,61 @@ def time_steps(fn, steps, warmup, torch):
     return t0.elapsed_time(t1) / 1e3, wall     # seconds (events), seconds (host clock)
 
 
+def stats(ms_list):
+    """Median, minimum, mean and 90th percentile of per-call times (microseconds)."""
+    xs = sorted(1e3 * x for x in ms_list)
+    n = len(xs)
+    return {"calls": n, "median_us": round(xs[n // 2], 3), "min_us": round(xs[0], 3),
+            "mean_us": round(sum(xs) / n, 3), "p90_us": round(xs[min(n - 1, int(0.9 * n))], 3)}
+
+
+def per_call_times(step, n, torch, flush_buf=None):
+    """HIP-event time of each of n calls on the current stream (milliseconds).  With
+    flush_buf, a write of that buffer (1 GiB) before each call, outside its events,
+    evicts the inputs from the MALL and the L2."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0x7F)
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def achievable(torch, R):
+    """Achievable-peak context measured in this run: the library's matrix-core loop
+    (bf16, no memory traffic) and a plain 1 GiB device copy (read + write)."""
+    out = torch.empty(256 * 8, dtype=torch.float32, device="cuda")
+    iters = 2000
+    R.calib_mfma(256, 8, 50, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    flops = 0.0
+    for _ in range(5):
+        flops += R.calib_mfma(256, 8, iters, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    a = torch.empty(1 << 28, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return {"mfma_loop_TFLOPs": round(mfma_tflops, 1), "mfma_loop_frac_of_spec": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+            "copy_GBps": round(copy_gbps, 1), "copy_frac_of_spec": round(copy_gbps / HBM_PEAK_GBS, 4),
+            "what": "bf16 16x16x32 matrix-core loop (256 workgroups x 8 waves, 16 independent accumulators per "
+                    "wave, no memory traffic); torch copy_ of 1 GiB fp32 (read + write bytes)"}
+
+
 def chunk_inputs(torch, B, H, N, dk, dv, gated, sets, seed):
     """Seeded synthetic inputs on the GPU: Q,K,V ~ N(0,1)/sqrt(dk) in bf16; per-head
     gammas or g = logsigmoid(x)/16.  `sets` independent copies to rotate through."""
@@ -106,7 +171,7 @@ def chunk_inputs(torch, B, H, N, dk, dv, gated, sets, seed):
 
 
 def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps, warmup, seed,
-                       kernel_times=False):
+                       kernel_times=False, dist_calls=0):
     per_set = alg_bytes(B, H, N, dk, dv, gated)
     sets = max(2, min(8, int(math.ceil(768e6 / per_set))))
     data = chunk_inputs(torch, B, H, N, dk, dv, gated, sets, seed)
@@ -133,6 +198,14 @@ def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps,
         kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / v["launches"], 3)}
                    for k, v in prof.items() if k != "dropped" and v["launches"] > 0}
         kernels["dropped"] = prof["dropped"]
+    dist = None
+    if dist_calls > 0:
+        # per-call times: back to back (inputs rotated as in the timed steps), and with
+        # the MALL and L2 flushed by a 1 GiB write before each call
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dist = {"unflushed": stats(per_call_times(step, dist_calls, torch)),
+                "flushed": stats(per_call_times(step, dist_calls, torch, flush))}
+        del flush
     per = t / steps
     nb = alg_bytes(B, H, N, dk, dv, gated)
     fl = alg_flops(B, H, N, dk, dv, C)
@@ -142,6 +215,7 @@ def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps,
         "alg_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS,
         "alg_TFLOPs": fl / per / 1e12, "mfma_frac": fl / per / 1e12 / BF16_PEAK_TFLOPS,
         "input_sets": sets, "workspace_bytes": ws_bytes, "wall_s": wall, "kernels": kernels,
+        "per_call": dist,
     }
 
 
@@ -254,10 +328,12 @@ def run_decode(torch, R, steps_per_call=1024, warm_calls=1, seed=4, gated=False)
     t, _ = time_steps(step, steps_per_call, warm_calls * 16, torch)
     per = t / steps_per_call
     nb = B * H * (2 * d * d * 4 + 4 * d * 2 + (4 if gated else 0))
+    # the same 1024 steps again, each bracketed by its own events
+    dist = stats(per_call_times(step, steps_per_call, torch))
     return {"workload": "gated_decode_bf16" if gated else "decode_bf16", "batch": B, "H": H, "dk": d, "dv": d,
             "steps": steps_per_call,
             "us_per_step": per * 1e6, "tokens_per_s": B / per,
-            "hbm_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS}
+            "hbm_GBps": nb / per / 1e9, "hbm_frac": nb / per / 1e9 / HBM_PEAK_GBS, "per_step": dist}
 
 
 def cpu_baseline(max_seconds=15.0):
@@ -298,16 +374,21 @@ def cpu_baseline(max_seconds=15.0):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
-def traffic_per_launch():
-    """HBM bytes per launch from the committed counter summary, or None if stale."""
+def counter_summary():
+    """The committed rocprofv3 counter summary of the headline kernel, or None if it was
+    taken on another version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("kernel_sha256_16") == kernel_hash() else None
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed counter summary, or None if stale."""
+    t = counter_summary()
+    return None if t is None else t.get("hbm_bytes_per_launch")
 
 
 SECONDARY_NAMES = ("decode_bf16", "gated_decode_bf16", "long_bf16_C512", "long_bf16_C256", "long_bf16_C128", "gated_bf16",
@@ -324,9 +405,10 @@ def secondary_line(torch, R, name):
         return run_decode(torch, R, seed=11, gated=True)
     if name.startswith("long_bf16_C"):
         return run_chunk_workload(torch, R, "long_bf16", 1, 16, 16384, 128, 128, int(name[11:]), g3, False, 50, 5,
-                                  seed=3)
+                                  seed=3, kernel_times=True)
     if name == "gated_bf16":
-        return run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None, True, 50, 5, seed=5)
+        return run_chunk_workload(torch, R, "gated_bf16", 2, 16, 8192, 128, 128, 64, None, True, 50, 5, seed=5,
+                                  kernel_times=True)
     if name == "train_bf16_backward":
         return run_bwd_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h, False, 20, 3, seed=6)
     if name == "gated_bf16_backward":
@@ -349,6 +431,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip decode/long/gated lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    ap.add_argument("--calib-mfma", action="store_true",
+                    help="run only the achievable-peak references (matrix-core loop, device copy)")
     ap.add_argument("--only", choices=SECONDARY_NAMES,
                     help="run only this secondary line and print it (for profiling one workload)")
     args = ap.parse_args()
@@ -373,13 +457,17 @@ def main():
         print(json.dumps({"calib_copy_bytes": n * 4}))
         return
 
+    if args.calib_mfma:
+        print(json.dumps({"achievable": achievable(torch, R)}))
+        return
+
     if args.only:
         print(json.dumps({args.only: secondary_line(torch, R, args.only)}))
         return
 
     h = [1.0 - 2.0 ** (-5.0 - i) for i in range(8)]
     head = run_chunk_workload(torch, R, "train_bf16", 4, 8, 2048, 256, 512, 64, h, False,
-                              args.steps, args.warmup, seed=2, kernel_times=True)
+                              args.steps, args.warmup, seed=2, kernel_times=True, dist_calls=max(100, args.steps))
 
     secondary = {}
     if not args.no_secondary:
@@ -390,12 +478,16 @@ def main():
     nb = alg_bytes(4, 8, 2048, 256, 512)
     fl = alg_flops(4, 8, 2048, 256, 512, 64)
     achieved = nb / (main_us * 1e-6) / 1e9
+    cs = counter_summary()
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_per_launch(),
-            "kernel": "chunk_kernel<256,128,8,false,0,true> (matrix-core chunkwise pass)",
+            "kernel": HEADLINE_KERNEL,
             "alg_bytes_per_launch": nb, "avg_launch_us": main_us,
             "mfma_tflops": round(fl / (main_us * 1e-6) / 1e12, 1),
             "mfma_frac": round(fl / (main_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            # matrix-core busy cycles / (GPU busy cycles x SIMDs), from the committed
+            # rocprofv3 counters of this kernel source (null once the kernel changed)
+            "mfma_busy_counter": None if cs is None else cs.get("mfma_busy_frac"),
             "step_kernels": head["kernels"]}
 
     line = {
@@ -415,7 +507,11 @@ def main():
                    "dk": 256, "dv": 512, "chunk": 64, "global_batch": 4, "seq_len": 2048,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "timing": {"protocol": "value and ms_per_step: HIP events around the timed steps back to back; per_call: "
+                               "events around each of the calls, unflushed and with a 1 GiB write before each",
+                   "per_call": head["per_call"]},
     }
+    line["achievable"] = achievable(torch, R)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     if secondary:

@@ -276,6 +276,18 @@ int retention_abi_version(void);
 retn_status retention_profile_enable(int on);
 retn_status retention_profile_read(double* ms, int* count, int nkinds, int* dropped);
 
+/*
+ * Measurement helper, not part of the operator: an achievable-peak reference for the
+ * bf16 matrix cores.  Launches `blocks` workgroups of `waves` waves (1..8) on `stream`;
+ * each wave runs `iters` rounds of 16 independent v_mfma_f32_16x16x32_bf16 products
+ * with no memory traffic and writes one float per wave to out[blocks * waves] (device
+ * memory, caller-owned; the values are of no interest).  The caller times the launch;
+ * retention_calib_mfma_flops returns the flops it performs.
+ * Errors: RETN_ERR_NULL (out), RETN_ERR_SHAPE (sizes out of range), RETN_ERR_HIP.
+ */
+retn_status retention_calib_mfma(float* out, int blocks, int waves, int iters, void* stream);
+double retention_calib_mfma_flops(int blocks, int waves, int iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ package does not load the library; the first call does, and raises if it is miss
 from ._lib import (  # noqa: F401
     RetentionError,
     bwd_workspace_bytes,
+    calib_mfma,
     gated_msr_fwd,
     gated_retention_chunkwise_bwd,
     gated_retention_chunkwise_fwd,
@@ -41,4 +42,5 @@ __all__ = [
     "lib",
     "profile_enable",
     "profile_read",
+    "calib_mfma",
 ]

@@ -39,6 +39,8 @@ EXPORTED = (
     "gated_retention_parallel_fwd",
     "gated_msr_fwd",
     "gated_msr_workspace_bytes",
+    "retention_calib_mfma",
+    "retention_calib_mfma_flops",
 )
 
 # Kernel kinds reported by retention_profile_read.
@@ -99,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.gated_msr_fwd.restype = ctypes.c_int
     L.gated_msr_workspace_bytes.argtypes = [_i] * 7
     L.gated_msr_workspace_bytes.restype = _sz
+    L.retention_calib_mfma.argtypes = [_vp, _i, _i, _i, _vp]
+    L.retention_calib_mfma.restype = ctypes.c_int
+    L.retention_calib_mfma_flops.argtypes = [_i, _i, _i]
+    L.retention_calib_mfma_flops.restype = ctypes.c_double
     _lib = L
     return L
 
@@ -462,3 +468,13 @@ def profile_read() -> dict:
     out = {k: {"ms": ms[i], "launches": cnt[i]} for i, k in enumerate(PROFILE_KINDS)}
     out["dropped"] = dropped.value
     return out
+
+
+def calib_mfma(blocks: int, waves: int, iters: int, out=None, stream=None) -> float:
+    """Launch the matrix-core loop reference (see retention_calib_mfma); returns the flops
+    it performs.  The caller times it."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(blocks * waves, dtype=torch.float32, device="cuda")
+    _check(lib().retention_calib_mfma(_ptr(out), blocks, waves, iters, _stream(stream)), "retention_calib_mfma")
+    return float(lib().retention_calib_mfma_flops(blocks, waves, iters))

@@ -245,3 +245,13 @@ def test_decode_wrapper_rejects_wrong_out_shape(monkeypatch):
             _lib.retention_decode_step(q, q, q, gamma, state, out=out)
         with pytest.raises(ValueError, match="out must be"):
             _lib.gated_retention_decode_step(q, q, q, torch.zeros(B, H), state, out=out)
+
+
+def test_calibration_loop_validation(L):
+    """The matrix-core loop reference validates its arguments before launching."""
+    assert L.retention_calib_mfma(None, 1, 1, 1, None) == ERR_NULL
+    assert L.retention_calib_mfma(FAKE, 0, 1, 1, None) == ERR_SHAPE
+    assert L.retention_calib_mfma(FAKE, 1, 9, 1, None) == ERR_SHAPE
+    assert L.retention_calib_mfma(FAKE, 1, 1, 0, None) == ERR_SHAPE
+    # 256 workgroups x 8 waves x 10 rounds x 16 products of 2*16*16*32 flops
+    assert L.retention_calib_mfma_flops(256, 8, 10) == 256 * 8 * 10 * 16 * 16384

@@ -119,3 +119,13 @@ def test_graph_capture_and_replay():
         # eager work between replays
         R().retention_chunkwise_fwd(x["q"], x["k"], x["v"], gm, 64)
         torch.cuda.synchronize()
+
+
+def test_calibration_loop_runs():
+    """The matrix-core loop reference runs and reports its flop count."""
+    print("\n[case] matrix-core loop reference", flush=True)
+    out = torch.empty(4 * 8, dtype=torch.float32, device="cuda")
+    flops = R().calib_mfma(4, 8, 10, out=out)
+    torch.cuda.synchronize()
+    assert flops == 4 * 8 * 10 * 16 * 16384
+    assert torch.all(torch.isfinite(out))
