@@ -62,14 +62,22 @@ typedef enum {
     RETN_ERR_SHAPE = 2,        /* a size is negative or out of range                */
     RETN_ERR_DTYPE = 3,        /* unknown element type                              */
     RETN_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. dk > 256)         */
-    RETN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
+    RETN_ERR_WORKSPACE = 5,    /* workspace missing, too small or misaligned        */
     RETN_ERR_ALIAS = 6,        /* an output overlaps an input                       */
-    RETN_ERR_HIP = 7           /* the HIP runtime reported an error at launch       */
+    RETN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch       */
+    /* Not statuses: they widen the type's range to every int, so that any int a
+       caller passes (e.g. to retention_status_string) is a valid value of it. */
+    RETN_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    RETN_STATUS_RANGE_MAX_ = 2147483647
 } retn_status;
 
 typedef enum {
     RETN_F32 = 0,
-    RETN_BF16 = 1
+    RETN_BF16 = 1,
+    /* Not element types: every int is a valid value of the type (others are
+       rejected with RETN_ERR_DTYPE). */
+    RETN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    RETN_DTYPE_RANGE_MAX_ = 2147483647
 } retn_dtype;
 
 /*

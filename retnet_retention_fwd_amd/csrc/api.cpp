@@ -329,9 +329,10 @@ const char* retention_status_string(retn_status status) {
         case RETN_ERR_SHAPE: return "a size is negative or out of range";
         case RETN_ERR_DTYPE: return "unknown element type";
         case RETN_ERR_UNSUPPORTED: return "valid arguments, but this shape is not supported";
-        case RETN_ERR_WORKSPACE: return "workspace missing or too small";
+        case RETN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case RETN_ERR_ALIAS: return "an output overlaps an input";
         case RETN_ERR_HIP: return "HIP runtime error at launch";
+        default: break;
     }
     return "unknown status";
 }
