@@ -1217,10 +1217,11 @@ hipError_t launch_chunk64_gated(const ChunkArgs& a, const MfmaPlan& p, hipStream
 // (two per SIMD) hide LDS and matrix-core latency better than 4 wider ones.  With
 // dk = 256 a 128-column tile fills the LDS (P then lives in the K buffer) and needs the
 // registers freed by single-block chunks.
-void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
+void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw, bool c64_fwd = false) {
     if (dk == 256 && !gated && dv % 128 == 0 && chunk <= kBlk) { dvt = 128; nw = 8; return; }
-    // 64-token chunks, gated: the single-block main pass fits 128 columns
-    if (dk == 256 && gated && dv % 128 == 0 && chunk == kBlk) { dvt = 128; nw = 8; return; }
+    // gated 64-token chunks on the single-block forward pass (which the caller
+    // guarantees): it fits 128 columns, the general kernel only 64
+    if (dk == 256 && gated && dv % 128 == 0 && chunk == kBlk && c64_fwd) { dvt = 128; nw = 8; return; }
     if (dk == 256) { dvt = 64; nw = 4; return; }
     if (dv % 128 == 0) { dvt = 128; nw = 8; return; }
     dvt = 64;
@@ -1238,7 +1239,7 @@ bool mfma_chunk_supported(int dk, int dv, int chunk, bool bf16) {
 
 MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool c64_fwd) {
     MfmaPlan p{};
-    pick_tile(dk, dv, chunk, gated, p.dvt, p.nw);
+    pick_tile(dk, dv, chunk, gated, p.dvt, p.nw, c64_fwd);
     const long bh = static_cast<long>(B) * H;
     const long base = bh * (dv / p.dvt);
     const int nchunks = (N + chunk - 1) / chunk;
