@@ -285,6 +285,29 @@ retn_status retention_profile_enable(int on);
 retn_status retention_profile_read(double* ms, int* count, int nkinds, int* dropped);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc): retention_chunkwise_fwd without the
+ * workspace arguments.  The segment-state scratch that retention_chunkwise_fwd takes
+ * from the caller's workspace comes instead from a device array of the library, of
+ * RETN_NOALLOC_SCRATCH_BYTES per device, which each device the library runs on holds
+ * until the process ends (its address is looked up once per device; nothing is
+ * allocated or freed).  Every call on a device shares that device's array and it keeps
+ * the last call's contents (no call needs it zeroed: each writes what it reads):
+ * calls that overlap on one device -- on different streams or threads, or inside one
+ * graph without a dependency between them -- race and give wrong results.
+ *   Arguments, layout, results and errors: as retention_chunkwise_fwd, plus
+ *   RETN_ERR_WORKSPACE when the call would need more scratch than
+ *   RETN_NOALLOC_SCRATCH_BYTES (retention_workspace_bytes(..., gated = 0) tells), and
+ *   RETN_ERR_HIP when the stream's device cannot be determined.
+ */
+#define RETN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+retn_status retention_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v,
+                                            const float* gamma, void* o,
+                                            const float* state_in, float* state_out,
+                                            int B, int H, int N, int dk, int dv, int chunk,
+                                            retn_dtype dtype, void* stream);
+
+/*
  * Measurement helper, not part of the operator: an achievable-peak reference for the
  * bf16 matrix cores.  Launches `blocks` workgroups of `waves` waves (1..8) on `stream`;
  * each wave runs `iters` rounds of 16 independent v_mfma_f32_16x16x32_bf16 products

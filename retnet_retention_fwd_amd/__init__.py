@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     profile_read,
     retention_chunkwise_bwd,
     retention_chunkwise_fwd,
+    retention_chunkwise_fwd_noalloc,
     retention_decode_step,
     retention_parallel_fwd,
     workspace_bytes,
@@ -43,4 +44,5 @@ __all__ = [
     "profile_enable",
     "profile_read",
     "calib_mfma",
+    "retention_chunkwise_fwd_noalloc",
 ]

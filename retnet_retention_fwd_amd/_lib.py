@@ -41,6 +41,7 @@ EXPORTED = (
     "gated_msr_workspace_bytes",
     "retention_calib_mfma",
     "retention_calib_mfma_flops",
+    "retention_chunkwise_fwd_noalloc",
 )
 
 # Kernel kinds reported by retention_profile_read.
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.retention_calib_mfma.restype = ctypes.c_int
     L.retention_calib_mfma_flops.argtypes = [_i, _i, _i]
     L.retention_calib_mfma_flops.restype = ctypes.c_double
+    L.retention_chunkwise_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+    L.retention_chunkwise_fwd_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -230,6 +233,53 @@ def retention_chunkwise_fwd(q, k, v, gamma, chunk, state_in=None, return_state=F
     """
     return _chunk_call("retention_chunkwise_fwd", q, k, v, gamma, chunk, state_in, return_state, out,
                        state_out, stream, workspace, False)
+
+
+def retention_chunkwise_fwd_noalloc(q, k, v, gamma, chunk, state_in=None, return_state=False, out=None,
+                                    state_out=None, stream=None):
+    """retention_chunkwise_fwd whose scratch comes from the library's own fixed device array
+    (for callers that cannot allocate; pass out and state_out to allocate nothing here
+    either).  Calls that overlap on one device race on that array."""
+    with _on_stream(stream):
+        return _noalloc_impl(q, k, v, gamma, chunk, state_in, return_state, out, state_out, stream)
+
+
+def _noalloc_impl(q, k, v, gamma, chunk, state_in, return_state, out, state_out, stream):
+    torch = _torch()
+    L = lib()
+    _require(q, "q")
+    dev = q.device
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(gamma, "gamma", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError(f"expected q,k [B,H,N,dk] and v [B,H,N,dv]; got {tuple(q.shape)} "
+                         f"{tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(gamma.shape) != (H,):
+        raise ValueError(f"gamma must have shape {(H,)}, got {tuple(gamma.shape)}")
+    if state_in is not None:
+        _require(state_in, "state_in", torch.float32, dev)
+        if tuple(state_in.shape) != (B, H, dk, dv):
+            raise ValueError("state_in must be [B,H,dk,dv]")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", q.dtype, dev)
+        if tuple(out.shape) != (B, H, N, dv):
+            raise ValueError("out must be [B,H,N,dv]")
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _require(state_out, "state_out", torch.float32, dev)
+        if tuple(state_out.shape) != (B, H, dk, dv):
+            raise ValueError("state_out must be [B,H,dk,dv]")
+    st = L.retention_chunkwise_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(out), _ptr(state_in),
+                                           _ptr(state_out), B, H, N, dk, dv, int(chunk), _dtype_code(q),
+                                           _stream(stream))
+    _check(st, "retention_chunkwise_fwd_noalloc")
+    return (out, state_out) if (return_state or state_out is not None) else out
 
 
 def gated_retention_chunkwise_fwd(q, k, v, g, chunk, state_in=None, return_state=False, out=None,

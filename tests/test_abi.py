@@ -255,3 +255,18 @@ def test_calibration_loop_validation(L):
     assert L.retention_calib_mfma(FAKE, 1, 1, 0, None) == ERR_SHAPE
     # 256 workgroups x 8 waves x 10 rounds x 16 products of 2*16*16*32 flops
     assert L.retention_calib_mfma_flops(256, 8, 10) == 256 * 8 * 10 * 16 * 16384
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(L):
+    """The entry point without workspace refuses a call that would need more scratch
+    than its fixed array holds, before anything touches the GPU."""
+    cap = 32 << 20
+    need = L.retention_workspace_bytes(1, 255, 200, 256, 128, 48, 1, 0)
+    assert need > cap
+    f = L.retention_chunkwise_fwd_noalloc
+    st = f(FAKE, FAKE + 64 * MB, FAKE + 128 * MB, FAKE + 192 * MB, FAKE + 256 * MB, None, None,
+           1, 255, 200, 256, 128, 48, 1, None)
+    assert st == ERR_WORKSPACE
+    # invalid arguments are still reported as such (nothing is launched)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 64, 16, 16, 16, 7, None) == ERR_DTYPE
+    assert f(None, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 64, 16, 16, 16, 0, None) == ERR_NULL
