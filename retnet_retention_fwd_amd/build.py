@@ -19,7 +19,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libretention_fwd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "profile.cpp", "backward.cpp", "generic_chunk.hip", "decode.hip", "mfma_chunk.hip", "chunk64.hip", "calib.hip", "noalloc.hip",
+SOURCES = ["api.cpp", "profile.cpp", "backward.cpp", "generic_chunk.hip", "decode.hip", "mfma_chunk.hip", "chunk64.hip", "chunkw.hip", "calib.hip", "noalloc.hip",
            "bwd_kernels.hip", "msr.hip"]
 
 # Packed-fp32 instructions are disabled for all device code (the compiler would

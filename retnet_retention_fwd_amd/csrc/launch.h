@@ -84,6 +84,11 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream
 struct KArgs;
 bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse);
 hipError_t launch_chunk1(const KArgs& ka, bool gated, hipStream_t stream);
+// Main pass for chunks of 256 or 512 tokens (chunkw.hip): forward, per-head decays,
+// bf16 output, contiguous rows, one slice, d_k 128, d_v a multiple of 128.
+bool chunkw_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse,
+                      bool gated);
+hipError_t launch_chunkw(const KArgs& ka, hipStream_t stream);
 // Parallel form on the matrix cores (no state): O = (Q K^T (.) D) V with the query blocks
 // of a (b,h) in parallel workgroups.
 bool mfma_parallel_supported(int dk, int dv, int N, bool gated, bool bf16);

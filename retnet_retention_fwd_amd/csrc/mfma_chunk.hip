@@ -1203,6 +1203,15 @@ hipError_t launch_chunk64(const ChunkArgs& a, const MfmaPlan& p, hipStream_t str
     if (e != hipSuccess) return e;
     return launch_chunk1(ka, false, stream);
 }
+// Chunks of 256 or 512 tokens (d_k = 128, per-head decays) take the query-row parallel
+// main pass (chunkw.hip).
+template <bool REV>
+hipError_t launch_chunk_rows(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    KArgs ka;
+    const hipError_t e = launch_prep<false, REV>(a, p, p.dvt, stream, ka);
+    if (e != hipSuccess) return e;
+    return launch_chunkw(ka, stream);
+}
 template <bool REV>
 hipError_t launch_chunk64_gated(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     KArgs ka;
@@ -1298,6 +1307,10 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
                          a.out_f32, a.reverse))
         return a.gated ? launch_chunk64_gated<REV>(a, p, stream) : launch_chunk64<REV>(a, p, stream);
     if (p.prefix_tokens > 0) return hipErrorInvalidValue;   // only the single-block pass walks prefixes
+    if (p.dvt == 128 && p.nw == 8 &&
+        chunkw_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
+                         a.out_f32, a.reverse, a.gated))
+        return launch_chunk_rows<REV>(a, p, stream);
 #define RETN_SHAPE(DK, DVT, NW) \
     if (a.dk == DK && p.dvt == DVT && p.nw == NW) return launch_variant<DK, DVT, NW, REV>(a, p, one, stream);
     RETN_SHAPE(64, 64, 4)

@@ -107,6 +107,15 @@ SMALL = [
     (1, 16, 600, 128, 1024, 64, "bf16", False, True),
     (2, 8, 450, 128, 1024, 64, "bf16", True, True),
     (1, 32, 300, 256, 512, 64, "bf16", False, True),     # ragged last chunk
+    # chunks of 128/256/512 with d_k = 128 (query-row parallel main pass): two column
+    # tiles, ragged last chunks (one that ends inside the second pass of a 512-token
+    # chunk, one of 8 tokens), several segments, and a chunk of one block
+    (1, 2, 700, 128, 256, 256, "bf16", False, True),
+    (2, 2, 1600, 128, 128, 512, "bf16", False, False),
+    (1, 1, 777, 128, 128, 512, "bf16", False, True),
+    (1, 2, 520, 128, 128, 256, "bf16", False, True),
+    (1, 4, 2700, 128, 128, 128, "bf16", False, True),
+    (1, 2, 5000, 128, 128, 512, "bf16", False, True),
 ]
 
 
@@ -143,6 +152,8 @@ STRONG = [
     (1, 2, 300, 128, 128, 128, True),
     (1, 2, 200, 64, 64, 40, True),
     (1, 2, 260, 128, 64, 64, False),
+    (1, 2, 1300, 128, 128, 512, False),
+    (1, 2, 700, 128, 128, 128, False),
 ]
 
 
@@ -162,7 +173,8 @@ def test_strong_decay(case):
 
 
 @pytest.mark.parametrize("case", [(1, 2, 200, 256, 256, 64), (1, 2, 200, 128, 128, 100), (1, 2, 130, 64, 64, 64),
-                                  (1, 2, 150, 128, 64, 40)], ids=lambda c: "N{}dk{}dv{}C{}".format(*c[2:]))
+                                  (1, 2, 150, 128, 64, 40), (1, 2, 600, 128, 128, 256), (1, 2, 1100, 128, 128, 512)],
+                         ids=lambda c: "N{}dk{}dv{}C{}".format(*c[2:]))
 def test_tiny_gamma(case):
     """Per-head decays far below the usual range: the decay factors the kernels split
     into per-lane and per-tile parts must not overflow."""
