@@ -175,16 +175,20 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
     //   V^T reads of column tile c for P V: (avp0 ^ 32 c) + 32 p*VRB (+16 rows);
     //   V^T reads of this wave's column tile for the state update: avs[pl] + kh*32*VRB;
     //   snapshot reads of column tile c: (ass[pl] ^ 32 c) + 32 ks*VRB.
-    uint32_t ak0, akt0[2], avs[2], avp0, ass[2];
-    // base ^ x formed at its use (the base passes through an empty asm there, so the
-    // compiler does not keep every variant in a register of its own)
+    uint32_t ak0, aq0, akt0[2], avs[2], avp0, ass[2];
+    // base ^ x formed at its use by one v_xor (inside the asm, so the compiler neither
+    // keeps every variant in a register of its own nor copies the base first)
     auto xa = [](uint32_t base, uint32_t x) -> uint32_t {
-        asm volatile("" : "+v"(base));
-        return base ^ x;
+        uint32_t r;
+        asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(x), "v"(base));
+        return r;
     };
     {
         const int s = swz_qk<QRB / 16>(l16);
         ak0 = opaque(lds0 + L_::kK + static_cast<uint32_t>(l16 * QRB + 16 * (4 * (s >> 2) + (g4 ^ (s & 3)))));
+        // Q reads start at this wave's rows of the block (32 (rg & 1) within the 64)
+        aq0 = opaque(lds0 + L_::kQ + static_cast<uint32_t>((32 * (rg & 1) + l16) * QRB +
+                                                            16 * (4 * (s >> 2) + (g4 ^ (s & 3)))));
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
             const int rb = 8 * g4 + trj + 4 * pl;
@@ -331,8 +335,6 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
             if (has_q(p1)) issue_q(p1, st ^ 1);
         }
 
-        const uint32_t sb = static_cast<uint32_t>(st) * L_::kKV;
-        const uint32_t sbq = static_cast<uint32_t>(st) * L_::kQTile;
         const int p = cur.p, kb = cur.kb;
         const int qrow0 = p * PROWS + rg * R;     // this wave's first query row (chunk-local)
         const int qb = qrow0 / kBlk;              // its query block
@@ -345,8 +347,7 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
             for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    qf[qt][ks] = lds16a(xa(ak0, 64u * ks) + (L_::kQ - L_::kK) + sbq +
-                                         static_cast<uint32_t>(((qrow0 % kBlk) + qt * 16) * QRB));
+                    qf[qt][ks] = lds16a(xa(aq0, 64u * ks) + static_cast<uint32_t>(qt * 16 * QRB));
             // snapshot fragments of column tile c (transposed reads, rows 8g + j + 4pl + 32ks)
             auto s_frag = [&](int c, int ks) -> u16x8_t {
                 u16x4_t r[2];
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
                     u16x8_t kf[KS];
                     if (any) {
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) kf[ks] = lds16a(xa(ak0, 64u * ks) + sb + static_cast<uint32_t>(kt * 16 * QRB));
+                        for (int ks = 0; ks < KS; ++ks) kf[ks] = lds16a(xa(ak0, 64u * ks) + static_cast<uint32_t>(kt * 16 * QRB));
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
                 // V^T fragments of the first four column tiles go out before the weights
                 u16x8_t va[4];
                 auto v_frag = [&](int c) -> u16x8_t {
-                    const uint32_t b = xa(avp0, 32u * c) + sb;
+                    const uint32_t b = xa(avp0, 32u * c);
                     return cat(lds_tra(b + static_cast<uint32_t>(pr * 32 * VRB)),
                                lds_tra(b + static_cast<uint32_t>((pr * 32 + 16) * VRB)));
                 };
@@ -459,13 +460,13 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 auto kt_frag = [&](int dt) -> u16x8_t {
-                    const uint32_t off = sb + kh * 32 * QRB;
+                    const uint32_t off = kh * 32 * QRB;
                     const uint32_t x = 64u * (dt >> 1) + 8u * (dt & 1);
                     return cat(lds_tra(xa(akt0[0], x) + off), lds_tra(xa(akt0[1], x) + off));
                 };
                 constexpr int G = 4;
                 u16x8_t kcur[G], knext[G];
-                const u16x8_t raw = cat(lds_tra(avs[0] + sb + kh * 32 * VRB), lds_tra(avs[1] + sb + kh * 32 * VRB));
+                const u16x8_t raw = cat(lds_tra(avs[0] + kh * 32 * VRB), lds_tra(avs[1] + kh * 32 * VRB));
 #pragma unroll
                 for (int j = 0; j < G; ++j) kcur[j] = kt_frag(j);
                 __builtin_amdgcn_sched_barrier(0);
@@ -533,6 +534,18 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
         cur = p1;
         has1 = next_pos(p1);
         st ^= 1;
+        // the read bases move to the stage of the next step
+        {
+            const uint32_t dkv = st != 0 ? static_cast<uint32_t>(L_::kKV) : static_cast<uint32_t>(-L_::kKV);
+            const uint32_t dq = st != 0 ? static_cast<uint32_t>(L_::kQTile) : static_cast<uint32_t>(-L_::kQTile);
+            ak0 += dkv;
+            akt0[0] += dkv;
+            akt0[1] += dkv;
+            avs[0] += dkv;
+            avs[1] += dkv;
+            avp0 += dkv;
+            aq0 += dq;
+        }
     }
 
     // ---- final state (last segment only), through LDS in whole rows of 16-byte stores
