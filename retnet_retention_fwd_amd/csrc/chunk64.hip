@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     const int bh = wid / (ndvt * nseg);
     const int h = bh % H;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int trj = l16 >> 2, trq = l16 & 3;
     const int col0 = dvt * DVT, wcol = wave * 16;
@@ -428,7 +428,8 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         const bool full = L == kBlk;
         const bool has_next = c + 1 < ntot;
         const bool next_q = c + 1 >= npre;      // the next chunk is a full step: copy its Q
-        const uint32_t next_row = static_cast<uint32_t>(chunk_row(c + 1));
+        // uniform; readfirstlane keeps it (and every copy offset made from it) scalar
+        const uint32_t next_row = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(chunk_row(c + 1)));
         constexpr uint32_t qoff = QB * L_::kQTile, koff = ST * L_::kKTile, voff = ST * L_::kVTile;
         const float* const gl = reinterpret_cast<const float*>(smem + L_::kG) + ST * kBlk;
         // copy op i of the next chunk (every index is tested by the callers' unrolled
