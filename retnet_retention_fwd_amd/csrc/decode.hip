@@ -6,8 +6,10 @@
 // The step streams the whole fp32 state once in and once out, so it is bound by HBM
 // bandwidth; the arithmetic is one FMA pair per state element.  One workgroup owns
 // one (b, h) state.  In the vector kernel each thread owns a float4 column group and
-// a strided set of rows, issues all of its state loads before using them, and the
-// partial sums of o over rows are combined through LDS.
+// a strided set of rows (consecutive threads cover whole rows, so every load and store
+// instruction moves whole 512-byte rows), issues all of its state loads before using
+// them, and sums o over its rows.  The row groups that share a column are combined by
+// lane exchanges inside each wave, and the waves' partial sums through LDS.
 
 #include "common.h"
 #include "launch.h"
@@ -27,9 +29,12 @@ __global__ __launch_bounds__(kThreads) void decode_vec_kernel(
     constexpr int RPP = kThreads / TPR;    // rows per pass
     const int dk = DK > 0 ? DK : dk_rt;
 
+    constexpr int RPW = 64 / TPR;          // row groups of one wave
+    constexpr int NWV = kThreads / 64;     // waves
+    static_assert(64 % TPR == 0 && RPP == RPW * NWV, "row groups split over the waves");
     __shared__ float qs[kMaxDk];
     __shared__ float ks[kMaxDk];
-    __shared__ f32v4 red[RPP][TPR];
+    __shared__ f32v4 red[NWV][TPR];
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
@@ -88,15 +93,25 @@ __global__ __launch_bounds__(kThreads) void decode_vec_kernel(
             acc.w = fmaf(qi, x.w, acc.w);
         }
     }
-    red[rg][cg] = acc;
+    // o over rows: first the RPW row groups of this wave (lanes TPR apart) by lane
+    // exchanges, then the waves' partial sums through LDS
+#pragma unroll
+    for (int m = TPR; m < 64; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, 64);
+        acc.y += __shfl_xor(acc.y, m, 64);
+        acc.z += __shfl_xor(acc.z, m, 64);
+        acc.w += __shfl_xor(acc.w, m, 64);
+    }
+    const int wave = tid >> 6;
+    if ((tid & 63) < TPR) red[wave][cg] = acc;
     __syncthreads();
-    // sum the RPP partial rows of o; thread t < DV owns output column t
+    // thread t < DV owns output column t
     if (tid < DV) {
         const int c4 = tid / 4, lane = tid % 4;
         float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) {
-            const f32v4 p = red[r][c4];
+        for (int w = 0; w < NWV; ++w) {
+            const f32v4 p = red[w][c4];
             sum += lane == 0 ? p.x : lane == 1 ? p.y : lane == 2 ? p.z : p.w;
         }
         io<T>::store(o + static_cast<size_t>(bh) * DV + tid, sum);
