@@ -13,13 +13,14 @@
 // chunks) and 128 state columns, and walks the segment's chunks in order, carrying the
 // state in fp32 matrix-core accumulators (each of its eight waves holds the 128 x 16
 // slice of its 16 columns).  Within a chunk the waves own query rows instead: a pass
-// covers 256 query rows, 32 per wave, and a chunk of 512 takes two passes.  A pass streams the 64-token key blocks it needs through LDS
-// from the last one down to block 0, each with the Q block of the same tokens; a wave
-// starts at the block holding its own rows (its diagonal block): it loads its Q
-// fragments from that stage, forms its cross term from a bf16 snapshot of the chunk's
-// entry state kept in LDS, and then, for every block down to 0, forms its scores
-// (K Q^T, decayed) in registers and accumulates P V with P taken straight from the
-// score accumulators.  The chunk's last pass also streams every block through the state
+// covers 256 query rows, 32 per wave, and a chunk of 512 takes two passes.  The Q blocks
+// of a pass sit in LDS from its first step (copied during the previous pass); at that
+// step every wave loads its Q fragments and forms its cross term from a bf16 snapshot
+// of the chunk's entry state kept in LDS.  The pass then streams the 64-token key
+// blocks it needs through LDS from block 0 up; for every block up to the one holding
+// its own rows (its diagonal block, its last), a wave forms its scores (K Q^T,
+// decayed) in registers and accumulates P V with P taken straight from the score
+// accumulators, and after the diagonal block it stores its rows of O.  The chunk's last pass also streams every block through the state
 // update.  So each wave reads every K and V fragment it multiplies once per block, the
 // scores never pass through LDS, and the key blocks of a chunk are read from memory
 // once per pass.
@@ -53,17 +54,16 @@ struct WCfg {
     static_assert(C % PROWS == 0, "passes must tile the chunk");
 };
 
-// LDS: two stages of one 64-token block each of K, V (128 columns) and Q, then the
-// bf16 snapshot of the chunk's entry state [128 rows][128 columns].  A step's tiles are
-// copied one step ahead.  (A third K/V stage, copied two steps ahead, measured no
-// faster: the walk is bound by instruction issue, not by copy latency.)
+// LDS: two stages of one 64-token block each of K and V (128 columns), the Q blocks of
+// one pass (copied a pass ahead), then the bf16 snapshot of the chunk's entry state
+// [128 rows][128 columns]: 160 KB.
 struct WLds {
     static constexpr int QRB = kWDk * 2, VRB = kWCols * 2;   // row bytes
     static constexpr int kKTile = kBlk * QRB, kVTile = kBlk * VRB, kQTile = kBlk * QRB;
     static constexpr int kK = 0, kV = kKTile;                 // within a K/V stage
     static constexpr int kKV = kKTile + kVTile;               // one K/V stage
-    static constexpr int kQ = 2 * kKV;                        // Q stage 0
-    static constexpr int kS = kQ + 2 * kQTile;
+    static constexpr int kQ = 2 * kKV;                        // Q block slots of a pass
+    static constexpr int kS = kQ + (kWWaves * 32 / kBlk) * kQTile;
     static constexpr int kBytes = kS + kWDk * VRB;
     static_assert(kBytes <= kLdsBytes, "LDS layout too large");
     static_assert(kBytes >= kWDk * kWCols * 4, "the final state is staged through LDS");
@@ -186,8 +186,9 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
     {
         const int s = swz_qk<QRB / 16>(l16);
         ak0 = opaque(lds0 + L_::kK + static_cast<uint32_t>(l16 * QRB + 16 * (4 * (s >> 2) + (g4 ^ (s & 3)))));
-        // Q reads start at this wave's rows of the block (32 (rg & 1) within the 64)
-        aq0 = opaque(lds0 + L_::kQ + static_cast<uint32_t>((32 * (rg & 1) + l16) * QRB +
+        // Q reads: this wave's rows sit in slot rg/2 of the pass's Q blocks, 32 (rg & 1)
+        // rows in
+        aq0 = opaque(lds0 + L_::kQ + static_cast<uint32_t>((rg >> 1) * L_::kQTile + (32 * (rg & 1) + l16) * QRB +
                                                             16 * (4 * (s >> 2) + (g4 ^ (s & 3)))));
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
@@ -228,31 +229,32 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
     // The registers hold S / 2^lk2 (a chunk's decay moves lk2, not the accumulators).
     float lk2 = 0.f;
 
-    // ---- the walk: steps (chunk, pass, key block kb from the pass's last block down to 0)
+    // ---- the walk: steps (chunk, pass, key block kb from block 0 up to the pass's last)
     struct Pos {
         int cs;   // chunk start
         int p;    // pass
         int kb;   // key block
     };
     auto chunk_len = [&](int cs) -> int { return min(C, t_end - cs); };
-    auto pass_top = [&](int cs, int p) -> int {   // the pass's first (highest) key block
+    auto pass_top = [&](int cs, int p) -> int {   // the pass's last key block
         const int nb = (chunk_len(cs) + kBlk - 1) / kBlk;
         return min(nb, (p + 1) * PBLK) - 1;
     };
     auto npass = [&](int cs) -> int { return ((chunk_len(cs) + kBlk - 1) / kBlk + PBLK - 1) / PBLK; };
-    auto next_pos = [&](Pos& s) -> bool {
-        if (s.kb > 0) { --s.kb; return true; }
-        if (s.p + 1 < npass(s.cs)) { ++s.p; s.kb = pass_top(s.cs, s.p); return true; }
+    // the first step of the pass after the one at s; false past the segment end
+    auto next_pass = [&](Pos& s) -> bool {
+        s.kb = 0;
+        if (s.p + 1 < npass(s.cs)) { ++s.p; return true; }
         s.cs += C;
-        if (s.cs >= t_end) return false;
         s.p = 0;
-        s.kb = pass_top(s.cs, 0);
-        return true;
+        return s.cs < t_end;
     };
-    // a step carries a Q block when its key block is one of the pass's query blocks
-    auto has_q = [&](const Pos& s) -> bool { return s.kb >= s.p * PBLK; };
+    auto next_pos = [&](Pos& s) -> bool {
+        if (s.kb < pass_top(s.cs, s.p)) { ++s.kb; return true; }
+        return next_pass(s);
+    };
 
-    // copies of the step at s: K and V into K/V stage b, Q into Q stage b
+    // copies of the step at s (K and V into stage b), and of the Q blocks of the pass at s
     auto issue_kv = [&](const Pos& s, int b) {
         const uint32_t row0 = static_cast<uint32_t>(s.cs + s.kb * kBlk);
         const uint32_t st = lds0 + b * L_::kKV + wofs;
@@ -261,11 +263,17 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < kNV; ++i) vcp.issue_one(i, st + L_::kV, v_rs, row0 * dv * 2);
     };
-    auto issue_q = [&](const Pos& s, int b) {
-        const uint32_t row0 = static_cast<uint32_t>(s.cs + s.kb * kBlk);
-        const uint32_t st = lds0 + L_::kQ + b * L_::kQTile + wofs;
+    auto issue_q = [&](const Pos& s) {
+        const int nq = pass_top(s.cs, s.p) - s.p * PBLK + 1;   // query blocks of the pass
 #pragma unroll
-        for (int i = 0; i < kNQ; ++i) kcp.issue_one(i, st, q_rs, row0 * QRB);
+        for (int j = 0; j < PBLK; ++j) {
+            if (j < nq) {
+                const uint32_t row0 = static_cast<uint32_t>(s.cs + (s.p * PBLK + j) * kBlk);
+                const uint32_t st = lds0 + L_::kQ + j * L_::kQTile + wofs;
+#pragma unroll
+                for (int i = 0; i < kNQ; ++i) kcp.issue_one(i, st, q_rs, row0 * QRB);
+            }
+        }
     };
     // the bf16 snapshot of the true state (S * 2^lk2) into LDS, row-major [dk][128]
     // with the V-tile swizzle
@@ -291,11 +299,11 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
 
     // ---- prologue: the first step's copies, the entry state's snapshot (every load
     // drains here)
-    Pos cur{t_begin, 0, pass_top(t_begin, 0)};
+    Pos cur{t_begin, 0, 0};
     Pos p1 = cur;
     bool has1 = next_pos(p1);
     issue_kv(cur, 0);
-    if (has_q(cur)) issue_q(cur, 0);
+    issue_q(cur);
     __builtin_amdgcn_s_waitcnt(0);
     write_snapshot();
 
@@ -305,6 +313,7 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
     // this wave issued all kNStore output stores at the end of the last step (full
     // chunks; a partial chunk's masked stores may be skipped, and it waits for all)
     bool stored = false;
+    bool q_ahead = true;      // the current pass's Q blocks have been copied
     int cs_prev = -1;
 
     while (true) {
@@ -328,20 +337,34 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
                 lk2 = 0.f;
             }
         }
-        // the next step's copies (its buffers were last read by the previous step, which
-        // every wave has finished)
-        if (has1) {
-            issue_kv(p1, st ^ 1);
-            if (has_q(p1)) issue_q(p1, st ^ 1);
+        // a pass of a single step leaves no step for the next pass's Q copies: they go
+        // out here, and every wave waits for them
+        if (cur.kb == 0 && !q_ahead) {
+            issue_q(cur);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        q_ahead = false;
+        // the next step's K and V (their buffers were last read by the previous step,
+        // which every wave has finished); at the pass's second step, once every wave
+        // holds its Q fragments, the next pass's Q blocks
+        if (has1) issue_kv(p1, st ^ 1);
+        if (cur.kb == 1) {
+            Pos np = cur;
+            if (next_pass(np)) {
+                issue_q(np);
+                q_ahead = true;
+            }
         }
 
         const int p = cur.p, kb = cur.kb;
         const int qrow0 = p * PROWS + rg * R;     // this wave's first query row (chunk-local)
         const int qb = qrow0 / kBlk;              // its query block
         const bool active = qrow0 < L && kb <= qb;
+        // (a wave's rows go through every key block from 0 to its diagonal block qb)
         const bool last_pass = p + 1 == npass(cur.cs);
 
-        if (active && kb == qb) {
+        if (qrow0 < L && kb == 0) {
             // this wave's Q fragments, and its cross term O^T = diag(xi) applied to S^T Q^T
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
@@ -506,8 +529,8 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
             }
         }
 
-        // end of this wave's part of the pass: its rows of O (rows past the chunk end skipped)
-        if (kb == 0 && qrow0 < L) {
+        // after its diagonal block, this wave's rows of O (rows past the chunk end skipped)
+        if (kb == qb && qrow0 < L) {
             bf16_t* const base = o + v_bh + static_cast<size_t>(cur.cs + qrow0) * dv + col0;
             // per-lane element offset, made here (not kept across the walk)
             const uint32_t lo = opaque(static_cast<uint32_t>(l16 * dv + 4 * g4));
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
         }
 
         if (!has1) break;
-        if (kb == 0 && last_pass) {
+        if (kb == pass_top(cur.cs, p) && last_pass) {
             // end of the chunk: every wave is past its cross-term reads of the snapshot;
             // the next chunk's snapshot goes in (published by the next step's barrier)
             lds_barrier();
@@ -537,14 +560,12 @@ __global__ __launch_bounds__(kWWaves * 64, 1) __attribute__((amdgpu_waves_per_eu
         // the read bases move to the stage of the next step
         {
             const uint32_t dkv = st != 0 ? static_cast<uint32_t>(L_::kKV) : static_cast<uint32_t>(-L_::kKV);
-            const uint32_t dq = st != 0 ? static_cast<uint32_t>(L_::kQTile) : static_cast<uint32_t>(-L_::kQTile);
             ak0 += dkv;
             akt0[0] += dkv;
             akt0[1] += dkv;
             avs[0] += dkv;
             avs[1] += dkv;
             avp0 += dkv;
-            aq0 += dq;
         }
     }
 
