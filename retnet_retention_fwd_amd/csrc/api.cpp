@@ -83,7 +83,7 @@ bool use_mfma(int N, int dk, int dv, int eff_chunk, retn_dtype dt) {
 size_t workspace_for(int B, int H, int N, int dk, int dv, int chunk, retn_dtype dt, bool gated) {
     const int c = effective_chunk(N, chunk);
     if (B <= 0 || H <= 0 || N <= 0 || !use_mfma(N, dk, dv, c, dt)) return 0;
-    return retn::mfma_chunk_plan(B, H, N, dk, dv, c, gated, true).workspace_bytes;
+    return retn::mfma_chunk_plan(B, H, N, dk, dv, c, gated).workspace_bytes;
 }
 
 retn_status chunk_common(const void* q, const void* k, const void* v, const float* decay, void* o,
@@ -102,7 +102,7 @@ retn_status chunk_common(const void* q, const void* k, const void* v, const floa
     size_t need = 0;
     retn::MfmaPlan plan{};
     if (mfma && B > 0 && H > 0 && N > 0) {
-        plan = retn::mfma_chunk_plan(B, H, N, dk, dv, eff_chunk, gated, true);
+        plan = retn::mfma_chunk_plan(B, H, N, dk, dv, eff_chunk, gated);
         need = plan.workspace_bytes;
     }
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))

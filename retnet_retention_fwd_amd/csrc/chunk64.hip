@@ -15,7 +15,11 @@
 // computed once (a step then needs two exponentials); the gated chunk-local prefix sums
 // are formed one chunk ahead by wave 0, so no step waits on them behind a barrier.
 // Fragment layouts, swizzles and the state-row permutation are those of the general
-// kernel (mfma_chunk.hip).
+// kernel (mfma_chunk.hip), and so are its call forms: rows of q and k (and of v) with a
+// stride, column slices run as extra chains, the time-reversed walk of the backward's
+// adjoint recurrence (REV: walk position m reads and writes token N-1-m and takes the
+// decay of token N-m, none at m = 0; per head, state_in enters divided by gamma; state_out
+// leaves multiplied by the decay of token 0) and, gated, fp32 output (OF32).
 //
 // Work decomposition: a workgroup owns one (b,h), one segment of the sequence and 128
 // state columns; its eight waves own 16 columns each and hold their DK x 16 slice of S
@@ -23,7 +27,8 @@
 //   barrier; cross term X = diag(2^G) Q S_prev (the next chunk's K and V copies go out
 //   between its matrix instructions); this wave's score tiles, decayed, bf16, into LDS;
 //   barrier; (one Q stage: the next chunk's Q copies) state update; X += P V; X staged
-//   in LDS as bf16 and stored in whole rows after the next barrier.
+//   in LDS as bf16 and stored in whole rows after the next barrier (fp32 output: stored
+//   from the accumulators, 16 bytes per lane).
 
 #include "cdna4.h"
 #include "chunk_tiles.h"
@@ -58,7 +63,7 @@ struct C1Lds {
     static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, bool REV, bool OF32>
 __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk1_kernel(
     const KArgs ka) {
     using L_ = C1Lds<DK, GATED>;
@@ -68,15 +73,16 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     constexpr int KS = DK / 32;    // reduction steps over DK
     constexpr int KL = KS < 4 ? KS : 4;
     constexpr int SL = KS < 4 ? KS : 4;
-    using QCopy = TileCopy<QRB, false, NW>;
-    using VCopy = TileCopy<VRB, true, NW>;
+    using QCopy = TileCopy<QRB, false, NW, REV>;
+    using VCopy = TileCopy<VRB, true, NW, REV>;
     constexpr int kNQ = QCopy::kPerWave, kNV = VCopy::kPerWave;
 
     const bf16_t* __restrict__ q = ka.q;
     const bf16_t* __restrict__ k = ka.k;
     const bf16_t* __restrict__ v = ka.v;
     const float* __restrict__ decay = ka.decay;
-    bf16_t* __restrict__ o = static_cast<bf16_t*>(ka.o);
+    typedef std::conditional_t<OF32, float, bf16_t> out_t;
+    out_t* __restrict__ o = static_cast<out_t*>(ka.o);
     const int H = ka.H, N = ka.N, dv = ka.dv;
     const int nseg = ka.nseg, ndvt = ka.ndvt;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -87,7 +93,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     if (ka.total_groups % 8 == 0) wid = (wid & 7) * (ka.total_groups >> 3) + (wid >> 3);
     const int dvt = wid % ndvt;
     const int seg = (wid / ndvt) % nseg;
-    const int bh = wid / (ndvt * nseg);
+    const int ch = wid / (ndvt * nseg);   // chain: (b,h) and column slice
+    const int nsl = ka.nsl > 1 ? ka.nsl : 1;
+    const int slc = ch % nsl;
+    const int bh = ch / nsl;
     const int h = bh % H;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,20 +112,24 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     const int npre = split && seg == 1 ? ka.pre_tokens / kBlk : 0;   // prefix chunks
     const float lg = GATED ? 0.f : log2f(decay[h]);
 
-    const size_t qk_bh = static_cast<size_t>(bh) * N * DK;
-    const size_t v_bh = static_cast<size_t>(bh) * N * dv;
-    const size_t s_bh = static_cast<size_t>(bh) * DK * dv;
+    // rows of q and k are ldqk elements apart, rows of v ldv; o is contiguous
+    const int ldqk = ka.ldqk, ldv = ka.ldv;
+    const uint32_t qk_rb = static_cast<uint32_t>(ldqk) * 2, v_rb = static_cast<uint32_t>(ldv) * 2;
+    const size_t qk_bh = static_cast<size_t>(bh) * N * ldqk + static_cast<size_t>(slc) * ka.sl_qk;
+    const size_t v_bh = static_cast<size_t>(bh) * N * ldv;
+    const size_t o_bh = static_cast<size_t>(bh) * N * dv + slc * ka.sl_o;
+    const size_t s_bh = static_cast<size_t>(bh) * DK * dv + slc * ka.sl_state;
     const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
-    // ranges end with the last row's own columns; rows past N read as zeros
-    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>(N) * DK * 2);
-    const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>(N) * DK * 2);
-    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>((N - 1) * dv + dv - col0) * 2);
+    // ranges end with the last row's own columns; rows past N (REV: before 0) read as zeros
+    const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
+    const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
+    const u32x4_t v_rs = make_rsrc(v + v_bh + col0, static_cast<uint32_t>((N - 1) * ldv + dv - col0) * 2);
     const uint32_t lds0 = lds_addr_of(smem);
     QCopy kcp;   // Q and K tiles (same row length and swizzle)
     VCopy vcp;
-    kcp.init(DK * 2, wave, lane, N);
-    vcp.init(dv * 2, wave, lane, N);
+    kcp.init(ldqk * 2, wave, lane, N);
+    vcp.init(ldv * 2, wave, lane, N);
     const uint32_t wofs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
 
     // State accumulator element (dt, i) of lane (g, l%16) holds state row srow(dt, i) of
@@ -143,15 +156,20 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             int sg0 = 0;
             if (ka.state_in != nullptr) {
                 load(ka.state_in + s_bh, 0.f, false);
+                if constexpr (REV && !GATED) {
+                    const float inv = 1.f / decay[h];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) S[dt] *= inv;
+                }
             } else if (seg > 0 && !split) {
-                load(ka.seg_state + static_cast<size_t>(bh) * nseg * s_stride_seg, 0.f, false);
+                load(ka.seg_state + static_cast<size_t>(ch) * nseg * s_stride_seg, 0.f, false);
                 sg0 = 1;
             }
             for (int sg = sg0; nseg > 1 && !split && sg < seg; ++sg)
-                load(ka.seg_state + (static_cast<size_t>(bh) * nseg + sg) * s_stride_seg,
-                     exp2f(ka.seg_log2[static_cast<size_t>(bh) * nseg + sg]), true);
+                load(ka.seg_state + (static_cast<size_t>(ch) * nseg + sg) * s_stride_seg,
+                     exp2f(ka.seg_log2[static_cast<size_t>(ch) * nseg + sg]), true);
         } else {
-            load(ka.seg_state + (static_cast<size_t>(bh) * nseg + seg) * s_stride_seg, 0.f, false);
+            load(ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg, 0.f, false);
         }
     }
 
@@ -238,12 +256,18 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     f32x4_t X[4];
 
     // ---- gated: wave 0 forms the chunk-local inclusive prefix of g (times log2 e) for
-    // a chunk into gl[stage][0..63] (positions past the chunk end repeat the last sum)
+    // a chunk into gl[stage][0..63] (positions past the chunk end repeat the last sum;
+    // REV: walk position m takes g of token N-m, 0 at m = 0)
     float gnext = 0.f;
     auto g_load = [&](int cs) {
         if (GATED && wave == 0) {
             const int lim = t_end - cs;
-            gnext = lane < lim ? g_bh[cs + lane] : 0.f;
+            if constexpr (REV) {
+                const int m = cs + lane;
+                gnext = lane < lim && m > 0 ? g_bh[N - m] : 0.f;
+            } else {
+                gnext = lane < lim ? g_bh[cs + lane] : 0.f;
+            }
         }
     };
     auto g_scan = [&](int stage) {
@@ -260,13 +284,13 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
     // ---- tile copies of chunk c into stage b (Q stage: b for two stages, 0 for one)
     auto k_copy = [&](int i, int b, uint32_t row0) {
-        kcp.issue_one(i, lds0 + L_::kK + b * L_::kKTile + wofs, k_rs, row0 * QRB);
+        kcp.issue_one(i, lds0 + L_::kK + b * L_::kKTile + wofs, k_rs, row0 * qk_rb);
     };
     auto q_copy = [&](int i, int b, uint32_t row0) {
-        kcp.issue_one(i, lds0 + L_::kQ + (QS == 2 ? b : 0) * L_::kQTile + wofs, q_rs, row0 * QRB);
+        kcp.issue_one(i, lds0 + L_::kQ + (QS == 2 ? b : 0) * L_::kQTile + wofs, q_rs, row0 * qk_rb);
     };
     auto v_copy = [&](int i, int b, uint32_t row0) {
-        vcp.issue_one(i, lds0 + L_::kV + b * L_::kVTile + wofs, v_rs, row0 * dv * 2);
+        vcp.issue_one(i, lds0 + L_::kV + b * L_::kVTile + wofs, v_rs, row0 * v_rb);
     };
 
     // ---- output staging: a finished block goes to LDS as bf16, row-major [64][128] with
@@ -296,12 +320,22 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         }
     };
     auto stage_emit = [&]() {
-        bf16_t* const base = o + v_bh + static_cast<size_t>(xs_row) * dv + col0;
+        if constexpr (REV) {   // walk row r is token N-1-(xs_row+r)
+            bf16_t* const base = reinterpret_cast<bf16_t*>(o) + o_bh + static_cast<size_t>(N - 1 - xs_row) * dv + col0;
 #pragma unroll
-        for (int r = 0; r < kXRounds; ++r) {
-            const int e = r * NW * 64 + tid;
-            const int row = e / kXU, u = e % kXU;
-            *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = xv[r];
+            for (int r = 0; r < kXRounds; ++r) {
+                const int e = r * NW * 64 + tid;
+                const int row = e / kXU, u = e % kXU;
+                *reinterpret_cast<u16x8_t*>(base + (u * 8 - row * dv)) = xv[r];
+            }
+        } else {
+            bf16_t* const base = reinterpret_cast<bf16_t*>(o) + o_bh + static_cast<size_t>(xs_row) * dv + col0;
+#pragma unroll
+            for (int r = 0; r < kXRounds; ++r) {
+                const int e = r * NW * 64 + tid;
+                const int row = e / kXU, u = e % kXU;
+                *reinterpret_cast<u16x8_t*>(base + static_cast<uint32_t>(row * dv + u * 8)) = xv[r];
+            }
         }
         xs_row = -1;
     };
@@ -449,7 +483,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // this chunk's tiles (and prefix sums) have landed and are visible to every wave
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();
-        if (xs_row >= 0) {
+        if (!OF32 && xs_row >= 0) {
             stage_load();
             stage_emit();
         }
@@ -487,6 +521,20 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
                         X[mt] = mfma16(b, qa[mt], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : X[mt]);
+                    if constexpr (OF32) {
+                        // fp32 output: the state operand also as a second bf16 term (its
+                        // rounding residual), so the cross term carries ~16 mantissa bits of S
+                        f32x4_t r0, r1;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            r0[i] = S[2 * ks][i] - bf16_to_f32(a0[i]);
+                            r1[i] = S[2 * ks + 1][i] - bf16_to_f32(a1[i]);
+                        }
+                        const u16x4_t c0 = bf4(r0), c1 = bf4(r1);
+                        const u16x8_t bl = (g4 & 1) ? cat(c1, c0) : cat(c0, c1);
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma16(bl, qa[mt], X[mt]);
+                    }
                     if (has_next) copy_slice(0, kCrossOps, ks, KS);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -575,17 +623,21 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // top of the step; the next barrier publishes them)
         if (has_next) g_scan(1 - ST);
 
-        // the output block: staged when more chunks follow (stored after the next
-        // barrier), else stored from registers (rows past the chunk end skipped)
-        if (full && has_next) {
+        // the output block: bf16, staged when more chunks follow (stored after the next
+        // barrier); else (and fp32) stored from the accumulators, rows past the chunk end
+        // skipped (REV: walk row r of the chunk is token N-1-(cs+r))
+        if (!OF32 && full && has_next) {
             stage_write();
             xs_row = cs;
         } else {
-            bf16_t* const base = o + v_bh + static_cast<size_t>(cs) * dv + col0 + wcol + 4 * g4;
+            out_t* const base = o + o_bh + static_cast<size_t>(REV ? N - 1 - cs : cs) * dv + col0 + wcol + 4 * g4;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int row = mt * 16 + l16;
-                if (row < L) *reinterpret_cast<u16x4_t*>(base + static_cast<uint32_t>(row * dv)) = bf4(X[mt]);
+                if (row >= L) continue;
+                out_t* const dst = REV ? base - static_cast<ptrdiff_t>(row) * dv : base + static_cast<uint32_t>(row * dv);
+                if constexpr (OF32) *reinterpret_cast<f32x4_t*>(dst) = X[mt];
+                else *reinterpret_cast<u16x4_t*>(dst) = bf4(X[mt]);
             }
         }
         return has_next;
@@ -599,7 +651,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     // ---- final state (last segment only), through LDS in whole rows of 16-byte stores
     if (seg == nseg - 1 && ka.state_out != nullptr) {
         float* const st = reinterpret_cast<float*>(smem);
-        const float r = exp2_fast(lk2);
+        // REV: the final state leaves multiplied by the decay of token 0
+        float lout = lk2;
+        if constexpr (REV) lout += GATED ? g_bh[0] * kLog2e : lg;
+        const float r = exp2_fast(lout);
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();   // every wave is done with the tile buffers
 #pragma unroll
@@ -621,29 +676,42 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     }
 }
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, bool REV, bool OF32>
 hipError_t launch_c1(const KArgs& ka, hipStream_t stream) {
     constexpr size_t lds = C1Lds<DK, GATED>::kBytes;
     static std::once_flag attr_once;   // thread-safe one-time init of the LDS limit
     std::call_once(attr_once, [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED, REV, OF32>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     });
     ProfScope prof(kProfMain, stream);
-    hipLaunchKernelGGL((chunk1_kernel<DK, GATED>), dim3(ka.total_groups), dim3(kC1Waves * 64), lds, stream, ka);
+    hipLaunchKernelGGL((chunk1_kernel<DK, GATED, REV, OF32>), dim3(ka.total_groups), dim3(kC1Waves * 64), lds,
+                       stream, ka);
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_c1_dk(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream) {
+    if (gated) {
+        if (out_f32)
+            return reverse ? launch_c1<DK, true, true, true>(ka, stream) : launch_c1<DK, true, false, true>(ka, stream);
+        return reverse ? launch_c1<DK, true, true, false>(ka, stream) : launch_c1<DK, true, false, false>(ka, stream);
+    }
+    if (out_f32) return hipErrorInvalidValue;
+    return reverse ? launch_c1<DK, false, true, false>(ka, stream) : launch_c1<DK, false, false, false>(ka, stream);
 }
 
 }  // namespace
 
-bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse) {
-    return chunk == kBlk && (dk == 128 || dk == 256) && dv % kC1Cols == 0 && ldqk == dk && ldv == dv &&
-           slices <= 1 && !out_f32 && !reverse;
+bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool gated) {
+    // copies move 16-byte units, so row strides are multiples of 8 elements
+    return chunk == kBlk && (dk == 128 || dk == 256) && dv % kC1Cols == 0 && ldqk >= dk && ldv >= dv &&
+           ldqk % 8 == 0 && ldv % 8 == 0 && slices >= 1 && (!out_f32 || gated);
 }
 
-hipError_t launch_chunk1(const KArgs& ka, bool gated, hipStream_t stream) {
-    if (ka.dk == 256) return gated ? launch_c1<256, true>(ka, stream) : launch_c1<256, false>(ka, stream);
-    if (ka.dk == 128) return gated ? launch_c1<128, true>(ka, stream) : launch_c1<128, false>(ka, stream);
+hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream) {
+    if (ka.dk == 256) return launch_c1_dk<256>(ka, gated, reverse, out_f32, stream);
+    if (ka.dk == 128) return launch_c1_dk<128>(ka, gated, reverse, out_f32, stream);
     return hipErrorInvalidValue;
 }
 

@@ -75,15 +75,16 @@ struct MfmaPlan {
     int prefix_tokens;
     size_t workspace_bytes;
 };
-// c64_fwd: the caller runs the forward with 64-token chunks on the single-block main
-// pass (contiguous rows, bf16 output, one slice), which can take a prefix split.
-MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool c64_fwd = false);
+// A call with 64-token chunks runs on the single-block main pass (below) whenever that
+// supports it, and can then take a prefix split instead of a pre-pass.
+MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated);
 hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream_t stream);
-// Main pass for chunks of exactly 64 tokens (chunk64.hip): forward, bf16 output,
-// contiguous rows, one slice, d_k 128 or 256, d_v a multiple of 128.
+// Main pass for chunks of exactly 64 tokens (chunk64.hip): d_k 128 or 256, d_v a
+// multiple of 128, row strides multiples of 8 elements, any slices, either walk
+// direction, fp32 output when gated.
 struct KArgs;
-bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse);
-hipError_t launch_chunk1(const KArgs& ka, bool gated, hipStream_t stream);
+bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool gated);
+hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream);
 // Main pass for chunks of 256 or 512 tokens (chunkw.hip): forward, per-head decays,
 // bf16 output, contiguous rows, one slice, d_k 128, d_v a multiple of 128.
 bool chunkw_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse,

@@ -1196,12 +1196,12 @@ hipError_t launch_shape(const ChunkArgs& a, const MfmaPlan& p, hipStream_t strea
 }
 
 // Chunks of exactly 64 tokens take the leaner single-block main pass (chunk64.hip).
-template <bool REV>
+template <bool GATED, bool REV>
 hipError_t launch_chunk64(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
     KArgs ka;
-    const hipError_t e = launch_prep<false, REV>(a, p, p.dvt, stream, ka);
+    const hipError_t e = launch_prep<GATED, REV>(a, p, p.dvt, stream, ka);
     if (e != hipSuccess) return e;
-    return launch_chunk1(ka, false, stream);
+    return launch_chunk1(ka, GATED, REV, a.out_f32, stream);
 }
 // Chunks of 256 or 512 tokens (d_k = 128, per-head decays) take the query-row parallel
 // main pass (chunkw.hip).
@@ -1212,13 +1212,6 @@ hipError_t launch_chunk_rows(const ChunkArgs& a, const MfmaPlan& p, hipStream_t 
     if (e != hipSuccess) return e;
     return launch_chunkw(ka, stream);
 }
-template <bool REV>
-hipError_t launch_chunk64_gated(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream) {
-    KArgs ka;
-    const hipError_t e = launch_prep<true, REV>(a, p, p.dvt, stream, ka);
-    if (e != hipSuccess) return e;
-    return launch_chunk1(ka, true, stream);
-}
 
 // State columns per workgroup and waves per workgroup for a head shape.
 // State columns per workgroup and waves per workgroup for a head shape.  Wider column
@@ -1226,11 +1219,11 @@ hipError_t launch_chunk64_gated(const ChunkArgs& a, const MfmaPlan& p, hipStream
 // (two per SIMD) hide LDS and matrix-core latency better than 4 wider ones.  With
 // dk = 256 a 128-column tile fills the LDS (P then lives in the K buffer) and needs the
 // registers freed by single-block chunks.
-void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw, bool c64_fwd = false) {
+void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
     if (dk == 256 && !gated && dv % 128 == 0 && chunk <= kBlk) { dvt = 128; nw = 8; return; }
-    // gated 64-token chunks on the single-block forward pass (which the caller
-    // guarantees): it fits 128 columns, the general kernel only 64
-    if (dk == 256 && gated && dv % 128 == 0 && chunk == kBlk && c64_fwd) { dvt = 128; nw = 8; return; }
+    // gated 64-token chunks run on the single-block pass, which fits 128 columns (the
+    // general kernel only 64)
+    if (dk == 256 && gated && dv % 128 == 0 && chunk == kBlk) { dvt = 128; nw = 8; return; }
     if (dk == 256) { dvt = 64; nw = 4; return; }
     if (dv % 128 == 0) { dvt = 128; nw = 8; return; }
     dvt = 64;
@@ -1246,9 +1239,9 @@ bool mfma_chunk_supported(int dk, int dv, int chunk, bool bf16) {
     return chunk >= 1 && chunk <= kMaxChunk;
 }
 
-MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool c64_fwd) {
+MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool gated) {
     MfmaPlan p{};
-    pick_tile(dk, dv, chunk, gated, p.dvt, p.nw, c64_fwd);
+    pick_tile(dk, dv, chunk, gated, p.dvt, p.nw);
     const long bh = static_cast<long>(B) * H;
     const long base = bh * (dv / p.dvt);
     const int nchunks = (N + chunk - 1) / chunk;
@@ -1260,8 +1253,8 @@ MfmaPlan mfma_chunk_plan(int B, int H, int N, int dk, int dv, int chunk, bool ga
     p.pre_dvt = dv % 128 == 0 ? 128 : 64;
     p.fuse_scan = p.nseg <= kFuseScanMax ? 1 : 0;
     p.prefix_tokens = 0;
-    if (c64_fwd && p.nseg == 2 && chunk == kBlk && p.dvt == 128 && nchunks >= 4 &&
-        chunk1_supported(dk, dv, chunk, dk, dv, 1, false, false)) {
+    if (p.nseg == 2 && chunk == kBlk && p.dvt == 128 && nchunks >= 4 &&
+        chunk1_supported(dk, dv, chunk, dk, dv, 1, false, gated)) {
         // Two segments: the second segment's workgroups compute their entry state by
         // walking the first segment state-only, which costs about kPrefixCost of a full
         // step per chunk; the first segment is made longer so both finish together.
@@ -1304,8 +1297,8 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
     const bool one = a.chunk <= kBlk;
     if (p.dvt == 128 && p.nw == 8 &&
         chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
-                         a.out_f32, a.reverse))
-        return a.gated ? launch_chunk64_gated<REV>(a, p, stream) : launch_chunk64<REV>(a, p, stream);
+                         a.out_f32, a.gated))
+        return a.gated ? launch_chunk64<true, REV>(a, p, stream) : launch_chunk64<false, REV>(a, p, stream);
     if (p.prefix_tokens > 0) return hipErrorInvalidValue;   // only the single-block pass walks prefixes
     if (p.dvt == 128 && p.nw == 8 &&
         chunkw_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,

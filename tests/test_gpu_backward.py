@@ -89,6 +89,11 @@ CASES = [
     (1, 1, 1000, 256, 512, 64, "bf16", False, True, True),
     (1, 1, 90, 128, 1024, 64, "bf16", False, True, True),     # the widest d_v: four slices
     (1, 1, 90, 128, 1024, 64, "bf16", True, True, True),
+    # 128 chains x column tiles: two segments, so the reversed d_v pass walks the first
+    # segment state-only in its second segment's workgroups (prefix split)
+    (2, 32, 300, 128, 256, 64, "bf16", False, True, True),
+    (2, 32, 300, 128, 256, 64, "bf16", True, True, True),
+    (1, 2, 150, 256, 256, 64, "bf16", True, True, True),      # gated d_k = 256, fp32 dq and dk
 ]
 
 
