@@ -122,6 +122,10 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
                convert_dot_supported(s.dk, nullptr, nullptr, nullptr, nullptr);
     if (p.f32acc && ptrs != nullptr)
         p.f32acc = al16(ptrs->q) && al16(ptrs->k) && al16(ptrs->dq) && al16(ptrs->dk);
+    // unsplit 128 x 128 heads in 64-token chunks: the single-block pass forms the dots
+    // itself from its fp32 accumulators and writes dq and dk as bf16 directly
+    p.rowdot = p.f32acc && p.parts == 1 && chunk1_dot_supported(p.w, s.dk, s.chunk);
+    if (p.rowdot) p.f32acc = false;
     // the slices of a dq or dk pass (one slice of fp32 when unsplit for the gate gradient)
     p.off_sl = take(p.parts > 1 || p.f32acc ? p.parts * tokens * s.dk * (p.f32acc ? sizeof(float) : es) : 0);
     p.total = off;
@@ -132,13 +136,28 @@ BwdPlan bwd_plan(const BwdShape& s, const BwdPtrs* ptrs) {
 namespace {
 
 // One forward pass on the kernel the plan chose.
+// Row dots of a pass's output (gated, see ChunkArgs::xdot).
+struct RowDot {
+    const void* x;
+    float* dG;
+    float sign;
+    bool accumulate;
+};
+
 hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
                         const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
-                        void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32) {
+                        void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32,
+                        const RowDot* rd = nullptr) {
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
                 ws_bytes};
     a.out_f32 = out_f32;
     a.reverse = rev;
+    if (rd != nullptr) {
+        a.xdot = rd->x;
+        a.dG = rd->dG;
+        a.dsign = rd->sign;
+        a.dacc = rd->accumulate;
+    }
     if (kind == kMfma) return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H, s.N, dkp, dvp, s.chunk, s.gated), st);
     return launch_generic_chunk(a, st);
 }
@@ -147,10 +166,11 @@ hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* 
 // chains of one matrix-core launch; slice p's output goes to o + p * tokens * dk.
 hipError_t sliced_pass(const BwdShape& s, const BwdPlan& p, int kind, const void* q, const void* k, const void* v,
                        const float* decay, void* o, const float* state_in, float* state_out, void* ws, hipStream_t st,
-                       bool rev, bool out_f32) {
+                       bool rev, bool out_f32, const RowDot* rd = nullptr) {
     if (p.parts == 1)
         return forward_pass(s, kind, q, k, v, decay, o, state_in, state_out, p.w, s.dk, ws, p.fwd_bytes, st, rev,
-                            out_f32);
+                            out_f32, rd);
+    if (rd != nullptr) return hipErrorInvalidValue;   // row dots need whole rows
     const size_t tokens = static_cast<size_t>(s.B) * s.H * s.N;
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, p.w, s.dk, s.chunk, s.bf16, s.gated, ws,
                 p.fwd_bytes};
@@ -219,9 +239,11 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     RETN_TRY(launch_state_transpose(has_s0 ? x.state_in : nullptr, s0t, has_ds ? x.dstate_out : nullptr, dst, bh, s.dk,
                                     s.dv, P, st));
 
-    // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS)
+    // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS);
+    // row dots: dG = q . dq
+    const RowDot rdq{x.q, dG, 1.f, false}, rdk{x.k, dG, -1.f, true};
     RETN_TRY(sliced_pass(s, p, p.kind_q, x.dout, x.v, x.k, x.decay, direct ? x.dq : sl, has_s0 ? s0t : nullptr,
-                         s.gated && has_ds ? sfin : nullptr, fws, st, false, f32));
+                         s.gated && has_ds ? sfin : nullptr, fws, st, false, f32, p.rowdot ? &rdq : nullptr));
     RETN_TRY(finish(x.dq, x.q, 1.f, false));
 
     // ---- dv = forward(k, q, dO) walking backwards from dS; it ends with dS0 = lam_0 U_0
@@ -230,12 +252,12 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
 
     // ---- dk = forward(v, dO, q) walking backwards from dS^T
     RETN_TRY(sliced_pass(s, p, p.kind_k, x.v, x.dout, x.q, x.decay, direct ? x.dk : sl, has_ds ? dst : nullptr,
-                         nullptr, fws, st, true, f32));
+                         nullptr, fws, st, true, f32, p.rowdot ? &rdk : nullptr));
     RETN_TRY(finish(x.dk, x.k, -1.f, true));
 
     // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>
     if (s.gated) {
-        if (!f32) RETN_TRY(launch_gate_rows(x.q, x.dq, x.k, x.dk, dG, bh, s.N, s.dk, s.bf16, st));
+        if (!f32 && !p.rowdot) RETN_TRY(launch_gate_rows(x.q, x.dq, x.k, x.dk, dG, bh, s.N, s.dk, s.bf16, st));
         RETN_TRY(launch_gate_scan(dG, has_ds ? dst : nullptr, sfin, s.dk, s.dv, P, x.dg, bh, s.N, st));
     }
 #undef RETN_TRY

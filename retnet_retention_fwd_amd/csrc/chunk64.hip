@@ -19,7 +19,10 @@
 // stride, column slices run as extra chains, the time-reversed walk of the backward's
 // adjoint recurrence (REV: walk position m reads and writes token N-1-m and takes the
 // decay of token N-m, none at m = 0; per head, state_in enters divided by gamma; state_out
-// leaves multiplied by the decay of token 0) and, gated, fp32 output (OF32).
+// leaves multiplied by the decay of token 0) and, gated, fp32 output.  For the gated
+// backward's dq and dk passes (one 128-column tile per row) the output can also leave
+// as bf16 together with each row's dot product against a second tensor taken from the
+// fp32 accumulators (OUT = kOutDot), which the gate gradient sums.
 //
 // Work decomposition: a workgroup owns one (b,h), one segment of the sequence and 128
 // state columns; its eight waves own 16 columns each and hold their DK x 16 slice of S
@@ -45,10 +48,14 @@ namespace {
 constexpr int kC1Cols = 128;   // state columns per workgroup
 constexpr int kC1Waves = 8;    // 16 columns per wave
 
+// Output forms: bf16; fp32; bf16 plus the row dots of the fp32 rows with a second tensor.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutDot = 2;
+
 // LDS layout: Q (one stage for d_k = 256, two otherwise), two stages of K and V, the P
-// fragments of the current chunk, the staging area of one output block, and (gated)
-// two stages of the chunk-local log2 prefix sums.
-template <int DK, bool GATED>
+// fragments of the current chunk, the staging area of one output block, (gated) two
+// stages of the chunk-local log2 prefix sums and (row dots) two stages of the waves'
+// partial dots [64 rows][8 waves].
+template <int DK, bool GATED, bool DOT = false>
 struct C1Lds {
     static constexpr int QRB = DK * 2, VRB = kC1Cols * 2;       // row bytes
     static constexpr int QS = DK == 256 ? 1 : 2;                // Q stages
@@ -59,14 +66,22 @@ struct C1Lds {
     static constexpr int kP = kV + 2 * kVTile;
     static constexpr int kX = kP + kPBytes;
     static constexpr int kG = kX + kBlk * kC1Cols * 2;
-    static constexpr int kBytes = kG + (GATED ? 2 * kBlk * 4 : 0);
+    static constexpr int kD = kG + (GATED ? 2 * kBlk * 4 : 0);
+    static constexpr int kDStage = kBlk * kC1Waves * 4;
+    static constexpr int kBytes = kD + (DOT ? 2 * kDStage : 0);
     static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
 
-template <int DK, bool GATED, bool REV, bool OF32>
+template <int DK, bool GATED, bool REV, int OUT>
 __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk1_kernel(
     const KArgs ka) {
-    using L_ = C1Lds<DK, GATED>;
+    constexpr bool OF32 = OUT == kOutF32;   // fp32 output
+    constexpr bool DOT = OUT == kOutDot;    // bf16 output and row dots
+    // fp32 results (the output, or the row dots) take the state operand of the cross term
+    // as two bf16 terms
+    constexpr bool HILO = OUT != kOutBf16;
+    static_assert(!DOT || (GATED && DK == 128), "row dots: gated, 128-wide scores");
+    using L_ = C1Lds<DK, GATED, DOT>;
     constexpr int NW = kC1Waves, DVT = kC1Cols;
     constexpr int QRB = L_::QRB, VRB = L_::VRB, QS = L_::QS;
     constexpr int DT = DK / 16;    // 16-row tiles of the state
@@ -121,6 +136,9 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     const size_t s_bh = static_cast<size_t>(bh) * DK * dv + slc * ka.sl_state;
     const size_t s_stride_seg = static_cast<size_t>(DK) * dv;
     const float* g_bh = GATED ? decay + static_cast<size_t>(bh) * N : nullptr;
+    // row dots: rows of the second tensor (dv elements, token order) and the dots' output
+    const bf16_t* const xd_bh = DOT ? ka.xdot + static_cast<size_t>(bh) * N * dv : nullptr;
+    float* const dG_bh = DOT ? ka.dG + static_cast<size_t>(bh) * N : nullptr;
     // ranges end with the last row's own columns; rows past N (REV: before 0) read as zeros
     const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
     const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
@@ -450,6 +468,49 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     // state update (state-only steps).
     const int ntot = npre + nck;
     auto chunk_row = [&](int c) -> int { return c < npre ? c * kBlk : t_begin + (c - npre) * kBlk; };
+
+    // ---- row dots: at a chunk's end each wave's partial dots over its 16 columns go to
+    // LDS; after the next barrier wave 7 sums each row's eight partials into dG (the last
+    // chunk's after the walk).  The second tensor's elements of a lane are loaded at the
+    // top of the chunk.
+    u16x4_t xdl[DOT ? 4 : 1];
+    int dot_row = -1, dot_len = 0, dot_st = 0;   // the chunk whose partials wait in LDS
+    auto dot_load = [&](int cs, int L) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = mt * 16 + l16;
+            const int tok = REV ? N - 1 - (cs + row) : cs + row;
+            xdl[mt] = row < L ? *reinterpret_cast<const u16x4_t*>(xd_bh + static_cast<size_t>(tok) * dv + col0 + wcol +
+                                                                    4 * g4)
+                              : u16x4_t{0, 0, 0, 0};
+        }
+    };
+    auto dot_part = [&](int st) {
+        float part[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            part[mt] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[mt] += X[mt][i] * bf16_to_f32(xdl[mt][i]);
+            part[mt] += __shfl_xor(part[mt], 16, 64);
+            part[mt] += __shfl_xor(part[mt], 32, 64);
+        }
+        if (g4 == 0) {
+            float* const dp = reinterpret_cast<float*>(smem + L_::kD + st * L_::kDStage);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) dp[(mt * 16 + l16) * NW + wave] = part[mt];
+        }
+    };
+    auto dot_flush = [&]() {
+        if (wave == NW - 1 && dot_row >= 0 && lane < dot_len) {
+            const float* const dp = reinterpret_cast<const float*>(smem + L_::kD + dot_st * L_::kDStage) + lane * NW;
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dp), b = *reinterpret_cast<const f32x4_t*>(dp + 4);
+            const float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+            float* const dst = dG_bh + (REV ? N - 1 - (dot_row + lane) : dot_row + lane);
+            *dst = (ka.dacc ? *dst : 0.f) + ka.dsign * sum;
+        }
+        dot_row = -1;
+    };
     constexpr int kOps = 2 * kNQ + kNV;                        // K, V, then Q copies
     constexpr int kCrossOps = QS == 2 ? kOps : kNQ + kNV;      // those issued in the cross term
     // Returns false past the last chunk.
@@ -487,6 +548,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             stage_load();
             stage_emit();
         }
+        if constexpr (DOT) {
+            dot_flush();
+            if (!sonly) dot_load(cs, L);
+        }
         if (has_next) g_load(static_cast<int>(next_row));
 
         // decays of this chunk
@@ -521,8 +586,8 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
                         X[mt] = mfma16(b, qa[mt], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : X[mt]);
-                    if constexpr (OF32) {
-                        // fp32 output: the state operand also as a second bf16 term (its
+                    if constexpr (HILO) {
+                        // fp32 results: the state operand also as a second bf16 term (its
                         // rounding residual), so the cross term carries ~16 mantissa bits of S
                         f32x4_t r0, r1;
 #pragma unroll
@@ -623,6 +688,13 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // top of the step; the next barrier publishes them)
         if (has_next) g_scan(1 - ST);
 
+        if constexpr (DOT) {
+            dot_part(ST);
+            dot_row = cs;
+            dot_len = L;
+            dot_st = ST;
+        }
+
         // the output block: bf16, staged when more chunks follow (stored after the next
         // barrier); else (and fp32) stored from the accumulators, rows past the chunk end
         // skipped (REV: walk row r of the chunk is token N-1-(cs+r))
@@ -646,6 +718,12 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     for (int c = 0;; c += 2) {
         if (!step(std::integral_constant<int, 0>{}, c)) break;
         if (!step(std::integral_constant<int, 1>{}, c + 1)) break;
+    }
+    if constexpr (DOT) {
+        if (dot_row >= 0) {
+            lds_barrier();
+            dot_flush();
+        }
     }
 
     // ---- final state (last segment only), through LDS in whole rows of 16-byte stores
@@ -676,29 +754,37 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     }
 }
 
-template <int DK, bool GATED, bool REV, bool OF32>
+template <int DK, bool GATED, bool REV, int OUT>
 hipError_t launch_c1(const KArgs& ka, hipStream_t stream) {
-    constexpr size_t lds = C1Lds<DK, GATED>::kBytes;
+    constexpr size_t lds = C1Lds<DK, GATED, OUT == kOutDot>::kBytes;
     static std::once_flag attr_once;   // thread-safe one-time init of the LDS limit
     std::call_once(attr_once, [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED, REV, OF32>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED, REV, OUT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     });
     ProfScope prof(kProfMain, stream);
-    hipLaunchKernelGGL((chunk1_kernel<DK, GATED, REV, OF32>), dim3(ka.total_groups), dim3(kC1Waves * 64), lds,
+    hipLaunchKernelGGL((chunk1_kernel<DK, GATED, REV, OUT>), dim3(ka.total_groups), dim3(kC1Waves * 64), lds,
                        stream, ka);
     return hipGetLastError();
 }
 
+template <int DK, bool GATED, int OUT>
+hipError_t launch_c1_dir(const KArgs& ka, bool reverse, hipStream_t stream) {
+    return reverse ? launch_c1<DK, GATED, true, OUT>(ka, stream) : launch_c1<DK, GATED, false, OUT>(ka, stream);
+}
+
 template <int DK>
-hipError_t launch_c1_dk(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream) {
+hipError_t launch_c1_dk(const KArgs& ka, bool gated, bool reverse, int out, hipStream_t stream) {
     if (gated) {
-        if (out_f32)
-            return reverse ? launch_c1<DK, true, true, true>(ka, stream) : launch_c1<DK, true, false, true>(ka, stream);
-        return reverse ? launch_c1<DK, true, true, false>(ka, stream) : launch_c1<DK, true, false, false>(ka, stream);
+        if (out == kOutF32) return launch_c1_dir<DK, true, kOutF32>(ka, reverse, stream);
+        if (out == kOutDot) {
+            if constexpr (DK == 128) return launch_c1_dir<DK, true, kOutDot>(ka, reverse, stream);
+            return hipErrorInvalidValue;
+        }
+        return launch_c1_dir<DK, true, kOutBf16>(ka, reverse, stream);
     }
-    if (out_f32) return hipErrorInvalidValue;
-    return reverse ? launch_c1<DK, false, true, false>(ka, stream) : launch_c1<DK, false, false, false>(ka, stream);
+    if (out != kOutBf16) return hipErrorInvalidValue;
+    return launch_c1_dir<DK, false, kOutBf16>(ka, reverse, stream);
 }
 
 }  // namespace
@@ -709,9 +795,14 @@ bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, 
            ldqk % 8 == 0 && ldv % 8 == 0 && slices >= 1 && (!out_f32 || gated);
 }
 
-hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream) {
-    if (ka.dk == 256) return launch_c1_dk<256>(ka, gated, reverse, out_f32, stream);
-    if (ka.dk == 128) return launch_c1_dk<128>(ka, gated, reverse, out_f32, stream);
+bool chunk1_dot_supported(int dk, int dv, int chunk) { return chunk == kBlk && dk == 128 && dv == kC1Cols; }
+
+hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, bool dot, hipStream_t stream) {
+    if (dot && (out_f32 || !gated || !chunk1_dot_supported(ka.dk, ka.dv, kBlk) || ka.nsl > 1 || ka.ndvt != 1))
+        return hipErrorInvalidValue;
+    const int out = dot ? kOutDot : out_f32 ? kOutF32 : kOutBf16;
+    if (ka.dk == 256) return launch_c1_dk<256>(ka, gated, reverse, out, stream);
+    if (ka.dk == 128) return launch_c1_dk<128>(ka, gated, reverse, out, stream);
     return hipErrorInvalidValue;
 }
 

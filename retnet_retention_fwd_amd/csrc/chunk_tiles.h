@@ -34,6 +34,13 @@ struct KArgs {
     // (64-token chunks only): segment 0 covers [0, pre_tokens), segment 1 the rest;
     // 0 = segments of seg_tokens each
     int pre_tokens;
+    // row dots (single-block pass, gated backward): dG[token] = (dacc ? dG[token] : 0) +
+    // dsign * <output row, xdot row>, taken from the fp32 accumulators; xdot rows have dv
+    // elements, contiguous per (b,h)
+    const bf16_t* xdot;
+    float* dG;
+    float dsign;
+    int dacc;
 };
 
 

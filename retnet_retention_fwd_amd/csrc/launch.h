@@ -40,6 +40,13 @@ struct ChunkArgs {
     int slices = 1;
     int slice_qk = 0;
     size_t slice_o = 0, slice_state = 0;
+    // Gated backward, single-block pass with one 128-column tile per row: besides the bf16
+    // output, dG[token] = (dacc ? dG[token] : 0) + dsign * <fp32 output row, xdot row>,
+    // xdot in the layout of o ([B,H,N,dv] bf16), dG [B,H,N].
+    const void* xdot = nullptr;
+    float* dG = nullptr;
+    float dsign = 1.f;
+    bool dacc = false;
 };
 
 struct DecodeArgs {
@@ -84,7 +91,9 @@ hipError_t launch_mfma_chunk(const ChunkArgs& a, const MfmaPlan& plan, hipStream
 // direction, fp32 output when gated.
 struct KArgs;
 bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool gated);
-hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, hipStream_t stream);
+// the row-dot form (ChunkArgs::xdot): gated, d_k = d_v = 128, one slice
+bool chunk1_dot_supported(int dk, int dv, int chunk);
+hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, bool dot, hipStream_t stream);
 // Main pass for chunks of 256 or 512 tokens (chunkw.hip): forward, per-head decays,
 // bf16 output, contiguous rows, one slice, d_k 128, d_v a multiple of 128.
 bool chunkw_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool reverse,
@@ -120,6 +129,7 @@ struct BwdPlan {
     int kind_q, kind_v, kind_k;   // kernel of each pass (1 matrix-core, 2 generic)
     size_t fwd_bytes;             // workspace of the largest forward pass
     bool f32acc;                  // gated bf16: the dq and dk passes write fp32 (for dg)
+    bool rowdot;                  // gated bf16 instead: they write bf16 and the row dots of dg
     // workspace offsets: forward-pass workspace, S0^T, dS^T, S_N^T, q.dq - k.dk, and the
     // d_v slices of a dq or dk pass
     size_t off_fwd, off_s0t, off_dst, off_sfin, off_dG, off_sl;

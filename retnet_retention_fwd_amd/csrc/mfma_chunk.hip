@@ -1162,6 +1162,10 @@ hipError_t launch_prep(const ChunkArgs& a, const MfmaPlan& p, int dvt, hipStream
     ka.sl_o = a.slice_o;
     ka.sl_state = a.slice_state;
     ka.pre_tokens = p.prefix_tokens;
+    ka.xdot = static_cast<const bf16_t*>(a.xdot);
+    ka.dG = a.dG;
+    ka.dsign = a.dsign;
+    ka.dacc = a.dacc ? 1 : 0;
     const int bh = a.B * a.H * ka.nsl;   // chains
     if (p.nseg > 1 && p.prefix_tokens == 0) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
@@ -1201,7 +1205,7 @@ hipError_t launch_chunk64(const ChunkArgs& a, const MfmaPlan& p, hipStream_t str
     KArgs ka;
     const hipError_t e = launch_prep<GATED, REV>(a, p, p.dvt, stream, ka);
     if (e != hipSuccess) return e;
-    return launch_chunk1(ka, GATED, REV, a.out_f32, stream);
+    return launch_chunk1(ka, GATED, REV, a.out_f32, a.xdot != nullptr, stream);
 }
 // Chunks of 256 or 512 tokens (d_k = 128, per-head decays) take the query-row parallel
 // main pass (chunkw.hip).
@@ -1295,6 +1299,10 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
     // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant, and
     // chunks of exactly one block (forward, bf16 output) the single-block main pass
     const bool one = a.chunk <= kBlk;
+    // the row-dot form exists on the single-block pass only
+    if (a.xdot != nullptr &&
+        !(p.dvt == 128 && p.nw == 8 && a.gated && !a.out_f32 && a.slices <= 1 && chunk1_dot_supported(a.dk, a.dv, a.chunk)))
+        return hipErrorInvalidValue;
     if (p.dvt == 128 && p.nw == 8 &&
         chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
                          a.out_f32, a.gated))
