@@ -109,15 +109,11 @@ struct TileCopy {
         (void)N;
     }
     // Offset and wave-uniform base of copy i for the block at row0 (bytes row0*sb).
-    // Forward: the base carries the block; REV: the lane offset does, and a row before
-    // the sequence start (negative offset) is sent out of range.
+    // Forward: the base carries the block; REV: the lane offset does.  A row before the
+    // sequence start has a negative offset, which as a 32-bit unsigned value lies at or
+    // above 2^31, past every range (ranges stay below 2^31 bytes), so it reads as zeros.
     __device__ __forceinline__ uint32_t lane_off(int i, uint32_t row0_bytes) const {
-        if constexpr (REV) {
-            const int d = static_cast<int>(voff[i]) - static_cast<int>(row0_bytes);
-            return d < 0 ? kOutOfRange : static_cast<uint32_t>(d);
-        } else {
-            return voff[i];
-        }
+        return REV ? voff[i] - row0_bytes : voff[i];
     }
     __device__ __forceinline__ static uint32_t base_off(uint32_t row0_bytes) { return REV ? 0u : row0_bytes; }
     // Rows past the end of the tensor lie outside the buffer's range and land in LDS
