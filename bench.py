@@ -60,7 +60,7 @@ BF16_PEAK_TFLOPS = 2516.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_bf16_traffic.json")
 # source of the headline's dominant kernel (the single-block chunkwise pass)
 KERNEL_SRC = os.path.join(ROOT, "retnet_retention_fwd_amd", "csrc", "chunk64.hip")
-HEADLINE_KERNEL = "chunk1_kernel<256, false> (single-block matrix-core chunkwise pass)"
+HEADLINE_KERNEL = "chunk1_kernel<256, false, false, 0> (single-block matrix-core chunkwise pass)"
 
 
 def kernel_hash() -> str:
