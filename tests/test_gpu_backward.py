@@ -94,6 +94,11 @@ CASES = [
     (2, 32, 300, 128, 256, 64, "bf16", False, True, True),
     (2, 32, 300, 128, 256, 64, "bf16", True, True, True),
     (1, 2, 150, 256, 256, 64, "bf16", True, True, True),      # gated d_k = 256, fp32 dq and dk
+    # row dots (gated, d_k = d_v = 128) in passes split in two segments: the reversed and the
+    # forward walks with a state-only prefix
+    (2, 64, 300, 128, 128, 64, "bf16", True, True, True),
+    (1, 2, 1, 128, 128, 64, "bf16", True, True, True),        # one token: a single partial chunk
+    (1, 1, 5, 256, 256, 64, "bf16", False, True, True),       # reversed d_k = 256 walk, five tokens
 ]
 
 
