@@ -22,7 +22,10 @@
 // leaves multiplied by the decay of token 0) and, gated, fp32 output.  For the gated
 // backward's dq and dk passes (one 128-column tile per row) the output can also leave
 // as bf16 together with each row's dot product against a second tensor taken from the
-// fp32 accumulators (OUT = kOutDot), which the gate gradient sums.
+// fp32 accumulators (OUT = kOutDot), which the gate gradient sums.  For the gated layer
+// (one 128-column tile per row) the output can leave already normalised and gated
+// (OUT = kOutNormGate): z = silu(gate) * o / rms(o), bf16, in the layer's token-major
+// layout, from the fp32 rows staged in LDS.
 //
 // Work decomposition: a workgroup owns one (b,h), one segment of the sequence and 128
 // state columns; its eight waves own 16 columns each and hold their DK x 16 slice of S
@@ -48,14 +51,15 @@ namespace {
 constexpr int kC1Cols = 128;   // state columns per workgroup
 constexpr int kC1Waves = 8;    // 16 columns per wave
 
-// Output forms: bf16; fp32; bf16 plus the row dots of the fp32 rows with a second tensor.
-constexpr int kOutBf16 = 0, kOutF32 = 1, kOutDot = 2;
+// Output forms: bf16; fp32; bf16 plus the row dots of the fp32 rows with a second tensor;
+// the gated layer's normalised and gated rows.
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutDot = 2, kOutNormGate = 3;
 
 // LDS layout: Q (one stage for d_k = 256, two otherwise), two stages of K and V, the P
 // fragments of the current chunk, the staging area of one output block, (gated) two
-// stages of the chunk-local log2 prefix sums and (row dots) two stages of the waves'
-// partial dots [64 rows][8 waves].
-template <int DK, bool GATED, bool DOT = false>
+// stages of the chunk-local log2 prefix sums, (row dots, norm-gate) two stages of the
+// waves' partial row sums [64 rows][8 waves] and (norm-gate) one fp32 output block.
+template <int DK, bool GATED, bool DOT = false, bool NG = false>
 struct C1Lds {
     static constexpr int QRB = DK * 2, VRB = kC1Cols * 2;       // row bytes
     static constexpr int QS = DK == 256 ? 1 : 2;                // Q stages
@@ -68,7 +72,8 @@ struct C1Lds {
     static constexpr int kG = kX + kBlk * kC1Cols * 2;
     static constexpr int kD = kG + (GATED ? 2 * kBlk * 4 : 0);
     static constexpr int kDStage = kBlk * kC1Waves * 4;
-    static constexpr int kBytes = kD + (DOT ? 2 * kDStage : 0);
+    static constexpr int kXF = kD + (DOT || NG ? 2 * kDStage : 0);
+    static constexpr int kBytes = kXF + (NG ? kBlk * kC1Cols * 4 : 0);
     static_assert(kBytes <= kLdsBytes, "LDS layout too large");
 };
 
@@ -77,11 +82,13 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     const KArgs ka) {
     constexpr bool OF32 = OUT == kOutF32;   // fp32 output
     constexpr bool DOT = OUT == kOutDot;    // bf16 output and row dots
-    // fp32 results (the output, or the row dots) take the state operand of the cross term
-    // as two bf16 terms
-    constexpr bool HILO = OUT != kOutBf16;
+    constexpr bool NG = OUT == kOutNormGate;   // normalised, gated bf16 rows
+    // fp32 results for the backward (the output, or the row dots) take the state operand of
+    // the cross term as two bf16 terms
+    constexpr bool HILO = OUT == kOutF32 || OUT == kOutDot;
     static_assert(!DOT || (GATED && DK == 128), "row dots: gated, 128-wide scores");
-    using L_ = C1Lds<DK, GATED, DOT>;
+    static_assert(!NG || (GATED && DK == 128 && !REV), "norm-gate: gated forward, 128-wide scores");
+    using L_ = C1Lds<DK, GATED, DOT, NG>;
     constexpr int NW = kC1Waves, DVT = kC1Cols;
     constexpr int QRB = L_::QRB, VRB = L_::VRB, QS = L_::QS;
     constexpr int DT = DK / 16;    // 16-row tiles of the state
@@ -139,6 +146,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     // row dots: rows of the second tensor (dv elements, token order) and the dots' output
     const bf16_t* const xd_bh = DOT ? ka.xdot + static_cast<size_t>(bh) * N * dv : nullptr;
     float* const dG_bh = DOT ? ka.dG + static_cast<size_t>(bh) * N : nullptr;
+    // norm-gate: token n's row of the gate and of z is ((b N + n) H + h) d_v in the layer's
+    // [B, N, H, d_v] layout
+    const size_t ng_b = static_cast<size_t>(bh / H) * N, ng_h = static_cast<size_t>(h) * dv;
+    auto ng_off = [&](int n) -> size_t { return (ng_b + n) * static_cast<size_t>(H) * dv + ng_h; };
     // ranges end with the last row's own columns; rows past N (REV: before 0) read as zeros
     const u32x4_t q_rs = make_rsrc(q + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
     const u32x4_t k_rs = make_rsrc(k + qk_bh, static_cast<uint32_t>((N - 1) * ldqk + DK) * 2);
@@ -501,6 +512,62 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             for (int mt = 0; mt < 4; ++mt) dp[(mt * 16 + l16) * NW + wave] = part[mt];
         }
     };
+    // ---- norm-gate: at a chunk's end the fp32 rows go to LDS (16-byte units XOR-rotated
+    // by the row) with each wave's partial sums of squares; after the next barrier every
+    // lane takes four 16-byte units, sums its row's eight partials and stores
+    // silu(gate) * x / rms as bf16.  Gate values are loaded at the top of their chunk.
+    constexpr int kNGU = DVT / 4;                          // 16-byte fp32 units per row
+    constexpr int kNGRounds = kBlk * kNGU / (NW * 64);
+    u16x4_t ngg[NG ? kNGRounds : 1];
+    int ng_row = -1, ng_len = 0;
+    auto ng_load = [&](int cs, int L) {
+#pragma unroll
+        for (int r = 0; r < kNGRounds; ++r) {
+            const int e = r * NW * 64 + tid, row = e / kNGU, u = e % kNGU;
+            ngg[r] = row < L ? *reinterpret_cast<const u16x4_t*>(ka.ng_gate + ng_off(cs + row) + col0 + 4 * u)
+                             : u16x4_t{0, 0, 0, 0};
+        }
+    };
+    auto ng_stage = [&]() {
+        float* const xf = reinterpret_cast<float*>(smem + L_::kXF);
+        float* const dp = reinterpret_cast<float*>(smem + L_::kD);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = mt * 16 + l16, u = wcol / 4 + g4;
+            *reinterpret_cast<f32x4_t*>(xf + row * DVT + 4 * (u ^ (row & 15))) = X[mt];
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += X[mt][i] * X[mt][i];
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (g4 == 0) dp[row * NW + wave] = part;
+        }
+    };
+    auto ng_emit = [&]() {
+        if (ng_row < 0) return;
+        const float* const xf = reinterpret_cast<const float*>(smem + L_::kXF);
+        const float* const dp = reinterpret_cast<const float*>(smem + L_::kD);
+#pragma unroll
+        for (int r = 0; r < kNGRounds; ++r) {
+            const int e = r * NW * 64 + tid, row = e / kNGU, u = e % kNGU;
+            if (row >= ng_len) continue;
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(xf + row * DVT + 4 * (u ^ (row & 15)));
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dp + row * NW);
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(dp + row * NW + 4);
+            const float ss = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+            // hardware reciprocal square root, exponential and reciprocal (about 1 ulp each,
+            // far below the bf16 rounding of z)
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.f / static_cast<float>(DVT)) + ka.ng_eps);
+            f32x4_t y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g = bf16_to_f32(ngg[r][i]);
+                y[i] = g * __builtin_amdgcn_rcpf(1.f + exp2_fast(-g * kLog2e)) * x[i] * inv;
+            }
+            *reinterpret_cast<u16x4_t*>(ka.ng_out + ng_off(ng_row + row) + col0 + 4 * u) = bf4(y);
+        }
+        ng_row = -1;
+    };
     auto dot_flush = [&]() {
         if (wave == NW - 1 && dot_row >= 0 && lane < dot_len) {
             const float* const dp = reinterpret_cast<const float*>(smem + L_::kD + dot_st * L_::kDStage) + lane * NW;
@@ -551,6 +618,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         if constexpr (DOT) {
             dot_flush();
             if (!sonly) dot_load(cs, L);
+        }
+        if constexpr (NG) {
+            ng_emit();
+            if (!sonly) ng_load(cs, L);
         }
         if (has_next) g_load(static_cast<int>(next_row));
 
@@ -698,7 +769,11 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // the output block: bf16, staged when more chunks follow (stored after the next
         // barrier); else (and fp32) stored from the accumulators, rows past the chunk end
         // skipped (REV: walk row r of the chunk is token N-1-(cs+r))
-        if (!OF32 && full && has_next) {
+        if (NG) {
+            ng_stage();
+            ng_row = cs;
+            ng_len = L;
+        } else if (!OF32 && full && has_next) {
             stage_write();
             xs_row = cs;
         } else {
@@ -723,6 +798,12 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         if (dot_row >= 0) {
             lds_barrier();
             dot_flush();
+        }
+    }
+    if constexpr (NG) {
+        if (ng_row >= 0) {
+            lds_barrier();
+            ng_emit();
         }
     }
 
@@ -756,7 +837,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
 template <int DK, bool GATED, bool REV, int OUT>
 hipError_t launch_c1(const KArgs& ka, hipStream_t stream) {
-    constexpr size_t lds = C1Lds<DK, GATED, OUT == kOutDot>::kBytes;
+    constexpr size_t lds = C1Lds<DK, GATED, OUT == kOutDot, OUT == kOutNormGate>::kBytes;
     static std::once_flag attr_once;   // thread-safe one-time init of the LDS limit
     std::call_once(attr_once, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk1_kernel<DK, GATED, REV, OUT>),
@@ -781,6 +862,12 @@ hipError_t launch_c1_dk(const KArgs& ka, bool gated, bool reverse, int out, hipS
             if constexpr (DK == 128) return launch_c1_dir<DK, true, kOutDot>(ka, reverse, stream);
             return hipErrorInvalidValue;
         }
+        if (out == kOutNormGate) {
+            if constexpr (DK == 128) {
+                if (!reverse) return launch_c1<DK, true, false, kOutNormGate>(ka, stream);
+            }
+            return hipErrorInvalidValue;
+        }
         return launch_c1_dir<DK, true, kOutBf16>(ka, reverse, stream);
     }
     if (out != kOutBf16) return hipErrorInvalidValue;
@@ -798,9 +885,11 @@ bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, 
 bool chunk1_dot_supported(int dk, int dv, int chunk) { return chunk == kBlk && dk == 128 && dv == kC1Cols; }
 
 hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, bool dot, hipStream_t stream) {
-    if (dot && (out_f32 || !gated || !chunk1_dot_supported(ka.dk, ka.dv, kBlk) || ka.nsl > 1 || ka.ndvt != 1))
+    const bool ng = ka.ng_gate != nullptr;
+    if ((dot || ng) && (out_f32 || (dot && ng) || !gated || !chunk1_dot_supported(ka.dk, ka.dv, kBlk) ||
+                        ka.nsl > 1 || ka.ndvt != 1 || (ng && reverse)))
         return hipErrorInvalidValue;
-    const int out = dot ? kOutDot : out_f32 ? kOutF32 : kOutBf16;
+    const int out = dot ? kOutDot : ng ? kOutNormGate : out_f32 ? kOutF32 : kOutBf16;
     if (ka.dk == 256) return launch_c1_dk<256>(ka, gated, reverse, out, stream);
     if (ka.dk == 128) return launch_c1_dk<128>(ka, gated, reverse, out, stream);
     return hipErrorInvalidValue;

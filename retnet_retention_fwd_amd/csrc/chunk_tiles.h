@@ -41,6 +41,11 @@ struct KArgs {
     float* dG;
     float dsign;
     int dacc;
+    // norm-gate output (single-block pass, gated layer): instead of o, z = silu(gate) * o *
+    // (mean(o^2) + eps)^(-1/2) per row, bf16, gate and z in [B, N, H, dv] layout
+    const bf16_t* ng_gate;
+    bf16_t* ng_out;
+    float ng_eps;
 };
 
 

@@ -47,6 +47,12 @@ struct ChunkArgs {
     float* dG = nullptr;
     float dsign = 1.f;
     bool dacc = false;
+    // Gated layer, single-block pass with one 128-column tile per row, forward: instead of
+    // o, z[b, n, h, :] = silu(gate[b, n, h, :]) * o_n * (mean(o_n^2) + ng_eps)^(-1/2) as bf16
+    // (gate and z in the layer's [B, N, H, dv] layout; o is not written).
+    const void* ng_gate = nullptr;
+    void* ng_out = nullptr;
+    float ng_eps = 0.f;
 };
 
 struct DecodeArgs {

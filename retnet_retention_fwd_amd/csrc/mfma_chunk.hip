@@ -1166,6 +1166,9 @@ hipError_t launch_prep(const ChunkArgs& a, const MfmaPlan& p, int dvt, hipStream
     ka.dG = a.dG;
     ka.dsign = a.dsign;
     ka.dacc = a.dacc ? 1 : 0;
+    ka.ng_gate = static_cast<const bf16_t*>(a.ng_gate);
+    ka.ng_out = static_cast<bf16_t*>(a.ng_out);
+    ka.ng_eps = a.ng_eps;
     const int bh = a.B * a.H * ka.nsl;   // chains
     if (p.nseg > 1 && p.prefix_tokens == 0) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
@@ -1299,9 +1302,10 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
     // multiple of its 64-token blocks; chunks of one block take the ONEBLK variant, and
     // chunks of exactly one block (forward, bf16 output) the single-block main pass
     const bool one = a.chunk <= kBlk;
-    // the row-dot form exists on the single-block pass only
-    if (a.xdot != nullptr &&
-        !(p.dvt == 128 && p.nw == 8 && a.gated && !a.out_f32 && a.slices <= 1 && chunk1_dot_supported(a.dk, a.dv, a.chunk)))
+    // the row-dot and norm-gate forms exist on the single-block pass only
+    if ((a.xdot != nullptr || a.ng_gate != nullptr) &&
+        !(p.dvt == 128 && p.nw == 8 && a.gated && !a.out_f32 && a.slices <= 1 && chunk1_dot_supported(a.dk, a.dv, a.chunk) &&
+          !(a.ng_gate != nullptr && (a.reverse || a.xdot != nullptr))))
         return hipErrorInvalidValue;
     if (p.dvt == 128 && p.nw == 8 &&
         chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,

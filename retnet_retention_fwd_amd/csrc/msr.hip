@@ -513,14 +513,24 @@ hipError_t run_msr(const MsrShape& s, const MsrPtrs& x, const MsrPlan& p, void* 
     }
     ChunkArgs a{q, k, v, g, o, nullptr, nullptr, s.B, s.H, s.N, s.dk, s.dv, p.chunk, true, true,
                 ws + p.off_ret, p.ret.workspace_bytes};
-    a.out_f32 = true;
-    RETN_TRY(launch_mfma_chunk(a, p.ret, st));
-    const size_t rows = T * s.H;
-    const size_t rows_per_block = 4 * static_cast<size_t>(64 / gate_lanes_per_row(s.dv));
-    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((rows + rows_per_block - 1) / rows_per_block, 1u << 20));
-    hipLaunchKernelGGL(msr_gate_kernel, dim3(blocks), dim3(256), 0, st, o, static_cast<const bf16_t*>(gp),
-                       static_cast<bf16_t*>(z), T, s.N, s.H, s.dv, s.norm_eps);
-    RETN_TRY(hipGetLastError());
+    if (chunk1_dot_supported(s.dk, s.dv, p.chunk)) {
+        // one 128-column tile per row: the retention pass normalises and gates its own
+        // fp32 rows and writes z (no fp32 round trip, no separate gate launch)
+        a.ng_gate = gp;
+        a.ng_out = z;
+        a.ng_eps = s.norm_eps;
+        RETN_TRY(launch_mfma_chunk(a, p.ret, st));
+    } else {
+        a.out_f32 = true;
+        RETN_TRY(launch_mfma_chunk(a, p.ret, st));
+        const size_t rows = T * s.H;
+        const size_t rows_per_block = 4 * static_cast<size_t>(64 / gate_lanes_per_row(s.dv));
+        const unsigned blocks =
+            static_cast<unsigned>(std::min<size_t>((rows + rows_per_block - 1) / rows_per_block, 1u << 20));
+        hipLaunchKernelGGL(msr_gate_kernel, dim3(blocks), dim3(256), 0, st, o, static_cast<const bf16_t*>(gp),
+                           static_cast<bf16_t*>(z), T, s.N, s.H, s.dv, s.norm_eps);
+        RETN_TRY(hipGetLastError());
+    }
     RETN_TRY(launch_gemm_tn(z, x.wo, x.y, M, s.D, s.H * s.dv, false, st));
 #undef RETN_TRY
     return hipSuccess;
