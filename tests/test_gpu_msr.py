@@ -76,6 +76,11 @@ CASES = [
     (1, 40, 64, 1, 64, 320, 64),
     (1, 1900, 64, 8, 128, 128, 64),
     (1, 1900, 192, 8, 128, 128, 64),
+    # d = 128 heads in 64-token chunks: the retention pass writes the normalised, gated
+    # rows itself; two batch rows (the token-major row index), a partial last chunk, one
+    # token
+    (2, 300, 128, 4, 128, 128, 64),
+    (1, 1, 64, 2, 128, 128, 64),
 ]
 
 
