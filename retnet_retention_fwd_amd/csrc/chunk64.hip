@@ -475,8 +475,8 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     // The walk: npre state-only chunks (the first segment of a prefix split, walked by
     // segment 1 for its entry state), then the segment's nck chunks.  Chunk c is staged
     // in stage c % 2; the next chunk's copies go out between the products of the cross
-    // term (full steps; with one Q stage its Q copies after the P barrier) or of the
-    // state update (state-only steps).
+    // term (full steps; with one Q stage its Q copies after the P barrier) or all at once
+    // before the state update (state-only steps).
     const int ntot = npre + nck;
     auto chunk_row = [&](int c) -> int { return c < npre ? c * kBlk : t_begin + (c - npre) * kBlk; };
 
@@ -730,12 +730,14 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
         }
 
-        // the state update; a state-only step issues all of the next chunk's copies
-        // between its products, a full step with one Q stage the Q copies
+        // the state update.  A state-only step is short and its next chunk's copies set
+        // its pace (their latency, not its arithmetic: measured), so it issues all of them
+        // before its products; a full step with one Q stage issues the Q copies between
+        // the products.
+        if (sonly && has_next) copy_slice(0, kOps, 0, 1);
         state_update(koff, voff, gl, L, full, [&](int kh, int gi, int ng) {
             if (!has_next) return;
-            if (sonly) copy_slice(0, kOps, kh * ng + gi, 2 * ng);
-            else if (QS == 1 && kh == 0) copy_slice(kCrossOps, kOps, gi, ng);
+            if (!sonly && QS == 1 && kh == 0) copy_slice(kCrossOps, kOps, gi, ng);
         });
         if (sonly) {
             if (has_next) g_scan(1 - ST);
