@@ -147,11 +147,12 @@ struct RowDot {
 hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
                         const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
                         void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32,
-                        const RowDot* rd = nullptr) {
+                        const RowDot* rd = nullptr, int st_ld = 0) {
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
                 ws_bytes};
     a.out_f32 = out_f32;
     a.reverse = rev;
+    a.state_in_ld = st_ld;
     if (rd != nullptr) {
         a.xdot = rd->x;
         a.dG = rd->dG;
@@ -166,10 +167,10 @@ hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* 
 // chains of one matrix-core launch; slice p's output goes to o + p * tokens * dk.
 hipError_t sliced_pass(const BwdShape& s, const BwdPlan& p, int kind, const void* q, const void* k, const void* v,
                        const float* decay, void* o, const float* state_in, float* state_out, void* ws, hipStream_t st,
-                       bool rev, bool out_f32, const RowDot* rd = nullptr) {
+                       bool rev, bool out_f32, const RowDot* rd = nullptr, int st_ld = 0) {
     if (p.parts == 1)
         return forward_pass(s, kind, q, k, v, decay, o, state_in, state_out, p.w, s.dk, ws, p.fwd_bytes, st, rev,
-                            out_f32, rd);
+                            out_f32, rd, st_ld);
     if (rd != nullptr) return hipErrorInvalidValue;   // row dots need whole rows
     const size_t tokens = static_cast<size_t>(s.B) * s.H * s.N;
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, p.w, s.dk, s.chunk, s.bf16, s.gated, ws,
@@ -181,7 +182,27 @@ hipError_t sliced_pass(const BwdShape& s, const BwdPlan& p, int kind, const void
     a.slice_qk = p.w;
     a.slice_o = tokens * s.dk;
     a.slice_state = static_cast<size_t>(s.B) * s.H * p.w * s.dk;
+    a.state_in_ld = st_ld;
     return launch_mfma_chunk(a, mfma_chunk_plan(s.B, s.H * p.parts, s.N, p.w, s.dk, s.chunk, s.gated), st);
+}
+
+// Per head, the dq and dk passes can read S0 and dS transposed in place (no transpose
+// launch) when the single-block pass runs them with no separate scan.  Gated, the gate
+// gradient pairs dS^T with the dq pass's final state in the transposed layout, so the
+// transposes stay.
+bool transposed_in_place(const BwdShape& s, const BwdPlan& p) {
+    if (s.gated || p.kind_q != kMfma || p.kind_k != kMfma || p.f32acc || p.rowdot) return false;
+    ChunkArgs a{};
+    a.B = s.B;
+    a.H = s.H;
+    a.N = s.N;
+    a.dk = p.w;
+    a.dv = s.dk;
+    a.chunk = s.chunk;
+    a.bf16 = s.bf16;
+    a.ldqk = p.parts > 1 ? s.dv : 0;
+    a.slices = p.parts;
+    return chunk1_takes(a, mfma_chunk_plan(s.B, s.H * p.parts, s.N, p.w, s.dk, s.chunk, s.gated));
 }
 
 }  // namespace
@@ -235,15 +256,21 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
         return hipSuccess;
     };
 
-    // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass), in one launch
-    RETN_TRY(launch_state_transpose(has_s0 ? x.state_in : nullptr, s0t, has_ds ? x.dstate_out : nullptr, dst, bh, s.dk,
-                                    s.dv, P, st));
+    // transposed states in d_v slices: S0^T (dq pass), dS^T (dk pass), in one launch, unless
+    // the passes read them transposed in place
+    const bool tin = transposed_in_place(s, p);
+    const int st_ld = tin ? s.dv : 0;
+    if (!tin)
+        RETN_TRY(launch_state_transpose(has_s0 ? x.state_in : nullptr, s0t, has_ds ? x.dstate_out : nullptr, dst, bh,
+                                        s.dk, s.dv, P, st));
+    const float* const s0_in = has_s0 ? (tin ? x.state_in : s0t) : nullptr;
+    const float* const ds_in = has_ds ? (tin ? x.dstate_out : dst) : nullptr;
 
     // ---- dq = forward(dO, v, k) from S0^T; its final state is S_N^T (gated, with dS);
     // row dots: dG = q . dq
     const RowDot rdq{x.q, dG, 1.f, false}, rdk{x.k, dG, -1.f, true};
-    RETN_TRY(sliced_pass(s, p, p.kind_q, x.dout, x.v, x.k, x.decay, direct ? x.dq : sl, has_s0 ? s0t : nullptr,
-                         s.gated && has_ds ? sfin : nullptr, fws, st, false, f32, p.rowdot ? &rdq : nullptr));
+    RETN_TRY(sliced_pass(s, p, p.kind_q, x.dout, x.v, x.k, x.decay, direct ? x.dq : sl, s0_in,
+                         s.gated && has_ds ? sfin : nullptr, fws, st, false, f32, p.rowdot ? &rdq : nullptr, st_ld));
     RETN_TRY(finish(x.dq, x.q, 1.f, false));
 
     // ---- dv = forward(k, q, dO) walking backwards from dS; it ends with dS0 = lam_0 U_0
@@ -251,8 +278,8 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
                           p.fwd_bytes, st, true, false));
 
     // ---- dk = forward(v, dO, q) walking backwards from dS^T
-    RETN_TRY(sliced_pass(s, p, p.kind_k, x.v, x.dout, x.q, x.decay, direct ? x.dk : sl, has_ds ? dst : nullptr,
-                         nullptr, fws, st, true, f32, p.rowdot ? &rdk : nullptr));
+    RETN_TRY(sliced_pass(s, p, p.kind_k, x.v, x.dout, x.q, x.decay, direct ? x.dk : sl, ds_in, nullptr, fws, st, true,
+                         f32, p.rowdot ? &rdk : nullptr, st_ld));
     RETN_TRY(finish(x.dk, x.k, -1.f, true));
 
     // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>

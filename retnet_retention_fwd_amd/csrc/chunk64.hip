@@ -183,8 +183,20 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         for (int dt = 0; dt < DT; ++dt) S[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (nseg == 1 || split || ka.fuse_scan) {
             int sg0 = 0;
-            if (ka.state_in != nullptr) {
+            if (ka.state_in != nullptr && ka.st_ld > 0) {
+                // the incoming state in place in the caller's layout, transposed: element
+                // (r, c) of slice slc is row c, column slc * DK + r of a [dv][st_ld] state
+                const float* const src = ka.state_in + static_cast<size_t>(bh) * dv * ka.st_ld +
+                                         static_cast<size_t>(slc) * DK;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[dt][i] = src[static_cast<size_t>(cidx) * ka.st_ld + srow(dt, i)];
+            } else if (ka.state_in != nullptr) {
                 load(ka.state_in + s_bh, 0.f, false);
+            }
+            if (ka.state_in != nullptr) {
                 if constexpr (REV && !GATED) {
                     const float inv = 1.f / decay[h];
 #pragma unroll

@@ -46,6 +46,9 @@ struct KArgs {
     const bf16_t* ng_gate;
     bf16_t* ng_out;
     float ng_eps;
+    // single-block pass: > 0 means state_in is the caller's [B*H][dv][st_ld] state read
+    // transposed in place (slice p's element (r, c) is row c, column p * dk + r)
+    int st_ld;
 };
 
 

@@ -53,6 +53,10 @@ struct ChunkArgs {
     const void* ng_gate = nullptr;
     void* ng_out = nullptr;
     float ng_eps = 0.f;
+    // > 0: state_in is a [B*H][dv][state_in_ld] state (the caller's layout of a pass that
+    // works on the transposed state in d_k slices) read transposed in place; only where
+    // chunk1_takes() says the single-block pass runs the call with no separate scan.
+    int state_in_ld = 0;
 };
 
 struct DecodeArgs {
@@ -99,6 +103,9 @@ struct KArgs;
 bool chunk1_supported(int dk, int dv, int chunk, int ldqk, int ldv, int slices, bool out_f32, bool gated);
 // the row-dot form (ChunkArgs::xdot): gated, d_k = d_v = 128, one slice
 bool chunk1_dot_supported(int dk, int dv, int chunk);
+// The call runs on the single-block pass and its entry states need no separate scan (so
+// it can take ChunkArgs::state_in_ld).
+bool chunk1_takes(const ChunkArgs& a, const MfmaPlan& p);
 hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, bool dot, hipStream_t stream);
 // Main pass for chunks of 256 or 512 tokens (chunkw.hip): forward, per-head decays,
 // bf16 output, contiguous rows, one slice, d_k 128, d_v a multiple of 128.

@@ -1169,6 +1169,7 @@ hipError_t launch_prep(const ChunkArgs& a, const MfmaPlan& p, int dvt, hipStream
     ka.ng_gate = static_cast<const bf16_t*>(a.ng_gate);
     ka.ng_out = static_cast<bf16_t*>(a.ng_out);
     ka.ng_eps = a.ng_eps;
+    ka.st_ld = a.state_in_ld;
     const int bh = a.B * a.H * ka.nsl;   // chains
     if (p.nseg > 1 && p.prefix_tokens == 0) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
@@ -1239,6 +1240,13 @@ void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
 
 }  // namespace
 
+bool chunk1_takes(const ChunkArgs& a, const MfmaPlan& p) {
+    return p.dvt == 128 && p.nw == 8 &&
+           chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
+                            a.out_f32, a.gated) &&
+           (p.nseg == 1 || p.prefix_tokens > 0 || p.fuse_scan);
+}
+
 bool mfma_chunk_supported(int dk, int dv, int chunk, bool bf16) {
     if (!bf16) return false;
     if (dk != 64 && dk != 128 && dk != 256) return false;
@@ -1307,6 +1315,7 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
         !(p.dvt == 128 && p.nw == 8 && a.gated && !a.out_f32 && a.slices <= 1 && chunk1_dot_supported(a.dk, a.dv, a.chunk) &&
           !(a.ng_gate != nullptr && (a.reverse || a.xdot != nullptr))))
         return hipErrorInvalidValue;
+    if (a.state_in_ld > 0 && !chunk1_takes(a, p)) return hipErrorInvalidValue;
     if (p.dvt == 128 && p.nw == 8 &&
         chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
                          a.out_f32, a.gated))
