@@ -498,7 +498,9 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     // top of the chunk.
     u16x4_t xdl[DOT ? 4 : 1];
     int dot_row = -1, dot_len = 0, dot_st = 0;   // the chunk whose partials wait in LDS
+    float dg_prev = 0.f;   // wave 7, accumulating: dG of row `lane` of the chunk, loaded early
     auto dot_load = [&](int cs, int L) {
+        if (wave == NW - 1 && ka.dacc && lane < L) dg_prev = dG_bh[REV ? N - 1 - (cs + lane) : cs + lane];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int row = mt * 16 + l16;
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dp), b = *reinterpret_cast<const f32x4_t*>(dp + 4);
             const float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
             float* const dst = dG_bh + (REV ? N - 1 - (dot_row + lane) : dot_row + lane);
-            *dst = (ka.dacc ? *dst : 0.f) + ka.dsign * sum;
+            *dst = (ka.dacc ? dg_prev : 0.f) + ka.dsign * sum;
         }
         dot_row = -1;
     };
