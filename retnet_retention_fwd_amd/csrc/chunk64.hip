@@ -167,22 +167,22 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     auto srow = [&](int dt, int i) -> int { return 32 * (dt >> 1) + 8 * g4 + 4 * ((dt ^ g4) & 1) + i; };
 
     // ---- incoming state: state_in, the scanned entry state, or (fuse_scan) composed here
+    // Each stored state is fetched as one batch of loads, all issued before any is used
+    // (the sched barrier keeps the scheduler from pairing every load with its use): the
+    // walk's start then waits on these loads' latency once per batch.
     f32x4_t S[DT];
     {
         const int cidx = col0 + wcol + l16;
-        auto load = [&](const float* src, float scale, bool add) {
+        auto fetch = [&](auto& x, const float* src) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = src[static_cast<uint32_t>(srow(dt, i) * dv + cidx)];
-                    S[dt][i] = add ? S[dt][i] * scale + x : x;
-                }
+                for (int i = 0; i < 4; ++i) x[dt][i] = src[static_cast<uint32_t>(srow(dt, i) * dv + cidx)];
+            __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) S[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (nseg == 1 || split || ka.fuse_scan) {
-            int sg0 = 0;
             if (ka.state_in != nullptr && ka.st_ld > 0) {
                 // the incoming state in place in the caller's layout, transposed: element
                 // (r, c) of slice slc is row c, column slc * DK + r of a [dv][st_ld] state
@@ -193,8 +193,9 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         S[dt][i] = src[static_cast<size_t>(cidx) * ka.st_ld + srow(dt, i)];
+                __builtin_amdgcn_sched_barrier(0);
             } else if (ka.state_in != nullptr) {
-                load(ka.state_in + s_bh, 0.f, false);
+                fetch(S, ka.state_in + s_bh);
             }
             if (ka.state_in != nullptr) {
                 if constexpr (REV && !GATED) {
@@ -202,15 +203,28 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) S[dt] *= inv;
                 }
-            } else if (seg > 0 && !split) {
-                load(ka.seg_state + static_cast<size_t>(ch) * nseg * s_stride_seg, 0.f, false);
-                sg0 = 1;
             }
-            for (int sg = sg0; nseg > 1 && !split && sg < seg; ++sg)
-                load(ka.seg_state + (static_cast<size_t>(ch) * nseg + sg) * s_stride_seg,
-                     exp2f(ka.seg_log2[static_cast<size_t>(ch) * nseg + sg]), true);
+            // the local states of the segments before this one, folded in order (from no
+            // incoming state, the first is taken as it is)
+            const int nfold = (nseg > 1 && !split) ? seg : 0;
+            const float* const ss = ka.seg_state + static_cast<size_t>(ch) * nseg * s_stride_seg;
+            const float* const sl = ka.seg_log2 + static_cast<size_t>(ch) * nseg;
+            int sg = 0;
+            if (nfold > 0 && ka.state_in == nullptr) {
+                fetch(S, ss);
+                sg = 1;
+            }
+            for (; sg < nfold; ++sg) {
+                float x[DT][4];
+                fetch(x, ss + sg * s_stride_seg);
+                const float scale = exp2f(sl[sg]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[dt][i] = S[dt][i] * scale + x[dt][i];
+            }
         } else {
-            load(ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg, 0.f, false);
+            fetch(S, ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg);
         }
     }
 
