@@ -147,12 +147,13 @@ struct RowDot {
 hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* k, const void* v,
                         const float* decay, void* o, const float* state_in, float* state_out, int dkp, int dvp,
                         void* ws, size_t ws_bytes, hipStream_t st, bool rev, bool out_f32,
-                        const RowDot* rd = nullptr, int st_ld = 0) {
+                        const RowDot* rd = nullptr, int st_ld = 0, bool seg_t = false) {
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, dkp, dvp, s.chunk, s.bf16, s.gated, ws,
                 ws_bytes};
     a.out_f32 = out_f32;
     a.reverse = rev;
     a.state_in_ld = st_ld;
+    a.seg_from_t = seg_t;
     if (rd != nullptr) {
         a.xdot = rd->x;
         a.dG = rd->dG;
@@ -167,11 +168,11 @@ hipError_t forward_pass(const BwdShape& s, int kind, const void* q, const void* 
 // chains of one matrix-core launch; slice p's output goes to o + p * tokens * dk.
 hipError_t sliced_pass(const BwdShape& s, const BwdPlan& p, int kind, const void* q, const void* k, const void* v,
                        const float* decay, void* o, const float* state_in, float* state_out, void* ws, hipStream_t st,
-                       bool rev, bool out_f32, const RowDot* rd = nullptr, int st_ld = 0) {
+                       bool rev, bool out_f32, const RowDot* rd = nullptr, int st_ld = 0, bool seg_t = false) {
     if (p.parts == 1)
         return forward_pass(s, kind, q, k, v, decay, o, state_in, state_out, p.w, s.dk, ws, p.fwd_bytes, st, rev,
-                            out_f32, rd, st_ld);
-    if (rd != nullptr) return hipErrorInvalidValue;   // row dots need whole rows
+                            out_f32, rd, st_ld, seg_t);
+    if (rd != nullptr || seg_t) return hipErrorInvalidValue;   // row dots and shared states: whole rows
     const size_t tokens = static_cast<size_t>(s.B) * s.H * s.N;
     ChunkArgs a{q, k, v, decay, o, state_in, state_out, s.B, s.H, s.N, p.w, s.dk, s.chunk, s.bf16, s.gated, ws,
                 p.fwd_bytes};
@@ -277,9 +278,13 @@ hipError_t run_backward(const BwdShape& s, const BwdPtrs& x, const BwdPlan& p, v
     RETN_TRY(forward_pass(s, p.kind_v, x.k, x.q, x.dout, x.decay, x.dv, x.dstate_out, x.dstate_in, s.dk, s.dv, fws,
                           p.fwd_bytes, st, true, false));
 
-    // ---- dk = forward(v, dO, q) walking backwards from dS^T
+    // ---- dk = forward(v, dO, q) walking backwards from dS^T.  Its state is U^T, so where
+    // both passes split the sequence alike, the segment states the dv pass left in the
+    // workspace serve it transposed and it runs no pre-pass of its own.
+    const bool share = P == 1 && p.kind_v == kMfma && p.kind_k == kMfma &&
+                       seg_shareable(s.B, s.H, s.N, s.dv, s.dk, s.chunk, s.gated, f32);
     RETN_TRY(sliced_pass(s, p, p.kind_k, x.v, x.dout, x.q, x.decay, direct ? x.dk : sl, ds_in, nullptr, fws, st, true,
-                         f32, p.rowdot ? &rdk : nullptr, st_ld));
+                         f32, p.rowdot ? &rdk : nullptr, st_ld, share));
     RETN_TRY(finish(x.dk, x.k, -1.f, true));
 
     // ---- gated: dg = reversed cumulative sum of q.dq - k.dk, plus <dS, S_N> = <dS^T, S_N^T>

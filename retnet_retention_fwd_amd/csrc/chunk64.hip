@@ -180,6 +180,21 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
                 for (int i = 0; i < 4; ++i) x[dt][i] = src[static_cast<uint32_t>(srow(dt, i) * dv + cidx)];
             __builtin_amdgcn_sched_barrier(0);
         };
+        // a segment state: seg_t, one of the transposed problem (d_k and d_v exchanged),
+        // whose row cidx holds this lane's four consecutive state rows in 16 bytes
+        auto fetch_seg = [&](auto& x, const float* src) {
+            if (ka.seg_t) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const f32x4_t t = *reinterpret_cast<const f32x4_t*>(src + static_cast<uint32_t>(cidx * DK + srow(dt, 0)));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[dt][i] = t[i];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                fetch(x, src);
+            }
+        };
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) S[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (nseg == 1 || split || ka.fuse_scan) {
@@ -211,12 +226,12 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
             const float* const sl = ka.seg_log2 + static_cast<size_t>(ch) * nseg;
             int sg = 0;
             if (nfold > 0 && ka.state_in == nullptr) {
-                fetch(S, ss);
+                fetch_seg(S, ss);
                 sg = 1;
             }
             for (; sg < nfold; ++sg) {
                 float x[DT][4];
-                fetch(x, ss + sg * s_stride_seg);
+                fetch_seg(x, ss + sg * s_stride_seg);
                 const float scale = exp2f(sl[sg]);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
                     for (int i = 0; i < 4; ++i) S[dt][i] = S[dt][i] * scale + x[dt][i];
             }
         } else {
-            fetch(S, ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg);
+            fetch_seg(S, ka.seg_state + (static_cast<size_t>(ch) * nseg + seg) * s_stride_seg);
         }
     }
 

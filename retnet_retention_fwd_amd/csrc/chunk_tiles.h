@@ -49,6 +49,9 @@ struct KArgs {
     // single-block pass: > 0 means state_in is the caller's [B*H][dv][st_ld] state read
     // transposed in place (slice p's element (r, c) is row c, column p * dk + r)
     int st_ld;
+    // single-block pass: 1 means seg_state holds the segment states of the transposed
+    // problem (d_k and d_v exchanged), read transposed (element (r, c) at c * d_k + r)
+    int seg_t;
 };
 
 

@@ -57,6 +57,12 @@ struct ChunkArgs {
     // works on the transposed state in d_k slices) read transposed in place; only where
     // chunk1_takes() says the single-block pass runs the call with no separate scan.
     int state_in_ld = 0;
+    // The workspace already holds the segment states (local, or scanned entry states) that
+    // an earlier call with this call's plan wrote for the transposed problem: d_k and d_v
+    // exchanged, same decays, direction, segments and state_in (transposed), one slice.
+    // This call skips its pre-pass and scan and reads them transposed; single-block pass
+    // only (seg_shareable()).
+    bool seg_from_t = false;
 };
 
 struct DecodeArgs {
@@ -106,6 +112,11 @@ bool chunk1_dot_supported(int dk, int dv, int chunk);
 // The call runs on the single-block pass and its entry states need no separate scan (so
 // it can take ChunkArgs::state_in_ld).
 bool chunk1_takes(const ChunkArgs& a, const MfmaPlan& p);
+// A call of shape (B, H, N, dk, dv) can take ChunkArgs::seg_from_t from a call of the
+// transposed shape (dk and dv exchanged) on the same workspace: both plans split the
+// sequence into the same segments with a pre-pass, and this call runs on the
+// single-block pass.
+bool seg_shareable(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool out_f32);
 hipError_t launch_chunk1(const KArgs& ka, bool gated, bool reverse, bool out_f32, bool dot, hipStream_t stream);
 // Main pass for chunks of 256 or 512 tokens (chunkw.hip): forward, per-head decays,
 // bf16 output, contiguous rows, one slice, d_k 128, d_v a multiple of 128.

@@ -1170,11 +1170,15 @@ hipError_t launch_prep(const ChunkArgs& a, const MfmaPlan& p, int dvt, hipStream
     ka.ng_out = static_cast<bf16_t*>(a.ng_out);
     ka.ng_eps = a.ng_eps;
     ka.st_ld = a.state_in_ld;
+    ka.seg_t = a.seg_from_t ? 1 : 0;
     const int bh = a.B * a.H * ka.nsl;   // chains
     if (p.nseg > 1 && p.prefix_tokens == 0) {
         const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
         ka.seg_state = static_cast<float*>(a.workspace);
         ka.seg_log2 = ka.seg_state + static_cast<size_t>(bh) * p.nseg * per_bh;
+    }
+    if (p.nseg > 1 && p.prefix_tokens == 0 && !a.seg_from_t) {
+        const size_t per_bh = static_cast<size_t>(a.dk) * a.dv;
         KArgs pre = ka;
         pre.total_groups = bh;
         hipError_t e = launch_pre<GATED, REV>(pre, p, stream);
@@ -1239,6 +1243,14 @@ void pick_tile(int dk, int dv, int chunk, bool gated, int& dvt, int& nw) {
 }
 
 }  // namespace
+
+bool seg_shareable(int B, int H, int N, int dk, int dv, int chunk, bool gated, bool out_f32) {
+    const MfmaPlan p = mfma_chunk_plan(B, H, N, dk, dv, chunk, gated);
+    const MfmaPlan t = mfma_chunk_plan(B, H, N, dv, dk, chunk, gated);
+    return p.nseg > 1 && p.prefix_tokens == 0 && t.prefix_tokens == 0 && p.nseg == t.nseg &&
+           p.seg_chunks == t.seg_chunks && p.fuse_scan == t.fuse_scan && p.workspace_bytes == t.workspace_bytes &&
+           p.dvt == 128 && p.nw == 8 && chunk1_supported(dk, dv, chunk, dk, dv, 1, out_f32, gated);
+}
 
 bool chunk1_takes(const ChunkArgs& a, const MfmaPlan& p) {
     return p.dvt == 128 && p.nw == 8 &&
@@ -1316,6 +1328,9 @@ hipError_t launch_dir(const ChunkArgs& a, const MfmaPlan& p, hipStream_t stream)
           !(a.ng_gate != nullptr && (a.reverse || a.xdot != nullptr))))
         return hipErrorInvalidValue;
     if (a.state_in_ld > 0 && !chunk1_takes(a, p)) return hipErrorInvalidValue;
+    if (a.seg_from_t && !(a.slices <= 1 && a.ldqk <= a.dk && a.ldv <= a.dv &&
+                          seg_shareable(a.B, a.H, a.N, a.dk, a.dv, a.chunk, a.gated, a.out_f32)))
+        return hipErrorInvalidValue;
     if (p.dvt == 128 && p.nw == 8 &&
         chunk1_supported(a.dk, a.dv, a.chunk, a.ldqk > 0 ? a.ldqk : a.dk, a.ldv > 0 ? a.ldv : a.dv, a.slices,
                          a.out_f32, a.gated))

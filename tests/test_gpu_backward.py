@@ -99,6 +99,12 @@ CASES = [
     (2, 64, 300, 128, 128, 64, "bf16", True, True, True),
     (1, 2, 1, 128, 128, 64, "bf16", True, True, True),        # one token: a single partial chunk
     (1, 1, 5, 256, 256, 64, "bf16", False, True, True),       # reversed d_k = 256 walk, five tokens
+    # the dk pass reads the dv pass's segment states transposed: scanned entry states (19 and
+    # 11 segments; gated row dots, and a per-head d_k = d_v = 256 walk), composed in the pass
+    # (3 segments) as above at (2, 2, 150) and (1, 2, 150)
+    (1, 1, 1200, 128, 128, 64, "bf16", True, True, True),
+    (1, 1, 700, 256, 256, 64, "bf16", False, True, True),
+    (1, 1, 700, 256, 256, 64, "bf16", False, False, False),
 ]
 
 
