@@ -363,6 +363,25 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         vcp.issue_one(i, lds0 + L_::kV + b * L_::kVTile + wofs, v_rs, row0 * v_rb);
     };
 
+    // ---- per head, the state-only prefix walk of a prefix split runs over three stages
+    // of K and V, so each prefix chunk's copies go out two chunks ahead (with one stage
+    // ahead a state-only step waits out its copies' whole latency).  Stages 0 and 1 are
+    // the walk's own; stage 2 takes the Q area (with two Q stages, the second) for K and
+    // the output staging area for V, which a state-only step leaves unused.  Prefix chunk
+    // p takes stage (p + 2 - npre) mod 3, so the last one is in stage 1 and its step can
+    // copy the first full chunk into stage 0 and the Q area.
+    constexpr bool P3 = !GATED;
+    constexpr uint32_t kP2K = L_::kQ + (QS == 2 ? L_::kQTile : 0);
+    static_assert(L_::kQTile == L_::kKTile && L_::kG - L_::kX == L_::kVTile, "third stage must fit the Q and staging areas");
+    auto pre_copy = [&](int ps, uint32_t row0) {
+        const uint32_t kb = ps == 0 ? L_::kK : ps == 1 ? L_::kK + L_::kKTile : kP2K;
+        const uint32_t vb = ps == 0 ? L_::kV : ps == 1 ? L_::kV + L_::kVTile : L_::kX;
+#pragma unroll
+        for (int i = 0; i < kNQ; ++i) kcp.issue_one(i, lds0 + kb + wofs, k_rs, row0 * qk_rb);
+#pragma unroll
+        for (int i = 0; i < kNV; ++i) vcp.issue_one(i, lds0 + vb + wofs, v_rs, row0 * v_rb);
+    };
+
     // ---- output staging: a finished block goes to LDS as bf16, row-major [64][128] with
     // the 16-byte units of row r rotated by XOR with r; after the next barrier every lane
     // stores 16-byte units, so each wave writes whole 256-byte rows.
@@ -419,14 +438,21 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         *reinterpret_cast<u16x8_t*>(smem + L_::kP + tid * 16) = u16x8_t{};
         // the first chunk walked: the first prefix chunk (no Q), or the segment's first
         const uint32_t r0 = static_cast<uint32_t>(npre > 0 ? 0 : t_begin);
-        if (npre == 0) {
+        if (P3 && npre > 0) {
+            // (three-stage prefix) prefix chunks 0 and 1 into their stages
+            const int ph = ((2 - npre) % 3 + 3) % 3;
+            pre_copy(ph, 0u);
+            if (npre > 1) pre_copy((ph + 1) % 3, static_cast<uint32_t>(kBlk));
+        } else {
+            if (npre == 0) {
 #pragma unroll
-            for (int i = 0; i < kNQ; ++i) q_copy(i, 0, r0);
+                for (int i = 0; i < kNQ; ++i) q_copy(i, 0, r0);
+            }
+#pragma unroll
+            for (int i = 0; i < kNQ; ++i) k_copy(i, 0, r0);
+#pragma unroll
+            for (int i = 0; i < kNV; ++i) v_copy(i, 0, r0);
         }
-#pragma unroll
-        for (int i = 0; i < kNQ; ++i) k_copy(i, 0, r0);
-#pragma unroll
-        for (int i = 0; i < kNV; ++i) v_copy(i, 0, r0);
         g_load(static_cast<int>(r0));
         __builtin_amdgcn_s_waitcnt(0);
         g_scan(0);
@@ -434,8 +460,10 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
 
 
     // The state update over the chunk's L keys (full: L = 64), after the caller has
-    // added the chunk's decay to lk2.
-    auto state_update = [&](uint32_t koff, uint32_t voff, const float* gl, int L, bool full, auto hook) {
+    // added the chunk's decay to lk2.  K^T fragments are read one group of state tiles
+    // ahead of the matrix instructions; the group size is GW (0: two tiles for d_k = 256,
+    // four for d_k = 128, which leaves room for a full step's other live registers).
+    auto state_update = [&](auto gw, uint32_t koff, uint32_t voff, const float* gl, int L, bool full, auto hook) {
         // rescale the registers once the state scale gets small (after the cross term,
         // which reads them at the old scale)
         if (lk2 < -64.f) {
@@ -459,7 +487,8 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
                     const uint32_t off = koff + kh * 32 * QRB + (sd / SL) * 256;
                     return cat(lds_tra(akt[0][sd % SL][dt & 1] + off), lds_tra(akt[1][sd % SL][dt & 1] + off));
                 };
-                constexpr int G = DT < 4 ? DT : (DT >= 16 ? 2 : 4);
+                constexpr int GW = decltype(gw)::value;
+                constexpr int G = GW > 0 ? (GW < DT ? GW : DT) : DT < 4 ? DT : (DT >= 16 ? 2 : 4);
                 u16x8_t acur[G], anext[G];
                 const u16x8_t raw = cat(lds_tra(avs[0] + voff + kh * 32 * VRB), lds_tra(avs[1] + voff + kh * 32 * VRB));
 #pragma unroll
@@ -627,7 +656,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
     auto step = [&](auto stage_c, int c) -> bool {
         constexpr int ST = decltype(stage_c)::value;
         constexpr int QB = QS == 2 ? ST : 0;
-        const bool sonly = c < npre;            // the state update alone
+        const bool sonly = !P3 && c < npre;   // the state update alone (two-stage prefix)
         const int cs = chunk_row(c);
         const int L = min(kBlk, t_end - cs);    // (prefix chunks are whole)
         const bool full = L == kBlk;
@@ -778,7 +807,7 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         // before its products; a full step with one Q stage issues the Q copies between
         // the products.
         if (sonly && has_next) copy_slice(0, kOps, 0, 1);
-        state_update(koff, voff, gl, L, full, [&](int kh, int gi, int ng) {
+        state_update(std::integral_constant<int, 0>{}, koff, voff, gl, L, full, [&](int kh, int gi, int ng) {
             if (!has_next) return;
             if (!sonly && QS == 1 && kh == 0) copy_slice(kCrossOps, kOps, gi, ng);
         });
@@ -835,9 +864,74 @@ __global__ __launch_bounds__(kC1Waves * 64, 1) __attribute__((amdgpu_waves_per_e
         return has_next;
     };
 
-    for (int c = 0;; c += 2) {
-        if (!step(std::integral_constant<int, 0>{}, c)) break;
-        if (!step(std::integral_constant<int, 1>{}, c + 1)) break;
+    // ---- (three-stage prefix) the state-only walk; the main walk then starts at chunk
+    // npre in stage 0
+    if constexpr (P3) {
+        if (npre > 0) {
+            // K^T read bases moved by d (stage 2 lies below them; an immediate cannot be
+            // negative)
+            auto kt_shift = [&](uint32_t d) {
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                    for (int sl = 0; sl < SL; ++sl)
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb) akt[pl][sl][hb] = opaque(akt[pl][sl][hb] + d);
+            };
+            constexpr int kPreOps = kNQ + kNV;   // one prefix chunk's copies per wave
+            auto pstep = [&](auto ps_c, int p) {
+                constexpr int PS = decltype(ps_c)::value;
+                // chunk p has landed (chunk p+1's copies may still be in flight)
+                if (p + 1 < npre) wait_vmcnt<kPreOps>();
+                else wait_vmcnt<0>();
+                lds_barrier();
+                // every wave is past chunk p-1: its stage takes chunk p+2; the last step
+                // copies the first full chunk into stage 0 and the Q area
+                if (p + 2 < npre) {
+                    pre_copy((PS + 2) % 3, static_cast<uint32_t>(__builtin_amdgcn_readfirstlane((p + 2) * kBlk)));
+                } else if (p + 1 == npre && nck > 0) {
+                    const uint32_t row = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t_begin));
+#pragma unroll
+                    for (int i = 0; i < kNQ; ++i) k_copy(i, 0, row);
+#pragma unroll
+                    for (int i = 0; i < kNV; ++i) v_copy(i, 0, row);
+#pragma unroll
+                    for (int i = 0; i < kNQ; ++i) q_copy(i, 0, row);
+                }
+                lk2 += static_cast<float>(kBlk) * lg;
+                constexpr uint32_t koff = PS == 1 ? L_::kKTile : 0;
+                constexpr uint32_t voff = PS == 0 ? 0 : PS == 1 ? L_::kVTile : L_::kX - L_::kV;
+                if constexpr (PS == 2) kt_shift(kP2K - L_::kK);
+                // (the cross term's registers are free: K^T reads go 4 (d_k = 256) or 8 state tiles ahead)
+                state_update(std::integral_constant<int, DK == 256 ? 4 : 8>{}, koff, voff, nullptr, kBlk, true, [](int, int, int) {});
+                if constexpr (PS == 2) kt_shift(L_::kK - kP2K);
+            };
+            // the steps before the first one in stage 0 are peeled (a jump into the loop
+            // would make the flow graph irreducible, which costs registers)
+            int p = 0;
+            const int ph = ((2 - npre) % 3 + 3) % 3;   // stage of prefix chunk 0
+            if (ph == 1) {
+                pstep(std::integral_constant<int, 1>{}, p++);
+                if (p < npre) pstep(std::integral_constant<int, 2>{}, p++);
+            } else if (ph == 2) {
+                pstep(std::integral_constant<int, 2>{}, p++);
+            }
+            while (p < npre) {
+                pstep(std::integral_constant<int, 0>{}, p);
+                if (++p == npre) break;
+                pstep(std::integral_constant<int, 1>{}, p);
+                if (++p == npre) break;
+                pstep(std::integral_constant<int, 2>{}, p);
+                ++p;
+            }
+        }
+    }
+    const int c0 = P3 ? npre : 0;
+    if (c0 < ntot) {
+        for (int c = c0;; c += 2) {
+            if (!step(std::integral_constant<int, 0>{}, c)) break;
+            if (!step(std::integral_constant<int, 1>{}, c + 1)) break;
+        }
     }
     if constexpr (DOT) {
         if (dot_row >= 0) {

@@ -107,6 +107,18 @@ SMALL = [
     (1, 16, 600, 128, 1024, 64, "bf16", False, True),
     (2, 8, 450, 128, 1024, 64, "bf16", True, True),
     (1, 32, 300, 256, 512, 64, "bf16", False, True),     # ragged last chunk
+    # per head, the state-only prefix runs over three stages; prefixes of 2 to 5 chunks
+    # enter it at each of them (d_k 256 and 128), and short sequences of one chunk, a
+    # one-token last chunk, 384 columns and a grid that is not a multiple of 8
+    (1, 32, 256, 256, 512, 64, "bf16", False, True),
+    (1, 32, 320, 256, 512, 64, "bf16", False, False),
+    (1, 16, 384, 128, 1024, 64, "bf16", False, True),
+    (1, 32, 448, 256, 512, 64, "bf16", False, True),
+    (1, 16, 256, 128, 1024, 64, "bf16", False, False),
+    (1, 32, 64, 256, 512, 64, "bf16", False, True),
+    (1, 32, 65, 256, 512, 64, "bf16", False, True),
+    (2, 22, 150, 256, 384, 64, "bf16", False, True),
+    (1, 43, 100, 256, 384, 64, "bf16", False, False),
     # chunks of 128/256/512 with d_k = 128 (query-row parallel main pass): two column
     # tiles, ragged last chunks (one that ends inside the second pass of a 512-token
     # chunk, one of 8 tokens), several segments, and a chunk of one block
