@@ -32,6 +32,9 @@ rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the copy-kernel calibration
 factor, and "mfma_busy_counter" the matrix-core busy fraction from the committed
 rocprofv3 counters (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs); both are
 null when the kernel source changed since they were taken.
+Every timed run is preceded by SETTLE_S (0.3 s) of untimed steps of the same workload and
+then the W warmup steps: the GPU's first few hundred milliseconds of sustained work run
+10-25% slower than its steady state.  The K timed steps are whole steps, unchanged.
 "timing" adds per-call HIP-event times of the headline (median, minimum, mean, p90 over
 at least 100 calls), back to back and with a 1 GiB write before each call that evicts
 the inputs from the MALL and L2; the decode lines add the per-step distribution.
@@ -78,7 +81,30 @@ def alg_flops(B, H, N, dk, dv, C):
     return B * H * N * ((C + 1) * (dk + dv) + 4 * dk * dv)
 
 
-def time_steps(fn, steps, warmup, torch):
+# Untimed steps run for this long before a workload's warmup steps.  The GPU runs its
+# first few hundred milliseconds of sustained work 10-25% slower than its steady state
+# (measured on the headline: 79-97 us per step over the first 80 steps of a process,
+# 73-75 us after 0.3 s of steps), so a short run would time that transient instead of
+# the operator.
+SETTLE_S = 0.3
+
+
+def settle(fn, torch, seconds=SETTLE_S):
+    """Run fn(0), fn(1), ... untimed until `seconds` of wall time have passed."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()   # keep the queue short, so the wall clock tracks the GPU
+    torch.cuda.synchronize()
+    return i
+
+
+def time_steps(fn, steps, warmup, torch, settle_s=SETTLE_S):
+    if settle_s > 0:
+        settle(fn, torch, settle_s)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -192,7 +218,7 @@ def run_chunk_workload(torch, R, name, B, H, N, dk, dv, C, gammas, gated, steps,
     if kernel_times:
         # same steps again, each library launch bracketed by HIP events on its stream
         R.profile_enable(True)
-        time_steps(step, steps, 0, torch)
+        time_steps(step, steps, 0, torch, settle_s=0)
         prof = R.profile_read()
         R.profile_enable(False)
         kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["ms"] / v["launches"], 3)}
@@ -507,8 +533,9 @@ def main():
                    "dk": 256, "dv": 512, "chunk": 64, "global_batch": 4, "seq_len": 2048,
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "timing": {"protocol": "value and ms_per_step: HIP events around the timed steps back to back; per_call: "
-                               "events around each of the calls, unflushed and with a 1 GiB write before each",
+        "timing": {"protocol": "value and ms_per_step: HIP events around the timed steps back to back, after "
+                               f"{SETTLE_S} s of untimed steps and the warmup steps; per_call: events around each "
+                               "of the calls, unflushed and with a 1 GiB write before each",
                    "per_call": head["per_call"]},
     }
     line["achievable"] = achievable(torch, R)
