@@ -394,10 +394,21 @@ def cpu_baseline(max_seconds=15.0):
     cpu = (t2.user - t1.user) + (t2.system - t1.system)
     threads = max(1, int(round(cpu / max(wall, 1e-9))))
     del t0
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    try:   # numpy's BLAS pool (the recurrence's elementwise loop does not use it)
+        from threadpoolctl import threadpool_info
+        blas = ",".join(f"{p.get('internal_api')}:{p.get('num_threads')}" for p in threadpool_info()
+                        if p.get("user_api") == "blas") or "none"
+    except Exception:   # threadpoolctl missing or unable to inspect: report unknown
+        blas = "unknown"
     return {"value": w.B * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"train_bf16 workload, all {w.B}x{w.H} (b,h), first {T} of {w.N} tokens, "
                       f"fp64 numpy recurrence; {wall:.1f} s wall, {cpu:.1f} s CPU; "
-                      f"host has {os.cpu_count()} logical CPUs"}
+                      f"host has {os.cpu_count()} logical CPUs, {affinity} in this process's affinity; "
+                      f"BLAS threads {blas}"}
 
 
 def counter_summary():
