@@ -35,6 +35,10 @@
 //   barrier; (one Q stage: the next chunk's Q copies) state update; X += P V; X staged
 //   in LDS as bf16 and stored in whole rows after the next barrier (fp32 output: stored
 //   from the accumulators, 16 bytes per lane).
+// Prefix split (two segments, no pre-pass): the second segment's workgroups first walk
+// the first segment's chunks state-only for their entry state.  Per head that walk runs
+// over three LDS stages of K and V (the Q and output staging areas hold the third), with
+// copies two chunks ahead; gated, it stays on the walk's own two stages.
 
 #include "cdna4.h"
 #include "chunk_tiles.h"
